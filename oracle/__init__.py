@@ -1,0 +1,179 @@
+"""CPU oracle for the tiled FP16 GEMM -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The GPU library never calls it and
+shares no code with it.
+
+The oracle computes the plain definition of the product the tiled kernel
+reaches (page "TileLang：比 Triton 低一层的 tile 语言", section
+"第一个 kernel：GEMM"; fused ReLU from "TileLang：让GPU编程像Python一样简单的高性能计算新范式",
+section "并行计算的优雅表达"):
+
+    C[i, j] = rne16(epi(sum_k a(A[i, k]) * a(B[k, j])))
+
+with exact binary16 decoding, a sequential fp64 sum over k and one
+round-to-nearest-even to binary16.  The arithmetic lives in plain C
+(``oracle_gemm.c``); this module marshals numpy arrays of binary16 bit
+patterns (``uint16``) to it.  The tolerance rule used to compare a GPU
+result with the oracle's is here too.
+
+Every function is pinned by the ``-m "not gpu"`` tests against facts that do
+not come from the oracle itself: numpy's own binary16 conversion, exact
+rational brute force, identity / permutation / integer cases and algebraic
+invariants.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_LIB = None
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        lib = ctypes.CDLL(_build.LIB)
+        i64, u16p, f64p, i64p = (ctypes.c_int64, ctypes.POINTER(ctypes.c_uint16),
+                                 ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64))
+        lib.oracle_f16_decode.argtypes = [ctypes.c_uint16]
+        lib.oracle_f16_decode.restype = ctypes.c_double
+        lib.oracle_f16_encode.argtypes = [ctypes.c_double]
+        lib.oracle_f16_encode.restype = ctypes.c_uint16
+        lib.oracle_f16_decode_array.argtypes = [u16p, f64p, i64]
+        lib.oracle_f16_decode_array.restype = None
+        lib.oracle_f16_encode_array.argtypes = [f64p, u16p, i64]
+        lib.oracle_f16_encode_array.restype = None
+        lib.oracle_cpu_threads.argtypes = []
+        lib.oracle_cpu_threads.restype = ctypes.c_int
+        lib.oracle_gemm_f16.argtypes = [i64, i64, i64, u16p, u16p, ctypes.c_int, u16p, ctypes.c_int]
+        lib.oracle_gemm_f16.restype = ctypes.c_int
+        lib.oracle_gemm_f16_sampled.argtypes = [i64, i64, i64, u16p, u16p, i64p, i64, i64p, i64,
+                                                ctypes.c_int, u16p, ctypes.c_int]
+        lib.oracle_gemm_f16_sampled.restype = ctypes.c_int
+        _LIB = lib
+    return _LIB
+
+
+def _ptr(a, ctype):
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def _as_bits(x, name):
+    x = np.asarray(x)
+    if x.dtype == np.float16:
+        x = x.view(np.uint16)
+    if x.dtype != np.uint16:
+        raise TypeError(f"{name}: expected binary16 bit patterns (uint16) or float16, got {x.dtype}")
+    return np.ascontiguousarray(x)
+
+
+def cpu_threads() -> int:
+    """Threads the oracle uses by default: the process's CPU affinity count."""
+    return int(_lib().oracle_cpu_threads())
+
+
+def decode(h) -> np.ndarray:
+    """Exact value (float64) of each binary16 bit pattern."""
+    h = _as_bits(h, "h")
+    out = np.empty(h.shape, dtype=np.float64)
+    _lib().oracle_f16_decode_array(_ptr(h, ctypes.c_uint16), _ptr(out, ctypes.c_double), h.size)
+    return out
+
+
+def encode(x) -> np.ndarray:
+    """Nearest binary16 (ties to even) of each float64, as uint16 bit patterns."""
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+    out = np.empty(x.shape, dtype=np.uint16)
+    _lib().oracle_f16_encode_array(_ptr(x, ctypes.c_double), _ptr(out, ctypes.c_uint16), x.size)
+    return out
+
+
+def gemm(A, B, relu: bool = False, threads: int = 0) -> np.ndarray:
+    """C = rne16(epi(A . B)) for A (M x K) and B (K x N) binary16; returns uint16 (M x N)."""
+    A = _as_bits(A, "A")
+    B = _as_bits(B, "B")
+    if A.ndim != 2 or B.ndim != 2 or A.shape[1] != B.shape[0]:
+        raise ValueError(f"shape mismatch: A {A.shape}, B {B.shape}")
+    M, K = A.shape
+    N = B.shape[1]
+    C = np.zeros((M, N), dtype=np.uint16)
+    rc = _lib().oracle_gemm_f16(M, N, K, _ptr(A, ctypes.c_uint16), _ptr(B, ctypes.c_uint16),
+                                int(bool(relu)), _ptr(C, ctypes.c_uint16), int(threads))
+    if rc != 0:
+        raise RuntimeError("oracle_gemm_f16 failed")
+    return C
+
+
+def gemm_sampled(A, B, rows, cols, relu: bool = False, threads: int = 0) -> np.ndarray:
+    """The block C[rows x cols] of rne16(epi(A . B)); returns uint16 (len(rows) x len(cols))."""
+    A = _as_bits(A, "A")
+    B = _as_bits(B, "B")
+    if A.ndim != 2 or B.ndim != 2 or A.shape[1] != B.shape[0]:
+        raise ValueError(f"shape mismatch: A {A.shape}, B {B.shape}")
+    M, K = A.shape
+    N = B.shape[1]
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    cols = np.ascontiguousarray(np.asarray(cols, dtype=np.int64))
+    C = np.zeros((rows.size, cols.size), dtype=np.uint16)
+    rc = _lib().oracle_gemm_f16_sampled(M, N, K, _ptr(A, ctypes.c_uint16), _ptr(B, ctypes.c_uint16),
+                                        _ptr(rows, ctypes.c_int64), rows.size,
+                                        _ptr(cols, ctypes.c_int64), cols.size,
+                                        int(bool(relu)), _ptr(C, ctypes.c_uint16), int(threads))
+    if rc != 0:
+        raise RuntimeError("oracle_gemm_f16_sampled failed (bad index or allocation failure)")
+    return C
+
+
+# ---- tolerance ------------------------------------------------------------
+
+ABS_FLOOR = 1e-3
+ULPS = 2
+
+
+def ulp(r_bits) -> np.ndarray:
+    """Spacing of binary16 just above |r|: 2^(max(E, 1) - 25) with E the biased
+    exponent field of r (2^-24 for zero and subnormals, 2^-10 in [1, 2))."""
+    r_bits = _as_bits(r_bits, "r")
+    E = (r_bits.astype(np.int64) >> 10) & 0x1F
+    return np.ldexp(1.0, np.maximum(E, 1) - 25)
+
+
+def compare(got_bits, ref_bits) -> dict:
+    """Elementwise check of a GPU result against the oracle's.
+
+    An element passes iff |g - r| <= max(2 * ulp(r), 1e-3), computed in fp64;
+    any NaN fails.  Returns counts and the worst errors (in fp64 and in ulps
+    of the reference).
+    """
+    g_bits = _as_bits(got_bits, "got")
+    r_bits = _as_bits(ref_bits, "ref")
+    if g_bits.shape != r_bits.shape:
+        raise ValueError(f"shape mismatch: {g_bits.shape} vs {r_bits.shape}")
+    g = decode(g_bits)
+    r = decode(r_bits)
+    u = ulp(r_bits)
+    with np.errstate(invalid="ignore"):
+        err = np.abs(g - r)
+        bound = np.maximum(ULPS * u, ABS_FLOOR)
+        ok = err <= bound
+    ok &= ~np.isnan(g) & ~np.isnan(r)
+    n = int(g.size)
+    n_fail = int(n - np.count_nonzero(ok))
+    finite = np.isfinite(err)
+    max_abs = float(err[finite].max()) if np.any(finite) else 0.0
+    ulp_err = np.where(finite, err / u, np.inf)
+    max_ulp = float(ulp_err.max()) if n else 0.0
+    return {
+        "n": n,
+        "n_fail": n_fail,
+        "pass": n_fail == 0,
+        "max_abs_err": max_abs,
+        "max_ulp_err": max_ulp,
+        "n_gt_1ulp": int(np.count_nonzero(ulp_err > 1.0)),
+        "n_bit_exact": int(np.count_nonzero(g_bits == r_bits)),
+    }
