@@ -1,0 +1,196 @@
+"""Benchmark: fp16 GEMM TFLOP/s on one MI355X and the fraction of the dense
+FP16 MFMA peak, on seeded synthetic inputs.
+
+One step is one call of the whole hot path, C = A . B, on the 8192 x 8192 x
+8192 workload (A ~ N(0, 1) activations, B ~ N(0, 1/sqrt(K)) weights, seed 4)
+with the inputs already resident in GPU memory.  Prints one JSON line.
+
+The roofline entry reports the GEMM kernel's achieved TFLOP/s (2 M N K per
+launch over the average launch duration, timed with events on the launch
+stream) against MI355X's dense FP16 MFMA peak; ``traffic`` is the HBM bytes
+per launch measured by rocprofv3 counters for this exact kernel source (null
+when the source has changed since they were taken).  The CPU baseline times
+the plain oracle on a bounded block of the same product.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = 256 * 2.4e9 * 4096 / 1e12          # 256 CUs x 2.4 GHz x 4096 flop/clk/CU (dense FP16 MFMA)
+METRIC = "fp16 GEMM TFLOP/s at 1 MI355X and % of dense FP16 MFMA peak"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_8192.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "tiled_dense_gemm_fp16_amd", "csrc", f)
+                  for f in ("gemm_f16_kernels.hip", "gemm_f16_internal.h", "gemm_f16_api.cpp")]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str, config_name: str):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel source, this workload and this configuration."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if (t.get("kernel_sha256") != kernel_source_hash() or t.get("workload") != workload
+            or t.get("kernel_config") != config_name):
+        return None
+    return float(t["fetch_bytes_per_launch"]) + float(t["write_bytes_per_launch"])
+
+
+def cpu_baseline(a, b, w, budget_s: float):
+    """Time the oracle on a seeded block of the same product (rows x columns
+    of C, full K), sized to take roughly ``budget_s`` seconds."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import workloads
+
+    A = a.view(torch.int16).numpy().view(np.uint16)
+    B = b.view(torch.int16).numpy().view(np.uint16)
+    rows_all, cols_all = workloads.sample_indices(w)
+    cols = cols_all.numpy()
+    # calibrate on a small block, then size the timed block
+    n_cal = 64
+    t0 = time.perf_counter()
+    oracle.gemm_sampled(A, B, rows_all[:n_cal].numpy(), cols)
+    t_cal = max(time.perf_counter() - t0, 1e-3)
+    n_rows = int(min(len(rows_all), max(n_cal, n_cal * budget_s / t_cal)))
+    rows = rows_all[:n_rows].numpy()
+    t0 = time.perf_counter()
+    oracle.gemm_sampled(A, B, rows, cols)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * len(rows) * len(cols) * w.K
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": oracle.cpu_threads(),
+        "kind": "oracle",
+        "sample": f"{len(rows)} seeded rows x {len(cols)} seeded columns of C at full K={w.K} "
+                  f"({flops / 1e9:.1f} GFLOP, fp64 accumulation) in {dt:.1f} s",
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="gemm_8192")
+    ap.add_argument("--config", type=int, default=-1, help="kernel configuration (-1: automatic)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the GEMM shards over GPUs without communication; see the design notes)",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import tiled_dense_gemm_fp16_amd as g
+    import workloads
+
+    if not os.path.exists(g.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+
+    w = workloads.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    a, b = workloads.make_inputs(w)
+    ad, bd = a.to(dev), b.to(dev)
+    cd = torch.empty((w.M, w.N), dtype=torch.float16, device=dev)
+    epi = "relu" if w.relu else "none"
+    plan = g.plan(w.M, w.N, w.K, ad.data_ptr(), bd.data_ptr(), cd.data_ptr(), config=args.config)
+    stream = torch.cuda.current_stream(dev)
+
+    for _ in range(args.warmup):
+        g.gemm(ad, bd, epilogue=epi, out=cd, config=args.config, stream=stream)
+    torch.cuda.synchronize()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        g.gemm(ad, bd, epilogue=epi, out=cd, config=args.config, stream=stream)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    launch_ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+    ms_per_step = wall * 1e3 / args.steps
+    flops = float(w.flops)
+    value = flops * args.steps / wall / 1e12
+    achieved = flops / (launch_ms.mean() * 1e-3) / 1e12
+
+    # a spot check of the timed output against the oracle (a 64 x 64 seeded block)
+    import oracle
+    rows, cols = workloads.sample_indices(w, 64)
+    got = cd[rows.to(dev)][:, cols.to(dev)].cpu().view(torch.int16).numpy().view(np.uint16)
+    ref = oracle.gemm_sampled(a.view(torch.int16).numpy().view(np.uint16),
+                              b.view(torch.int16).numpy().view(np.uint16), rows.numpy(), cols.numpy(),
+                              relu=w.relu)
+    spot = oracle.compare(got, ref)
+
+    config_name = g.config_name(plan["config"])
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "epilogue": epi,
+                   "inputs": f"{w.dist} seed {w.seed}", "kernel": config_name},
+        "pct_of_peak": round(100.0 * value / PEAK_TFLOPS, 2),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": round(PEAK_TFLOPS, 1),
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_TFLOPS, 4),
+            "traffic": measured_traffic(w.name, config_name),
+            "kernel_ms_mean": round(float(launch_ms.mean()), 5),
+            "kernel_ms_median": round(float(np.median(launch_ms)), 5),
+            "kernel_ms_min": round(float(launch_ms.min()), 5),
+            "algorithmic_flops": flops,
+            "algorithmic_bytes": float(w.min_bytes),
+        },
+        "spot_check": {"n": spot["n"], "pass": spot["pass"], "max_ulp_err": spot["max_ulp_err"]},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(a, b, w, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+    return 0 if spot["pass"] else 1
+
+
+if __name__ == "__main__":
+    sys.exit(main())

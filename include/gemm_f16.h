@@ -1,0 +1,164 @@
+/*
+ * gemm_f16.h -- C ABI of the tiled FP16 GEMM library for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The operation is the tiled GEMM that the TileLang pages use as their main
+ * example ("TileLang：比 Triton 低一层的 tile 语言", section
+ * "第一个 kernel：GEMM"; "5分钟上手TileLang：GPU内核开发指南", section
+ * "安装与第一个内核"):
+ *
+ *     C[M x N] = epi( A[M x K] . B[K x N] )
+ *
+ * with binary16 operands, products accumulated in fp32 registers over a
+ * pipelined K loop, an optional fused ReLU epilogue max(C, 0) applied to the
+ * fp32 accumulator ("TileLang：让GPU编程像Python一样简单的高性能计算新范式",
+ * section "并行计算的优雅表达"), and one round-to-nearest-even conversion to
+ * binary16 in the final copy ("5分钟上手TileLang：GPU内核开发指南", section
+ * "避坑与调参").  As on the pages, the caller provides A and B and receives C;
+ * here the caller also owns C's memory.
+ *
+ * Layout: A, B and C are dense, row-major, contiguous device arrays of IEEE
+ * binary16 (lda = K, ldb = N, ldc = N).  Pointers need only 2-byte
+ * alignment; 16-byte alignment of the pointers and of the row pitches (K and
+ * N multiples of 8) selects the fastest kernels, other shapes run a slower
+ * path that gives the same results (never an error).
+ *
+ * Ownership: all three buffers belong to the caller.  The library allocates
+ * no device memory per call and keeps no per-call state; it is safe to call
+ * from several host threads.
+ *
+ * Execution: asynchronous on the given HIP stream (a hipStream_t passed as
+ * void*; NULL is the default stream).  No host synchronisation.  The result
+ * is deterministic: no atomics, so it is bitwise reproducible run to run for
+ * a given shape and kernel configuration.
+ *
+ * Errors: arguments are validated before any HIP call; on error nothing is
+ * launched and C is untouched.  A launch error is reported as
+ * GEMM_F16_ERROR_LAUNCH_FAILED.  Faults during execution surface at the
+ * caller's next synchronisation, as with any HIP work.  No C++ exception
+ * crosses this interface.
+ */
+#ifndef GEMM_F16_H
+#define GEMM_F16_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gemm_f16_status {
+    GEMM_F16_SUCCESS = 0,
+    /* negative dimension, null pointer with a nonzero extent, unknown
+     * epilogue or configuration, C overlapping A or B */
+    GEMM_F16_ERROR_INVALID_VALUE = 1,
+    /* a pointer that is not 2-byte aligned */
+    GEMM_F16_ERROR_MISALIGNED = 2,
+    /* no HIP device is visible */
+    GEMM_F16_ERROR_NO_DEVICE = 3,
+    /* the current device is not gfx950 */
+    GEMM_F16_ERROR_UNSUPPORTED_DEVICE = 4,
+    /* the kernel launch itself failed */
+    GEMM_F16_ERROR_LAUNCH_FAILED = 5,
+    /* a dimension beyond the library's limits (see GEMM_F16_MAX_*) */
+    GEMM_F16_ERROR_UNSUPPORTED_SIZE = 6
+} gemm_f16_status_t;
+
+typedef enum gemm_f16_epilogue {
+    GEMM_F16_EPILOGUE_NONE = 0,   /* C = rne16(A . B) */
+    GEMM_F16_EPILOGUE_RELU = 1    /* C = rne16(max(A . B, 0)); -0 becomes +0 */
+} gemm_f16_epilogue_t;
+
+/* Size limits: M at most 2^31 - 1; K and N at most 2^22, so that the panel
+ * of A, B or C one workgroup addresses (at most 256 rows) spans at most
+ * 2 GiB and fits a 32-bit buffer offset; and at most 2^31 - 1 output tiles. */
+#define GEMM_F16_MAX_DIM ((int64_t)2147483647)
+#define GEMM_F16_MAX_K ((int64_t)1 << 22)
+#define GEMM_F16_MAX_N ((int64_t)1 << 22)
+
+/* Automatic kernel choice for gemm_f16_ex / gemm_f16_plan. */
+#define GEMM_F16_CONFIG_AUTO (-1)
+
+/*
+ * C = epi(A . B) for A (M x K), B (K x N), C (M x N), all binary16 row-major.
+ *   M, N, K   : dimensions, >= 0.  M == 0 or N == 0: nothing to do (success,
+ *               no launch).  K == 0: C is filled with +0 (the empty sum).
+ *   A, B      : device pointers (read only); may be NULL only when the
+ *               matrix has no elements.
+ *   C         : device pointer (written); must not overlap A or B.
+ *   epilogue  : a gemm_f16_epilogue_t value.
+ *   stream    : hipStream_t, or NULL for the default stream.
+ * Returns GEMM_F16_SUCCESS once the work is enqueued.
+ */
+gemm_f16_status_t gemm_f16(int64_t M, int64_t N, int64_t K,
+                           const void *A, const void *B, void *C,
+                           int epilogue, void *stream);
+
+/*
+ * As gemm_f16, with an explicit kernel configuration: an index in
+ * [0, gemm_f16_num_configs()) or GEMM_F16_CONFIG_AUTO.  A configuration that
+ * cannot run this shape or alignment (gemm_f16_plan says why) returns
+ * GEMM_F16_ERROR_INVALID_VALUE.  Intended for tests and tuning sweeps; every
+ * configuration computes the same function.
+ */
+gemm_f16_status_t gemm_f16_ex(int64_t M, int64_t N, int64_t K,
+                              const void *A, const void *B, void *C,
+                              int epilogue, int config, void *stream);
+
+/* How a call would run; filled by gemm_f16_plan without any HIP call. */
+typedef struct gemm_f16_plan {
+    int32_t config;        /* configuration index actually chosen */
+    int32_t block_m;       /* output tile rows per workgroup (bM) */
+    int32_t block_n;       /* output tile columns per workgroup (bN) */
+    int32_t block_k;       /* K depth of one LDS stage (bK) */
+    int32_t stages;        /* LDS ring-buffer stages */
+    int32_t threads;       /* threads per workgroup */
+    int32_t direct_lds;    /* 1: operands go global -> LDS without registers */
+    int32_t vec_a;         /* binary16 elements per global load of A */
+    int32_t vec_b;         /* binary16 elements per global load of B */
+    int32_t vec_c;         /* binary16 elements per store of C */
+    int64_t tiles_m;       /* ceil(M / bM) */
+    int64_t tiles_n;       /* ceil(N / bN) */
+    int64_t grid;          /* workgroups launched (tiles_m * tiles_n) */
+    int64_t k_tiles;       /* K-loop trip count ceil(K / bK) */
+    int64_t lds_bytes;     /* LDS per workgroup */
+    double flops;          /* 2 M N K: the algorithmic work of the call */
+    double min_bytes;      /* 2 (M K + K N + M N): operands read once, C written once */
+} gemm_f16_plan_t;
+
+/*
+ * Describe the kernel a call with these arguments would launch (config may
+ * be GEMM_F16_CONFIG_AUTO).  Pointers are used only for alignment checks and
+ * may be NULL-but-aligned stand-ins (any multiple of 16) when only the shape
+ * matters.  Pure host logic: no HIP call, no GPU needed.
+ */
+gemm_f16_status_t gemm_f16_plan(int64_t M, int64_t N, int64_t K,
+                                const void *A, const void *B, const void *C,
+                                int config, gemm_f16_plan_t *plan);
+
+/* Number of kernel configurations compiled into the library. */
+int gemm_f16_num_configs(void);
+
+/* Short human-readable name of a configuration ("256x256x64_s2_direct", ...)
+ * or NULL for an index out of range.  The string is static. */
+const char *gemm_f16_config_name(int config);
+
+/*
+ * LDS bytes that `stages` ring-buffer stages of an unpadded bM x bK A tile
+ * and bK x bN B tile of binary16 occupy: stages * 2 * bK * (bM + bN).  This
+ * is the shared-memory budget of the pages' worked exercise
+ * ("TileLang：比 Triton 低一层的 tile 语言", section "练习", exercises 1-2);
+ * the library's LDS layouts are swizzled, not padded, so their footprint is
+ * exactly this.  Returns -1 for negative arguments.
+ */
+int64_t gemm_f16_stage_bytes(int64_t block_m, int64_t block_n, int64_t block_k,
+                             int64_t stages);
+
+/* Static English description of a status code. */
+const char *gemm_f16_status_string(gemm_f16_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GEMM_F16_H */

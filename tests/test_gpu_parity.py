@@ -1,0 +1,204 @@
+"""GPU parity of the HIP GEMM against the CPU oracle, through the C ABI.
+
+Bar: every element within max(2 fp16 ulps of the oracle's value, 1e-3)
+(``oracle.compare``); bit-exact where the exact result is representable
+(identity, integer-valued operands); bitwise run-to-run determinism; no write
+outside C.  The tile GEMM, its fused ReLU and the fp16 write-back are those
+of "TileLang：比 Triton 低一层的 tile 语言" (section "第一个 kernel：GEMM") and
+"TileLang：让GPU编程像Python一样简单的高性能计算新范式" (section
+"并行计算的优雅表达"); the pages ask for boundary shapes whose M, N, K are not
+tile multiples (same page as the first, section "工程上的几个注意点").
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tiled_dense_gemm_fp16_amd as g
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def u16(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def run(a, b, epilogue="none", config=g.CONFIG_AUTO):
+    c = g.gemm(a.to(DEV), b.to(DEV), epilogue=epilogue, config=config)
+    torch.cuda.synchronize()
+    return u16(c)
+
+
+def check(a, b, epilogue="none", config=g.CONFIG_AUTO, label=""):
+    print(f"[parity] {label} {tuple(a.shape)}x{tuple(b.shape)} epi={epilogue} config={config}", flush=True)
+    got = run(a, b, epilogue, config)
+    ref = oracle.gemm(u16(a), u16(b), relu=(epilogue == "relu"))
+    res = oracle.compare(got, ref)
+    assert res["pass"], f"{label}: {res}"
+    return res
+
+
+def configs_for(M, N, K):
+    """Every configuration that accepts this (aligned-pointer) shape."""
+    out = []
+    for c in range(g.num_configs()):
+        try:
+            g.plan(M, N, K, 1 << 20, 1 << 20, 1 << 20, config=c)
+            out.append(c)
+        except g.GemmError:
+            pass
+    return out
+
+
+# shapes spanning several tiles of every configuration, with ragged tails
+ALIGNED_SHAPES = [(64, 64, 64), (520, 392, 200), (300, 264, 136), (1, 8, 8), (257, 520, 72),
+                  (96, 1040, 8)]
+
+
+@pytest.mark.parametrize("shape", ALIGNED_SHAPES)
+def test_every_config_aligned_shapes(shape):
+    M, N, K = shape
+    a, b = workloads.draw(M, N, K, "uniform", M + N + K)
+    cfgs = configs_for(M, N, K)
+    assert len(cfgs) == g.num_configs()
+    for c in cfgs:
+        check(a, b, config=c, label=f"config {g.config_name(c)}")
+
+
+# K and N that are not multiples of 8 force narrower vectors (staged kernels)
+RAGGED_SHAPES = [(37, 45, 53), (130, 129, 67), (200, 300, 100), (65, 66, 34), (3, 5, 7), (129, 36, 1)]
+
+
+@pytest.mark.parametrize("shape", RAGGED_SHAPES)
+@pytest.mark.parametrize("epilogue", ["none", "relu"])
+def test_ragged_shapes(shape, epilogue):
+    M, N, K = shape
+    a, b = workloads.draw(M, N, K, "uniform", 7 * M + N + K)
+    check(a, b, epilogue, label="auto")
+    for c in configs_for(M, N, K):
+        check(a, b, epilogue, config=c, label=f"config {g.config_name(c)}")
+
+
+def test_misaligned_pointers():
+    # operands and output that start one element into a buffer are only
+    # 2-byte aligned; with K, N not multiples of 8 every vector width drops
+    M, N, K = 70, 90, 40
+    a, b = workloads.draw(M, N, K, "uniform", 11)
+    a_buf = torch.empty(M * K + 1, dtype=torch.float16, device=DEV)
+    a_buf[1:] = a.to(DEV).flatten()
+    a_mis = a_buf[1:].view(M, K)
+    c_buf = torch.empty(M * N + 1, dtype=torch.float16, device=DEV)
+    c_mis = c_buf[1:].view(M, N)
+    assert a_mis.data_ptr() % 4 != 0 and c_mis.data_ptr() % 4 != 0
+    p = g.plan(M, N, K, a_mis.data_ptr(), 1 << 20, c_mis.data_ptr())
+    assert (p["vec_a"], p["vec_c"]) == (1, 1)
+    g.gemm(a_mis, b.to(DEV), out=c_mis)
+    torch.cuda.synchronize()
+    res = oracle.compare(u16(c_mis), oracle.gemm(u16(a), u16(b)))
+    assert res["pass"], res
+
+
+def test_degenerate_dimensions():
+    # K == 0: the empty sum, C = +0 everywhere (also with ReLU)
+    a = torch.empty(33, 0, dtype=torch.float16, device=DEV)
+    b = torch.empty(0, 17, dtype=torch.float16, device=DEV)
+    for epi in ("none", "relu"):
+        c = torch.full((33, 17), 7.0, dtype=torch.float16, device=DEV)
+        g.gemm(a, b, epilogue=epi, out=c)
+        torch.cuda.synchronize()
+        assert np.all(u16(c) == 0)
+    # M == 0 or N == 0: nothing launched, success
+    g.gemm(torch.empty(0, 8, dtype=torch.float16, device=DEV), torch.empty(8, 8, dtype=torch.float16, device=DEV))
+    g.gemm(torch.empty(8, 8, dtype=torch.float16, device=DEV), torch.empty(8, 0, dtype=torch.float16, device=DEV))
+    # single elements
+    a, b = workloads.draw(1, 1, 1, "uniform", 3)
+    check(a, b, label="1x1x1")
+    a, b = workloads.draw(1, 1, 4096, "uniform", 4)
+    check(a, b, label="dot product")
+
+
+def test_no_writes_outside_c():
+    M, N, K = 300, 264, 72
+    a, b = workloads.draw(M, N, K, "uniform", 21)
+    ad, bd = a.to(DEV), b.to(DEV)
+    guard = 4096
+    for c in [g.CONFIG_AUTO] + configs_for(M, N, K):
+        buf = torch.full((M * N + 2 * guard,), -1234.0, dtype=torch.float16, device=DEV)
+        out = buf[guard:guard + M * N].view(M, N)
+        g.gemm(ad, bd, out=out, config=c)
+        torch.cuda.synchronize()
+        host = u16(buf)
+        sentinel = np.float16(-1234.0).view(np.uint16)
+        assert np.all(host[:guard] == sentinel) and np.all(host[guard + M * N:] == sentinel), c
+        res = oracle.compare(host[guard:guard + M * N].reshape(M, N), oracle.gemm(u16(a), u16(b)))
+        assert res["pass"], (c, res)
+
+
+def test_exact_cases_bit_identical():
+    # identity: I . B == B exactly; integer operands: exact integer products
+    n = 264
+    _, b = workloads.draw(n, 200, n, "uniform", 5)
+    eye = torch.eye(n, dtype=torch.float16)
+    assert np.array_equal(run(eye, b), u16(b))
+    for c in configs_for(n, 200, n):
+        assert np.array_equal(run(eye, b, config=c), u16(b)), c
+    M, N, K = 3000, 5000, 4100
+    a, b = workloads.draw_ints(M, N, K, seed=8, lo=-2, hi=2)
+    got = run(a, b)
+    exact = (a.double() @ b.double()).to(torch.float16)     # |C| <= 4K < 2^24: fp64 is exact
+    assert np.array_equal(got, u16(exact))
+
+
+def test_relu_equals_max_of_plain():
+    a, b = workloads.draw(520, 392, 200, "uniform", 12)
+    for c in configs_for(520, 392, 200):
+        plain = run(a, b, "none", c)
+        relu = run(a, b, "relu", c)
+        neg = (plain & 0x8000) != 0
+        assert np.array_equal(relu[~neg], plain[~neg]) and np.all(relu[neg] == 0), c
+
+
+def test_deterministic():
+    a, b = workloads.draw(1000, 1100, 900, "normal", 13)
+    ad, bd = a.to(DEV), b.to(DEV)
+    first = u16(g.gemm(ad, bd))
+    for _ in range(3):
+        assert np.array_equal(u16(g.gemm(ad, bd)), first)
+
+
+# ---- the benchmark workloads, in the configuration the benchmark launches ----
+
+@pytest.mark.parametrize("name", ["gemm_256", "gemm_1024_relu", "gemm_4096", "gemm_ragged_3000x5000x4100"])
+def test_workload_full(name):
+    w = workloads.WORKLOADS[name]
+    a, b = workloads.make_inputs(w)
+    res = check(a, b, "relu" if w.relu else "none", label=name)
+    print(f"[parity] {name}: {res}", flush=True)
+
+
+@pytest.mark.parametrize("name", ["gemm_8192", "gemm_mlp_8192x28672x8192"])
+def test_workload_sampled(name):
+    w = workloads.WORKLOADS[name]
+    a, b = workloads.make_inputs(w)
+    rows, cols = workloads.sample_indices(w)
+    print(f"[parity] {name}: gemm on GPU", flush=True)
+    c = g.gemm(a.to(DEV), b.to(DEV))
+    torch.cuda.synchronize()
+    got = u16(c[rows.to(DEV)][:, cols.to(DEV)])
+    del c
+    print(f"[parity] {name}: oracle on {oracle.cpu_threads()} threads", flush=True)
+    ref = oracle.gemm_sampled(u16(a), u16(b), rows.numpy(), cols.numpy())
+    res = oracle.compare(got, ref)
+    print(f"[parity] {name}: {res}", flush=True)
+    assert res["pass"], res
+    # tile-edge rows and columns of the output, checked separately
+    edge_r = np.array(sorted({0, 1, 255, 256, w.M - 1}))
+    edge_c = np.array(sorted({0, 1, 255, 256, w.N - 1}))
+    c = g.gemm(a.to(DEV), b.to(DEV))
+    torch.cuda.synchronize()
+    got = u16(c[torch.from_numpy(edge_r).to(DEV)][:, torch.from_numpy(edge_c).to(DEV)])
+    res = oracle.compare(got, oracle.gemm_sampled(u16(a), u16(b), edge_r, edge_c))
+    assert res["pass"], res

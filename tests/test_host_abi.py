@@ -1,0 +1,166 @@
+"""CPU tests of the C ABI: symbols, argument validation, planning.
+
+No kernel is launched: validation and planning run before any HIP call, so
+these run on a machine without a GPU.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import tiled_dense_gemm_fp16_amd as g
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gemm_f16.h")
+GOLDEN = os.path.join(ROOT, "tests", "golden", "smem_budget.txt")
+
+# an address aligned to 256 bytes that is never dereferenced (validation only)
+FAKE = 1 << 20
+
+
+@pytest.fixture(scope="module", autouse=True)
+def built():
+    if not os.path.exists(g.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gemm_f16\w*)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert {"gemm_f16", "gemm_f16_ex", "gemm_f16_plan", "gemm_f16_status_string"} <= set(names)
+    lib = ctypes.CDLL(g.LIB_PATH)
+    for name in names:
+        assert hasattr(lib, name), f"{name} declared in gemm_f16.h but not exported"
+    # and the binding describes exactly the declared functions
+    assert set(g.SIGNATURES) == set(names)
+
+
+def test_status_strings():
+    for st in range(0, 7):
+        assert g.status_string(st) != "unknown status"
+    assert g.status_string(99) == "unknown status"
+
+
+def test_config_table():
+    n = g.num_configs()
+    assert n >= 2
+    names = [g.config_name(c) for c in range(n)]
+    assert all(names) and len(set(names)) == n
+    assert g.config_name(n) is None and g.config_name(-1) is None
+    for c in range(n):
+        p = g.plan(4096, 4096, 4096, FAKE, FAKE, FAKE, config=c)
+        assert p["config"] == c
+        assert p["lds_bytes"] <= 163840                     # MI355X LDS per workgroup
+        assert p["lds_bytes"] == g.stage_bytes(p["block_m"], p["block_n"], p["block_k"], p["stages"])
+        assert p["threads"] == 256
+
+
+def _golden_rows():
+    rows, trips = [], []
+    for line in open(GOLDEN):
+        line = line.split("#")[0].strip()
+        if not line:
+            continue
+        f = line.split()
+        if f[0] == "ktrip":
+            trips.append(tuple(int(x) for x in f[1:4]))
+        else:
+            rows.append(tuple(int(x) for x in f[:5]))
+    return rows, trips
+
+
+def test_shared_memory_budget_matches_pages():
+    rows, trips = _golden_rows()
+    assert len(rows) == 6 and len(trips) == 1
+    for bm, bn, bk, s, expected in rows:
+        assert g.stage_bytes(bm, bn, bk, s) == expected
+    assert g.stage_bytes(-1, 1, 1, 1) == -1
+    # the pages' H100 remark: 228 KB holds two 96 KB blocks; MI355X's 160 KiB holds one
+    assert 228 * 1024 // g.stage_bytes(128, 128, 64, 3) == 2
+    assert 163840 // g.stage_bytes(128, 128, 64, 3) == 1
+    for K, bk, iters in trips:
+        # a configuration with the pages' block_K reports the same trip count
+        cfgs = [c for c in range(g.num_configs()) if g.plan(K, K, K, FAKE, FAKE, FAKE, config=c)["block_k"] == bk]
+        assert cfgs
+        for c in cfgs:
+            assert g.plan(K, K, K, FAKE, FAKE, FAKE, config=c)["k_tiles"] == iters
+
+
+def test_plan_geometry_and_vector_widths():
+    p = g.plan(3000, 5000, 4100, FAKE, FAKE, FAKE)
+    assert p["tiles_m"] == -(-3000 // p["block_m"]) and p["tiles_n"] == -(-5000 // p["block_n"])
+    assert p["grid"] == p["tiles_m"] * p["tiles_n"]
+    assert p["k_tiles"] == -(-4100 // p["block_k"])
+    assert p["vec_a"] == 4                       # K = 4100: rows only 8-byte aligned
+    assert p["vec_b"] == 8 and p["vec_c"] == 4
+    assert p["direct_lds"] == 0                  # 16-byte direct loads need 16-byte rows
+    assert p["flops"] == 2.0 * 3000 * 5000 * 4100
+    assert p["min_bytes"] == 2.0 * (3000 * 4100 + 4100 * 5000 + 3000 * 5000)
+    # odd pitches and 2-byte-aligned pointers
+    p = g.plan(33, 17, 9, FAKE + 2, FAKE + 6, FAKE + 2)
+    assert (p["vec_a"], p["vec_b"], p["vec_c"]) == (1, 1, 1)
+    p = g.plan(64, 64, 64, FAKE + 4, FAKE + 8, FAKE)
+    assert (p["vec_a"], p["vec_b"], p["vec_c"]) == (2, 4, 4)
+    # large aligned problems take a direct-to-LDS configuration
+    assert g.plan(8192, 8192, 8192, FAKE, FAKE, FAKE)["direct_lds"] == 1
+    # a direct configuration refuses a misaligned pitch
+    direct = [c for c in range(g.num_configs()) if g.plan(64, 64, 64, FAKE, FAKE, FAKE, config=c)["direct_lds"]]
+    with pytest.raises(g.GemmError):
+        g.plan(64, 64, 68, FAKE, FAKE, FAKE, config=direct[0])
+
+
+@pytest.mark.parametrize("args,status", [
+    ((-1, 4, 4, FAKE, FAKE, FAKE * 2), 1),                   # negative dimension
+    ((4, -1, 4, FAKE, FAKE, FAKE * 2), 1),
+    ((4, 4, -1, FAKE, FAKE, FAKE * 2), 1),
+    ((4, 4, 4, 0, FAKE, FAKE * 2), 1),                       # null A with elements
+    ((4, 4, 4, FAKE, 0, FAKE * 2), 1),                       # null B
+    ((4, 4, 4, FAKE, FAKE * 3, 0), 1),                       # null C
+    ((4, 4, 4, FAKE + 1, FAKE * 3, FAKE * 2), 2),            # odd pointer
+    ((4, 4, 4, FAKE, FAKE * 3 + 1, FAKE * 2), 2),
+    ((4, 4, 4, FAKE, FAKE * 3, FAKE * 2 + 1), 2),
+    ((4, 4, 4, FAKE, FAKE * 3, FAKE + 8), 1),                # C overlaps A
+    ((4, 4, 4, FAKE, FAKE * 3, FAKE * 3 - 2), 1),            # C's last element overlaps B's first
+    ((4, (1 << 22) + 1, 4, FAKE, FAKE * 3, FAKE * 2), 6),    # N beyond the limit
+    ((4, 4, (1 << 22) + 1, FAKE, FAKE * 3, FAKE * 2), 6),    # K beyond the limit
+    ((1 << 31, 4, 4, FAKE, FAKE * 3, FAKE * 2), 6),          # M beyond int32
+])
+def test_invalid_arguments_rejected_before_any_launch(args, status):
+    M, N, K, A, B, C = args
+    assert g.gemm_f16_raw(M, N, K, A, B, C, 0) == status
+    assert g.gemm_f16_raw(M, N, K, A, B, C, 0, config=0) == status
+
+
+def test_bad_epilogue_and_config():
+    assert g.gemm_f16_raw(4, 4, 4, FAKE, FAKE * 3, FAKE * 2, 2) == 1
+    assert g.gemm_f16_raw(4, 4, 4, FAKE, FAKE * 3, FAKE * 2, -1) == 1
+    assert g.gemm_f16_raw(4, 4, 4, FAKE, FAKE * 3, FAKE * 2, 0, config=g.num_configs()) == 1
+    assert g.gemm_f16_raw(4, 4, 4, FAKE, FAKE * 3, FAKE * 2, 0, config=-2) == 1
+    with pytest.raises(g.GemmError):
+        g.plan(4, 4, 4, FAKE, FAKE, FAKE, config=99)
+
+
+def test_empty_outputs_succeed_without_a_device():
+    # M == 0 or N == 0: nothing to do, no HIP call, so this works on a CPU host too
+    assert g.gemm_f16_raw(0, 5, 7, 0, FAKE, 0, 0) == 0
+    assert g.gemm_f16_raw(5, 0, 7, FAKE, 0, 0, 1) == 0
+    assert g.gemm_f16_raw(0, 0, 0, 0, 0, 0, 0) == 0
+
+
+def test_python_wrapper_argument_checks():
+    import torch
+
+    a = torch.zeros(4, 4, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        g.gemm(a, a, epilogue="gelu")
+    with pytest.raises(ValueError):
+        g.gemm(a, a)                                           # CPU tensors
+    with pytest.raises(ValueError):
+        g.gemm(a.float(), a)

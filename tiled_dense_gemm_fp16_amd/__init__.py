@@ -1,0 +1,155 @@
+"""Python binding of the gfx950 FP16 GEMM library (libgemm_f16.so).
+
+Argument marshalling only: every step of C = epi(A . B) runs in the HIP
+kernels behind the C ABI declared in ``include/gemm_f16.h``.  PyTorch is
+used for device memory and streams.  There is no fallback: if the library
+has not been built, or the GPU is not a gfx950, calls raise.
+
+The tile program this implements is the GEMM of "TileLang：比 Triton 低一层的
+tile 语言" (section "第一个 kernel：GEMM"): C is returned as a new tensor
+unless ``out`` is given, as the pages' kernels allocate their output.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgemm_f16.so")
+
+SUCCESS = 0
+EPILOGUE_NONE = 0
+EPILOGUE_RELU = 1
+CONFIG_AUTO = -1
+_EPILOGUES = {"none": EPILOGUE_NONE, "relu": EPILOGUE_RELU}
+
+# exported symbols and their ctypes signatures (mirrors include/gemm_f16.h)
+_i64, _vp, _int = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+
+
+class Plan(ctypes.Structure):
+    """gemm_f16_plan_t: how a call would run."""
+    _fields_ = [
+        ("config", ctypes.c_int32), ("block_m", ctypes.c_int32), ("block_n", ctypes.c_int32),
+        ("block_k", ctypes.c_int32), ("stages", ctypes.c_int32), ("threads", ctypes.c_int32),
+        ("direct_lds", ctypes.c_int32), ("vec_a", ctypes.c_int32), ("vec_b", ctypes.c_int32),
+        ("vec_c", ctypes.c_int32), ("tiles_m", ctypes.c_int64), ("tiles_n", ctypes.c_int64),
+        ("grid", ctypes.c_int64), ("k_tiles", ctypes.c_int64), ("lds_bytes", ctypes.c_int64),
+        ("flops", ctypes.c_double), ("min_bytes", ctypes.c_double),
+    ]
+
+    def as_dict(self) -> dict:
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+SIGNATURES = {
+    "gemm_f16": ([_i64, _i64, _i64, _vp, _vp, _vp, _int, _vp], _int),
+    "gemm_f16_ex": ([_i64, _i64, _i64, _vp, _vp, _vp, _int, _int, _vp], _int),
+    "gemm_f16_plan": ([_i64, _i64, _i64, _vp, _vp, _vp, _int, ctypes.POINTER(Plan)], _int),
+    "gemm_f16_num_configs": ([], _int),
+    "gemm_f16_config_name": ([_int], ctypes.c_char_p),
+    "gemm_f16_stage_bytes": ([_i64, _i64, _i64, _i64], _i64),
+    "gemm_f16_status_string": ([_int], ctypes.c_char_p),
+}
+
+_lib = None
+
+
+class GemmError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: status {status} ({status_string(status)})")
+
+
+def lib() -> ctypes.CDLL:
+    """Load libgemm_f16.so (built in-tree by ``__graft_entry__.build()``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build the HIP library first "
+                               "(python -c 'import __graft_entry__ as g; g.build()')")
+        h = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in SIGNATURES.items():
+            fn = getattr(h, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = h
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().gemm_f16_status_string(int(status)).decode()
+
+
+def num_configs() -> int:
+    return int(lib().gemm_f16_num_configs())
+
+
+def config_name(config: int) -> str | None:
+    s = lib().gemm_f16_config_name(int(config))
+    return s.decode() if s is not None else None
+
+
+def stage_bytes(block_m: int, block_n: int, block_k: int, stages: int) -> int:
+    return int(lib().gemm_f16_stage_bytes(block_m, block_n, block_k, stages))
+
+
+def plan(M: int, N: int, K: int, A_ptr: int = 0, B_ptr: int = 0, C_ptr: int = 0,
+         config: int = CONFIG_AUTO) -> dict:
+    """How gemm_f16 would run this shape (pure host logic, no GPU needed).
+    Pointers only matter for alignment; 0 stands for an aligned buffer."""
+    p = Plan()
+    st = lib().gemm_f16_plan(M, N, K, A_ptr or None, B_ptr or None, C_ptr or None, config,
+                             ctypes.byref(p))
+    if st != SUCCESS:
+        raise GemmError(st, "gemm_f16_plan")
+    return p.as_dict()
+
+
+def gemm_f16_raw(M: int, N: int, K: int, A_ptr: int, B_ptr: int, C_ptr: int, epilogue: int = 0,
+                 stream: int = 0, config: int = CONFIG_AUTO) -> int:
+    """Call the C entry point with raw device addresses; returns the status code."""
+    if config == CONFIG_AUTO:
+        return int(lib().gemm_f16(M, N, K, A_ptr or None, B_ptr or None, C_ptr or None, epilogue,
+                                  stream or None))
+    return int(lib().gemm_f16_ex(M, N, K, A_ptr or None, B_ptr or None, C_ptr or None, epilogue,
+                                 config, stream or None))
+
+
+def gemm(a, b, epilogue: str = "none", out=None, config: int = CONFIG_AUTO, stream=None):
+    """C = epi(a @ b) for 2-D contiguous float16 CUDA (HIP) tensors a (M x K), b (K x N).
+
+    Returns ``out`` (allocated as an M x N float16 tensor when not given).  The
+    kernel is enqueued on ``stream`` (default: torch's current stream) and the
+    call returns without synchronising.
+    """
+    import torch
+
+    if epilogue not in _EPILOGUES:
+        raise ValueError(f"epilogue must be one of {sorted(_EPILOGUES)}, got {epilogue!r}")
+    for name, t in (("a", a), ("b", b)):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.float16 or t.dim() != 2:
+            raise ValueError(f"{name} must be a 2-D torch.float16 tensor")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous (row-major)")
+    M, K = a.shape
+    K2, N = b.shape
+    if K != K2:
+        raise ValueError(f"inner dimensions differ: a is {tuple(a.shape)}, b is {tuple(b.shape)}")
+    if a.device != b.device:
+        raise ValueError("a and b are on different devices")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=a.device)
+    elif (out.dtype != torch.float16 or tuple(out.shape) != (M, N) or not out.is_contiguous()
+          or out.device != a.device):
+        raise ValueError(f"out must be a contiguous float16 tensor of shape {(M, N)} on {a.device}")
+    if stream is None:
+        stream = torch.cuda.current_stream(a.device)
+    with torch.cuda.device(a.device):
+        st = gemm_f16_raw(M, N, K, a.data_ptr(), b.data_ptr(), out.data_ptr(), _EPILOGUES[epilogue],
+                          stream.cuda_stream, config)
+    if st != SUCCESS:
+        raise GemmError(st, "gemm_f16")
+    return out

@@ -1,0 +1,260 @@
+// gemm_f16_api.cpp -- the C ABI of the FP16 GEMM library: argument
+// validation, kernel planning and launch.  Validation and planning make no
+// HIP call, so they behave identically with or without a GPU.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "gemm_f16.h"
+#include "gemm_f16_internal.h"
+
+namespace gemm_f16_impl {
+
+const ConfigDesc kConfigs[kNumConfigs] = {
+    {"256x256x64_s2_direct", 256, 256, 64, 2, true},
+    {"256x128x64_s3_direct", 256, 128, 64, 3, true},
+    {"128x128x64_s3_direct", 128, 128, 64, 3, true},
+    {"128x128x32_s2_staged", 128, 128, 32, 2, false},
+    {"64x64x64_s2_staged", 64, 64, 64, 2, false},
+};
+
+namespace {
+
+constexpr int kComputeUnits = 256;   // MI355X
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Largest vector width v in {8, 4, 2, 1} such that every row of a matrix
+// with row pitch `pitch` elements starting at `p` is 2v-byte aligned.
+int vec_width(const void *p, int64_t pitch)
+{
+    uintptr_t addr = (uintptr_t)p;
+    for (int v = 8; v > 1; v /= 2)
+        if (pitch % v == 0 && addr % (uintptr_t)(2 * v) == 0)
+            return v;
+    return 1;
+}
+
+bool overlaps(const void *a, int64_t a_bytes, const void *b, int64_t b_bytes)
+{
+    if (a_bytes <= 0 || b_bytes <= 0)
+        return false;
+    uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + (uintptr_t)b_bytes && b0 < a0 + (uintptr_t)a_bytes;
+}
+
+gemm_f16_status_t validate(int64_t M, int64_t N, int64_t K, const void *A, const void *B,
+                           const void *C, bool check_c_overlap)
+{
+    if (M < 0 || N < 0 || K < 0)
+        return GEMM_F16_ERROR_INVALID_VALUE;
+    if (M > GEMM_F16_MAX_DIM || N > GEMM_F16_MAX_N || K > GEMM_F16_MAX_K)
+        return GEMM_F16_ERROR_UNSUPPORTED_SIZE;
+    const bool a_nonempty = M > 0 && K > 0, b_nonempty = K > 0 && N > 0, c_nonempty = M > 0 && N > 0;
+    if ((a_nonempty && !A) || (b_nonempty && !B) || (c_nonempty && !C))
+        return GEMM_F16_ERROR_INVALID_VALUE;
+    if (((uintptr_t)A | (uintptr_t)B | (uintptr_t)C) & 1u)
+        return GEMM_F16_ERROR_MISALIGNED;
+    if (check_c_overlap && c_nonempty &&
+        (overlaps(C, 2 * M * N, A, a_nonempty ? 2 * M * K : 0) ||
+         overlaps(C, 2 * M * N, B, b_nonempty ? 2 * K * N : 0)))
+        return GEMM_F16_ERROR_INVALID_VALUE;
+    return GEMM_F16_SUCCESS;
+}
+
+// Relative MFMA throughput a workgroup of each configuration sustains
+// (larger tiles reuse each LDS byte more).  Used only to rank configurations.
+double config_efficiency(int c)
+{
+    switch (c) {
+    case 0: return 1.00;
+    case 1: return 0.92;
+    case 2: return 0.80;
+    case 3: return 0.55;
+    default: return 0.35;
+    }
+}
+
+bool config_fits(int c, int va, int vb)
+{
+    return !kConfigs[c].direct || (va == 8 && vb == 8);
+}
+
+void fill_plan(int c, int64_t M, int64_t N, int64_t K, int va, int vb, int vc, gemm_f16_plan_t *p)
+{
+    const ConfigDesc &d = kConfigs[c];
+    memset(p, 0, sizeof(*p));
+    p->config = c;
+    p->block_m = d.block_m;
+    p->block_n = d.block_n;
+    p->block_k = d.block_k;
+    p->stages = d.stages;
+    p->threads = 256;
+    p->direct_lds = d.direct ? 1 : 0;
+    p->vec_a = d.direct ? 8 : va;
+    p->vec_b = d.direct ? 8 : vb;
+    p->vec_c = vc;
+    p->tiles_m = ceil_div(M, d.block_m);
+    p->tiles_n = ceil_div(N, d.block_n);
+    p->grid = p->tiles_m * p->tiles_n;
+    p->k_tiles = ceil_div(K, d.block_k);
+    p->lds_bytes = gemm_f16_stage_bytes(d.block_m, d.block_n, d.block_k, d.stages);
+    p->flops = 2.0 * (double)M * (double)N * (double)K;
+    p->min_bytes = 2.0 * ((double)M * K + (double)K * N + (double)M * N);
+}
+
+// Pick the configuration with the lowest modelled time: full rounds of
+// workgroups over the 256 CUs times the tile's work at its efficiency.
+int choose_config(int64_t M, int64_t N, int va, int vb)
+{
+    int best = -1;
+    double best_t = 0.0;
+    for (int c = 0; c < kNumConfigs; ++c) {
+        if (!config_fits(c, va, vb))
+            continue;
+        const ConfigDesc &d = kConfigs[c];
+        int64_t grid = ceil_div(M, d.block_m) * ceil_div(N, d.block_n);
+        double rounds = (double)ceil_div(grid, kComputeUnits);
+        double t = rounds * (double)d.block_m * (double)d.block_n / config_efficiency(c);
+        if (best < 0 || t < best_t * 0.999) {
+            best = c;
+            best_t = t;
+        }
+    }
+    return best;
+}
+
+gemm_f16_status_t make_plan(int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *C,
+                            int config, gemm_f16_plan_t *plan)
+{
+    if (config != GEMM_F16_CONFIG_AUTO && (config < 0 || config >= kNumConfigs))
+        return GEMM_F16_ERROR_INVALID_VALUE;
+    const int va = vec_width(A, K), vb = vec_width(B, N);
+    const int vc = (N % 4 == 0 && (uintptr_t)C % 8 == 0) ? 4 : 1;
+    int c = config == GEMM_F16_CONFIG_AUTO ? choose_config(M, N, va, vb) : config;
+    if (!config_fits(c, va, vb))
+        return GEMM_F16_ERROR_INVALID_VALUE;
+    fill_plan(c, M, N, K, va, vb, vc, plan);
+    if (plan->grid > 0x7fffffff)
+        return GEMM_F16_ERROR_UNSUPPORTED_SIZE;
+    return GEMM_F16_SUCCESS;
+}
+
+// Per-device check that the device is gfx950, done once per device.
+constexpr int kMaxDevices = 64;
+std::mutex g_dev_mutex;
+int g_dev_state[kMaxDevices];   // 0 unknown, 1 gfx950, 2 other
+
+gemm_f16_status_t check_device()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+        return GEMM_F16_ERROR_NO_DEVICE;
+    if (dev >= kMaxDevices)
+        return GEMM_F16_ERROR_UNSUPPORTED_DEVICE;
+    std::lock_guard<std::mutex> lock(g_dev_mutex);
+    if (g_dev_state[dev] == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+            return GEMM_F16_ERROR_NO_DEVICE;
+        g_dev_state[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    }
+    return g_dev_state[dev] == 1 ? GEMM_F16_SUCCESS : GEMM_F16_ERROR_UNSUPPORTED_DEVICE;
+}
+
+gemm_f16_status_t run(int64_t M, int64_t N, int64_t K, const void *A, const void *B, void *C, int epilogue,
+                      int config, void *stream)
+{
+    gemm_f16_status_t st = validate(M, N, K, A, B, C, true);
+    if (st != GEMM_F16_SUCCESS)
+        return st;
+    if (epilogue != GEMM_F16_EPILOGUE_NONE && epilogue != GEMM_F16_EPILOGUE_RELU)
+        return GEMM_F16_ERROR_INVALID_VALUE;
+    gemm_f16_plan_t plan;
+    st = make_plan(M, N, K, A, B, C, config, &plan);
+    if (st != GEMM_F16_SUCCESS)
+        return st;
+    if (M == 0 || N == 0)
+        return GEMM_F16_SUCCESS;
+    st = check_device();
+    if (st != GEMM_F16_SUCCESS)
+        return st;
+    KernelArgs a;
+    a.A = (const _Float16 *)A;
+    a.B = (const _Float16 *)B;
+    a.C = (_Float16 *)C;
+    a.M = (int)M;
+    a.N = (int)N;
+    a.K = (int)K;
+    a.tiles_m = (int)plan.tiles_m;
+    a.tiles_n = (int)plan.tiles_n;
+    a.group_m = 8;
+    a.relu = epilogue == GEMM_F16_EPILOGUE_RELU ? 1 : 0;
+    a.vec_c = plan.vec_c;
+    hipError_t e = launch(plan.config, a, plan.vec_a, plan.vec_b, plan.grid, (hipStream_t)stream);
+    return e == hipSuccess ? GEMM_F16_SUCCESS : GEMM_F16_ERROR_LAUNCH_FAILED;
+}
+
+} // namespace
+} // namespace gemm_f16_impl
+
+using namespace gemm_f16_impl;
+
+extern "C" {
+
+gemm_f16_status_t gemm_f16(int64_t M, int64_t N, int64_t K, const void *A, const void *B, void *C,
+                           int epilogue, void *stream)
+{
+    return run(M, N, K, A, B, C, epilogue, GEMM_F16_CONFIG_AUTO, stream);
+}
+
+gemm_f16_status_t gemm_f16_ex(int64_t M, int64_t N, int64_t K, const void *A, const void *B, void *C,
+                              int epilogue, int config, void *stream)
+{
+    return run(M, N, K, A, B, C, epilogue, config, stream);
+}
+
+gemm_f16_status_t gemm_f16_plan(int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *C,
+                                int config, gemm_f16_plan_t *plan)
+{
+    if (!plan)
+        return GEMM_F16_ERROR_INVALID_VALUE;
+    gemm_f16_status_t st = validate(M, N, K, A, B, C, false);
+    if (st != GEMM_F16_SUCCESS)
+        return st;
+    return make_plan(M, N, K, A, B, C, config, plan);
+}
+
+int gemm_f16_num_configs(void) { return kNumConfigs; }
+
+const char *gemm_f16_config_name(int config)
+{
+    if (config < 0 || config >= kNumConfigs)
+        return nullptr;
+    return kConfigs[config].name;
+}
+
+int64_t gemm_f16_stage_bytes(int64_t block_m, int64_t block_n, int64_t block_k, int64_t stages)
+{
+    if (block_m < 0 || block_n < 0 || block_k < 0 || stages < 0)
+        return -1;
+    return stages * 2 * block_k * (block_m + block_n);
+}
+
+const char *gemm_f16_status_string(gemm_f16_status_t status)
+{
+    switch (status) {
+    case GEMM_F16_SUCCESS: return "success";
+    case GEMM_F16_ERROR_INVALID_VALUE: return "invalid value";
+    case GEMM_F16_ERROR_MISALIGNED: return "pointer not 2-byte aligned";
+    case GEMM_F16_ERROR_NO_DEVICE: return "no HIP device";
+    case GEMM_F16_ERROR_UNSUPPORTED_DEVICE: return "device is not gfx950";
+    case GEMM_F16_ERROR_LAUNCH_FAILED: return "kernel launch failed";
+    case GEMM_F16_ERROR_UNSUPPORTED_SIZE: return "size beyond the library's limits";
+    }
+    return "unknown status";
+}
+
+} // extern "C"

@@ -1,0 +1,42 @@
+// gemm_f16_internal.h -- shared between the host API (gemm_f16_api.cpp) and
+// the gfx950 kernels (gemm_f16_kernels.hip).  Not part of the public ABI.
+#ifndef GEMM_F16_INTERNAL_H
+#define GEMM_F16_INTERNAL_H
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gemm_f16_impl {
+
+// Kernel arguments, passed by value.  All dimensions fit in int32 (the public
+// API limits M, N, K to 2^31 - 1 and K, N to 2^22).
+struct KernelArgs {
+    const _Float16 *A;   // M x K, row-major
+    const _Float16 *B;   // K x N, row-major
+    _Float16 *C;         // M x N, row-major
+    int M, N, K;
+    int tiles_m, tiles_n;
+    int group_m;         // tile rows walked together by the tile remap
+    int relu;            // 1: max(acc, 0) before the fp16 conversion
+    int vec_c;           // 4: 8-byte stores of C are aligned; 1: 2-byte stores
+};
+
+// Static description of one compiled kernel configuration.
+struct ConfigDesc {
+    const char *name;
+    int block_m, block_n, block_k;
+    int stages;
+    bool direct;          // operands move global -> LDS with buffer_load ... lds
+};
+
+constexpr int kNumConfigs = 5;
+extern const ConfigDesc kConfigs[kNumConfigs];
+
+// Launch configuration `config` with `grid` workgroups of 256 threads on `s`.
+// va / vb: elements per global load of A / B (8, 4, 2 or 1; direct configs
+// require 8).  Returns the launch status.
+hipError_t launch(int config, const KernelArgs &a, int va, int vb, int64_t grid, hipStream_t s);
+
+} // namespace gemm_f16_impl
+
+#endif

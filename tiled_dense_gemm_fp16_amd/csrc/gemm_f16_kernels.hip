@@ -1,0 +1,539 @@
+// gemm_f16_kernels.hip -- gfx950 kernels of the tiled FP16 GEMM C = epi(A . B).
+//
+// One workgroup computes one bM x bN output tile, as in the tile program of
+// "TileLang：比 Triton 低一层的 tile 语言" (section "第一个 kernel：GEMM"):
+// an fp32 accumulator fragment held in registers, a K loop over bK-deep
+// slices of A and B staged through a multi-stage shared-memory (LDS) ring so
+// that the loads of later slices overlap the math on the current one
+// (section "练习", exercises 1-2, on stage counts and their memory cost), and
+// a final copy that applies the optional ReLU ("TileLang：让GPU编程像Python一样
+// 简单的高性能计算新范式", section "并行计算的优雅表达") and rounds to fp16
+// ("5分钟上手TileLang：GPU内核开发指南", section "避坑与调参").
+//
+// What is CDNA4-specific (the pages' Hopper design -- TMA, wgmma, mbarrier
+// producer/consumer warpgroups -- does not exist here):
+//  * 256 threads = 4 wave64s in a WM x WN grid; each wave owns a
+//    (bM/WM) x (bN/WN) sub-tile made of 32x32 blocks computed with
+//    v_mfma_f32_32x32x16_f16 into fp32 accumulators.
+//  * The MFMA computes the transposed tile C^T = B^T . A^T: its first operand
+//    is a 32(n) x 16(k) slice of B^T and its second a 16(k) x 32(m) slice of
+//    A^T, so every lane ends up holding four consecutive n of one output row
+//    and writes them with one 8-byte store.
+//  * A is staged in LDS as [m][k] (k contiguous) and read with ds_read_b128.
+//    B is staged as it lies in memory, [k][n] (n contiguous), and read with
+//    gfx950's transposing ds_read_b64_tr_b16, which hands each lane four k
+//    values of one column n.  Both LDS tiles are XOR-swizzled in 16-byte
+//    chunks (no padding) to spread the reads over the LDS banks.
+//  * "direct" kernels move operands global -> LDS with 16-byte
+//    buffer_load ... lds (no registers, no LDS-write instructions); "staged"
+//    kernels load through registers with 16/8/4/2-byte vectors and serve
+//    pitches or pointers that are not 16-byte aligned.
+//  * All global accesses are raw buffer instructions whose descriptor bounds
+//    the matrix panel the workgroup touches: out-of-range rows read as zero
+//    and out-of-range stores are dropped by the hardware; columns past the
+//    row end are masked explicitly (they would otherwise wrap to the next row).
+//  * Workgroup ids are remapped so that each XCD (own L2) receives a
+//    contiguous range of tiles, walked in groups of GROUP_M tile rows.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gemm_f16_internal.h"
+
+namespace gemm_f16_impl {
+
+typedef _Float16 half_t;
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef float float16v __attribute__((ext_vector_type(16)));
+typedef int int4v __attribute__((ext_vector_type(4)));
+typedef int int2v __attribute__((ext_vector_type(2)));
+
+#define LDS_AS __attribute__((address_space(3)))
+
+// Descriptor word 3 for gfx9-family raw buffers (untyped, 32-bit dwords).
+constexpr int kBufferFlags = 0x00020000;
+// Bit 31 set in a voffset puts it at or beyond every descriptor's
+// num_records (panels never exceed 2 GiB): reads give 0, writes are dropped.
+// It is OR-ed in arithmetically so that the compiler keeps one straight-line
+// instruction instead of branching around each access.
+constexpr uint32_t kOob = 0x80000000u;
+__device__ __forceinline__ uint32_t oob_unless(bool ok) { return (uint32_t)(!ok) << 31; }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             kBufferFlags);
+}
+
+// s_waitcnt vmcnt(n) leaving expcnt and lgkmcnt unconstrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// ---- LDS swizzles ---------------------------------------------------------
+// A tile: rows of BK halves = BK/8 chunks of 16 bytes.  ds_read_b128 of a
+// fragment touches 32 consecutive rows at one logical chunk; the XOR makes
+// any 8 consecutive rows land in 8 different 16-byte bank groups.
+template <int CHUNKS>
+__device__ __forceinline__ int swz_a(int row)
+{
+    if constexpr (CHUNKS >= 8)
+        return row & 7;
+    else if constexpr (CHUNKS == 4)
+        return (row >> 1) & 3;
+    else if constexpr (CHUNKS == 2)
+        return (row >> 2) & 1;
+    else
+        return 0;
+}
+
+// B tile: rows of BN halves.  A transposing read covers 4 consecutive rows x
+// 32 bytes per 16-lane group; XOR-ing chunk bits 1-2 with the row's low two
+// bits puts those 16 eight-byte pieces on 16 different bank pairs.
+template <int CHUNKS>
+__device__ __forceinline__ int swz_b(int row)
+{
+    return (2 * (row & 3)) & (CHUNKS - 1);
+}
+
+// ---- tile index remap -----------------------------------------------------
+// Workgroups are handed to the 8 XCDs round-robin (id % 8).  Give XCD x a
+// contiguous block of logical tile ids so its L2 sees neighbouring tiles, then
+// walk tiles GROUP_M rows at a time (column-major inside the group) so that
+// concurrently running tiles share A row-panels and B column-panels.
+__device__ __forceinline__ void tile_coords(int wg, int grid, int tiles_m, int tiles_n, int group_m,
+                                            int &tm, int &tn)
+{
+    constexpr int kXcds = 8;
+    int per = grid / kXcds, rem = grid % kXcds;
+    int xcd = wg % kXcds, local = wg / kXcds;
+    int id = (xcd < rem) ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
+    int width = group_m * tiles_n;
+    int group = id / width;
+    int first_m = group * group_m;
+    int gm = min(tiles_m - first_m, group_m);
+    int in_group = id - group * width;
+    tm = first_m + in_group % gm;
+    tn = in_group / gm;
+}
+
+// ---- the kernel -------------------------------------------------------------
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool DIRECT, int VA, int VB>
+struct Tile {
+    static constexpr int kThreads = 256;
+    static constexpr int kWaves = 4;
+    static_assert(WM * WN == kWaves, "4 waves");
+    static constexpr int WTM = BM / WM;              // wave sub-tile rows (m)
+    static constexpr int WTN = BN / WN;              // wave sub-tile cols (n)
+    static constexpr int TM = WTM / 32;              // 32x32 MFMA blocks per wave along m
+    static constexpr int TN = WTN / 32;              // ... along n
+    static_assert(TM >= 1 && TN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
+    static_assert(BK % 16 == 0, "BK multiple of the MFMA depth");
+    static constexpr int CA = BK / 8;                // 16-byte chunks per A row in LDS
+    static constexpr int CB = BN / 8;                // 16-byte chunks per B row in LDS
+    static_assert(CB >= 4 && (CB & (CB - 1)) == 0, "B row chunks: power of two >= 4");
+    static_assert((CA & (CA - 1)) == 0, "A row chunks: power of two");
+    static constexpr int A_STAGE = BM * BK;          // halves
+    static constexpr int B_STAGE = BK * BN;
+    static constexpr int LDS_BYTES = STAGES * (A_STAGE + B_STAGE) * 2;
+    static_assert(LDS_BYTES <= 163840, "LDS budget");
+    // direct loads: one wave instruction fills 1 KiB of LDS
+    static constexpr int A_DMA = A_STAGE * 2 / (kThreads * 16);   // per thread per k-tile
+    static constexpr int B_DMA = B_STAGE * 2 / (kThreads * 16);
+    static_assert(!DIRECT || (A_STAGE * 2 % (kThreads * 16) == 0 && B_STAGE * 2 % (kThreads * 16) == 0),
+                  "direct tiles must be whole 4 KiB block-wide loads");
+    static_assert(!DIRECT || (VA == 8 && VB == 8), "direct loads move 16-byte chunks");
+    // staged loads: vectors of VA / VB halves
+    static constexpr int A_VECS = A_STAGE / VA / kThreads;
+    static constexpr int B_VECS = B_STAGE / VB / kThreads;
+    static_assert(DIRECT || (A_STAGE % (VA * kThreads) == 0 && B_STAGE % (VB * kThreads) == 0),
+                  "staged tiles must split evenly over 256 threads");
+    static constexpr int LOADS_PER_TILE = DIRECT ? (A_DMA + B_DMA) : (A_VECS + B_VECS);
+};
+
+template <int V>
+struct VecT;
+template <>
+struct VecT<8> {
+    typedef int4v type;
+};
+template <>
+struct VecT<4> {
+    typedef int2v type;
+};
+template <>
+struct VecT<2> {
+    typedef int type;
+};
+template <>
+struct VecT<1> {
+    typedef short type;
+};
+
+template <int V>
+__device__ __forceinline__ typename VecT<V>::type buf_load(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    if constexpr (V == 8)
+        return __builtin_bit_cast(int4v, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    else if constexpr (V == 4)
+        return __builtin_bit_cast(int2v, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+    else if constexpr (V == 2)
+        return (int)__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+    else
+        return (short)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+
+template <int V>
+__device__ __forceinline__ void lds_store(half_t *p, typename VecT<V>::type v)
+{
+    *reinterpret_cast<typename VecT<V>::type *>(p) = v;
+}
+
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool DIRECT, int VA, int VB>
+__global__ void __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(1, 1)))
+gemm_f16_kernel(KernelArgs args)
+{
+    using T = Tile<BM, BN, BK, WM, WN, STAGES, DIRECT, VA, VB>;
+    __shared__ __attribute__((aligned(1024))) half_t lds[T::LDS_BYTES / 2];
+    half_t *const As = lds;                                  // STAGES x [BM][BK]
+    half_t *const Bs = lds + STAGES * T::A_STAGE;            // STAGES x [BK][BN]
+
+    const int M = args.M, N = args.N, K = args.K;
+    int tm, tn;
+    tile_coords(blockIdx.x, gridDim.x, args.tiles_m, args.tiles_n, args.group_m, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm0 = (wave / WN) * T::WTM;                   // wave sub-tile origin in the tile
+    const int wn0 = (wave % WN) * T::WTN;
+
+    // A panel: rows m0 .. m0+BM-1 (rows past M are outside the descriptor -> 0)
+    const int a_rows = min(BM, M - m0);
+    const half_t *a_base = args.A + (int64_t)m0 * K;
+    const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(a_base, (uint32_t)a_rows * (uint32_t)K * 2u);
+
+    const int nk = (K + BK - 1) / BK;
+
+    // ---- per-thread load assignments (fixed over the K loop) ----
+    // A: element (r, c) of the tile is A[m0 + r][k0 + c]
+    // B: element (r, c) of the tile is B[k0 + r][n0 + c]
+    // Masking: A rows past M and B rows past K lie outside their descriptors
+    // and read as 0.  A columns past K would read the next row and are masked:
+    // they meet B rows past K, which are 0, but a non-finite value there would
+    // turn 0 into NaN.  B columns past N are not masked: they only feed
+    // output columns past N, which are never stored.
+    // Direct: instruction i of this wave fills LDS bytes [(wave + 4 i) KiB, +1 KiB)
+    // of the stage and lane l lands at byte 16 l of that KiB.  Consecutive
+    // instructions of a thread are a fixed number of rows apart (a multiple
+    // of the swizzle period), so one base offset plus a row stride covers all.
+    constexpr int A_ROWS_PER_KB = 512 / BK;
+    constexpr int B_ROWS_PER_KB = 512 / BN > 0 ? 512 / BN : 1;
+    static_assert(!DIRECT || (4 * A_ROWS_PER_KB) % 8 == 0, "A row step keeps the swizzle phase");
+    static_assert(!DIRECT || BN <= 512, "direct B rows fit in 1 KiB");
+    static_assert(!DIRECT || (4 * 1024 / (BN * 2)) % 4 == 0, "B row step keeps the swizzle phase");
+    uint32_t a_off0, b_off0;          // byte offset of this thread's first vector
+    int a_col0;                       // tile column (halves) of A vectors (direct: same for all)
+    int a_lds[DIRECT ? 1 : T::A_VECS];
+    int a_colv[DIRECT ? 1 : T::A_VECS];
+    int b_lds[DIRECT ? 1 : T::B_VECS];
+    uint32_t a_offv[DIRECT ? 1 : T::A_VECS];
+    uint32_t b_offv[DIRECT ? 1 : T::B_VECS];
+
+    if constexpr (DIRECT) {
+        {
+            int byte = wave * 1024 + lane * 16;
+            int r = byte / (BK * 2);
+            int pc = (byte % (BK * 2)) / 16;
+            int c = pc ^ swz_a<T::CA>(r);
+            a_col0 = c * 8;
+            a_off0 = ((uint32_t)r * (uint32_t)K + (uint32_t)(c * 8)) * 2u;
+        }
+        {
+            int byte = wave * 1024 + lane * 16;
+            int r = byte / (BN * 2);
+            int pc = (byte % (BN * 2)) / 16;
+            int c = pc ^ swz_b<T::CB>(r);
+            b_off0 = ((uint32_t)r * (uint32_t)N + (uint32_t)(n0 + c * 8)) * 2u;
+        }
+    } else {
+        a_col0 = 0;
+        a_off0 = b_off0 = 0;
+#pragma unroll
+        for (int i = 0; i < T::A_VECS; ++i) {
+            int v = tid + T::kThreads * i;
+            int r = v / (BK / VA);
+            int c = (v % (BK / VA)) * VA;                 // column in halves
+            a_colv[i] = c;
+            a_offv[i] = ((uint32_t)r * (uint32_t)K + (uint32_t)c) * 2u;
+            a_lds[i] = r * BK + (((c / 8) ^ swz_a<T::CA>(r)) * 8) + (c % 8);
+        }
+#pragma unroll
+        for (int i = 0; i < T::B_VECS; ++i) {
+            int v = tid + T::kThreads * i;
+            int r = v / (BN / VB);
+            int c = (v % (BN / VB)) * VB;
+            b_offv[i] = ((uint32_t)r * (uint32_t)N + (uint32_t)(n0 + c)) * 2u;
+            b_lds[i] = r * BN + (((c / 8) ^ swz_b<T::CB>(r)) * 8) + (c % 8);
+        }
+    }
+    // byte distance between consecutive direct loads of one thread
+    const uint32_t a_step = (uint32_t)(4 * A_ROWS_PER_KB) * (uint32_t)K * 2u;
+    const uint32_t b_step = (uint32_t)(4 * 1024 / (BN * 2)) * (uint32_t)N * 2u;
+    (void)B_ROWS_PER_KB;
+
+    // Issue the global loads of k-tile kt into LDS stage s (direct) or into registers (staged).
+    typename VecT<VA>::type a_reg[DIRECT ? 1 : T::A_VECS];
+    typename VecT<VB>::type b_reg[DIRECT ? 1 : T::B_VECS];
+
+    auto issue_loads = [&](int kt, half_t *dst_a, half_t *dst_b) {
+        const int k0 = kt * BK;
+        const uint32_t a_shift = (uint32_t)k0 * 2u;
+        const int b_rows = min(BK, K - k0);
+        const __amdgpu_buffer_rsrc_t b_rsrc =
+            make_rsrc(args.B + (int64_t)k0 * N, (uint32_t)b_rows * (uint32_t)N * 2u);
+        if constexpr (DIRECT) {
+            // K % 8 == 0: a chunk is wholly inside or wholly past the row end
+            const uint32_t a_mask = oob_unless(k0 + a_col0 < K);
+#pragma unroll
+            for (int i = 0; i < T::A_DMA; ++i) {
+                uint32_t off = (a_off0 + a_shift + (uint32_t)i * a_step) | a_mask;
+                LDS_AS void *dst = (LDS_AS void *)(dst_a + (wave + T::kWaves * i) * 512);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, dst, 16, off, 0, 0, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < T::B_DMA; ++i) {
+                uint32_t off = b_off0 + (uint32_t)i * b_step;
+                LDS_AS void *dst = (LDS_AS void *)(dst_b + (wave + T::kWaves * i) * 512);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, dst, 16, off, 0, 0, 0);
+            }
+        } else {
+            (void)dst_a;
+            (void)dst_b;
+#pragma unroll
+            for (int i = 0; i < T::A_VECS; ++i) {
+                uint32_t off = (a_offv[i] + a_shift) | oob_unless(k0 + a_colv[i] < K);
+                a_reg[i] = buf_load<VA>(a_rsrc, off);
+            }
+#pragma unroll
+            for (int i = 0; i < T::B_VECS; ++i) {
+                b_reg[i] = buf_load<VB>(b_rsrc, b_offv[i]);
+            }
+        }
+    };
+    auto store_staged = [&](int s) {
+        if constexpr (!DIRECT) {
+#pragma unroll
+            for (int i = 0; i < T::A_VECS; ++i)
+                lds_store<VA>(As + s * T::A_STAGE + a_lds[i], a_reg[i]);
+#pragma unroll
+            for (int i = 0; i < T::B_VECS; ++i)
+                lds_store<VB>(Bs + s * T::B_STAGE + b_lds[i], b_reg[i]);
+        } else {
+            (void)s;
+        }
+    };
+
+    float16v acc[T::TM][T::TN];
+#pragma unroll
+    for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < T::TN; ++j)
+            acc[i][j] = float16v{};
+
+    // Fragment addressing inside one stage (in halves).
+    // Second MFMA operand (A^T, 16 k x 32 m): lane l reads row m = l % 32 of
+    // the block, logical chunk 2 ks + l / 32 (8 consecutive k).
+    const int ya_row = lane & 31;
+    const int ya_chunk = lane >> 5;
+    // First MFMA operand (B^T, 32 n x 16 k) via two transposing reads: in its
+    // 16-lane group g (n half g % 2, k half g / 2) lane j supplies the address
+    // of row k = 8 (g / 2) + j / 4 (+4 for the second read), columns
+    // 16 (g % 2) + 4 (j % 4) .. +3; lane j then receives column 16 (g % 2) + j.
+    const int xg = lane >> 4, xj = lane & 15;
+    const int xb_row = 8 * (xg >> 1) + (xj >> 2);
+    const int xb_col = 16 * (xg & 1) + 4 * (xj & 3);
+
+    auto compute = [&](const half_t *as, const half_t *bs) {
+#pragma unroll
+        for (int ks = 0; ks < BK / 16; ++ks) {
+            half8 y[T::TM];
+            half8 x[T::TN];
+#pragma unroll
+            for (int i = 0; i < T::TM; ++i) {
+                int r = wm0 + 32 * i + ya_row;
+                int c = 2 * ks + ya_chunk;
+                y[i] = *reinterpret_cast<const half8 *>(as + r * BK + ((c ^ swz_a<T::CA>(r)) * 8));
+            }
+#pragma unroll
+            for (int j = 0; j < T::TN; ++j) {
+                int n = wn0 + 32 * j + xb_col;
+                int r0 = 16 * ks + xb_row;
+                int r1 = r0 + 4;
+                const half_t *p0 = bs + r0 * BN + (((n >> 3) ^ swz_b<T::CB>(r0)) * 8) + (n & 7);
+                const half_t *p1 = bs + r1 * BN + (((n >> 3) ^ swz_b<T::CB>(r1)) * 8) + (n & 7);
+                short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS short4v *)p0);
+                short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS short4v *)p1);
+                half4 lo_h = __builtin_bit_cast(half4, lo);
+                half4 hi_h = __builtin_bit_cast(half4, hi);
+                x[j] = half8{lo_h[0], lo_h[1], lo_h[2], lo_h[3], hi_h[0], hi_h[1], hi_h[2], hi_h[3]};
+            }
+#pragma unroll
+            for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+                for (int j = 0; j < T::TN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(x[j], y[i], acc[i][j], 0, 0, 0);
+        }
+    };
+
+    // One K step: start the loads of tile kt_next into (wr_a, wr_b) and do the
+    // math on the stage (rd_a, rd_b).  The restrict qualifiers tell the
+    // compiler that the stage being filled is not the stage being read, so it
+    // does not make the LDS reads wait for the loads just issued.
+    auto step = [&](const half_t *__restrict__ rd_a, const half_t *__restrict__ rd_b,
+                    half_t *__restrict__ wr_a, half_t *__restrict__ wr_b, int kt_next) {
+        if (kt_next < nk)
+            issue_loads(kt_next, wr_a, wr_b);
+        compute(rd_a, rd_b);
+    };
+
+    // ---- pipelined K loop ----
+    if constexpr (DIRECT) {
+#pragma unroll
+        for (int s = 0; s < STAGES - 1; ++s)
+            if (s < nk)
+                issue_loads(s, As + s * T::A_STAGE, Bs + s * T::B_STAGE);
+        for (int kt0 = 0; kt0 < nk; kt0 += STAGES) {
+#pragma unroll
+            for (int s = 0; s < STAGES; ++s) {
+                const int kt = kt0 + s;
+                if (kt < nk) {
+                    // tile kt is the oldest of (at most) STAGES-1 tiles in flight
+                    if (kt + STAGES - 2 < nk)
+                        wait_vmcnt<(STAGES - 2) * T::LOADS_PER_TILE>();
+                    else
+                        wait_vmcnt<0>();
+                    __syncthreads();
+                    const int w = (s + STAGES - 1) % STAGES;
+                    step(As + s * T::A_STAGE, Bs + s * T::B_STAGE, As + w * T::A_STAGE, Bs + w * T::B_STAGE,
+                         kt + STAGES - 1);
+                }
+            }
+        }
+    } else {
+        // registers hold one tile in flight; LDS has STAGES stages (>= 2)
+        if (nk > 0) {
+            issue_loads(0, nullptr, nullptr);
+            store_staged(0);
+        }
+        if (nk > 1)
+            issue_loads(1, nullptr, nullptr);
+        __syncthreads();
+        for (int kt0 = 0; kt0 < nk; kt0 += STAGES) {
+#pragma unroll
+            for (int s = 0; s < STAGES; ++s) {
+                const int kt = kt0 + s;
+                if (kt < nk) {
+                    if (kt + 1 < nk)
+                        store_staged((s + 1) % STAGES);     // tile kt+1 -> the stage freed at kt-1
+                    if (kt + 2 < nk)
+                        issue_loads(kt + 2, nullptr, nullptr);
+                    compute(As + s * T::A_STAGE, Bs + s * T::B_STAGE);
+                    __syncthreads();
+                }
+            }
+        }
+    }
+
+    // ---- epilogue: optional ReLU, RNE to fp16, masked stores ----
+    const int c_rows = min(BM, M - m0);
+    half_t *c_base = args.C + (int64_t)m0 * N;
+    const __amdgpu_buffer_rsrc_t c_rsrc = make_rsrc(c_base, (uint32_t)c_rows * (uint32_t)N * 2u);
+    const bool relu = args.relu != 0;
+    const int vec_c = args.vec_c;
+#pragma unroll
+    for (int i = 0; i < T::TM; ++i) {
+        const int r = wm0 + 32 * i + (lane & 31);            // row inside the panel
+#pragma unroll
+        for (int j = 0; j < T::TN; ++j) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int n = n0 + wn0 + 32 * j + 8 * g + 4 * (lane >> 5);
+                float v0 = acc[i][j][4 * g + 0], v1 = acc[i][j][4 * g + 1];
+                float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
+                if (relu) {
+                    v0 = __builtin_fmaxf(v0, 0.0f);
+                    v1 = __builtin_fmaxf(v1, 0.0f);
+                    v2 = __builtin_fmaxf(v2, 0.0f);
+                    v3 = __builtin_fmaxf(v3, 0.0f);
+                }
+                // RNE conversions kept as scalars: hipcc mis-lowers a bit_cast of a
+                // single element of an fp16 ext_vector (it re-reads element 0)
+                const half_t h0 = (half_t)v0, h1 = (half_t)v1, h2 = (half_t)v2, h3 = (half_t)v3;
+                const uint32_t off = ((uint32_t)r * (uint32_t)N + (uint32_t)n) * 2u;
+                if (vec_c == 4) {
+                    // N % 4 == 0: the four columns are all inside or all outside
+                    half4 h = {h0, h1, h2, h3};
+                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(int2v, h), c_rsrc,
+                                                          off | oob_unless(n < N), 0, 0);
+                } else {
+                    const short hs[4] = {__builtin_bit_cast(short, h0), __builtin_bit_cast(short, h1),
+                                         __builtin_bit_cast(short, h2), __builtin_bit_cast(short, h3)};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        __builtin_amdgcn_raw_buffer_store_b16(hs[e], c_rsrc,
+                                                              (off + 2u * e) | oob_unless(n + e < N), 0, 0);
+                }
+            }
+        }
+    }
+}
+
+// ---- launchers ----------------------------------------------------------------
+
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool DIRECT, int VA, int VB>
+static hipError_t launch_one(const KernelArgs &a, int64_t grid, hipStream_t stream)
+{
+    hipLaunchKernelGGL((gemm_f16_kernel<BM, BN, BK, WM, WN, STAGES, DIRECT, VA, VB>), dim3((unsigned)grid),
+                       dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <int BM, int BN, int BK, int WM, int WN, int STAGES>
+static hipError_t launch_staged(const KernelArgs &a, int va, int vb, int64_t grid, hipStream_t s)
+{
+#define GEMM_F16_VB(VA_)                                                                   \
+    switch (vb) {                                                                          \
+    case 8: return launch_one<BM, BN, BK, WM, WN, STAGES, false, VA_, 8>(a, grid, s);      \
+    case 4: return launch_one<BM, BN, BK, WM, WN, STAGES, false, VA_, 4>(a, grid, s);      \
+    case 2: return launch_one<BM, BN, BK, WM, WN, STAGES, false, VA_, 2>(a, grid, s);      \
+    default: return launch_one<BM, BN, BK, WM, WN, STAGES, false, VA_, 1>(a, grid, s);     \
+    }
+    switch (va) {
+    case 8: GEMM_F16_VB(8)
+    case 4: GEMM_F16_VB(4)
+    case 2: GEMM_F16_VB(2)
+    default: GEMM_F16_VB(1)
+    }
+#undef GEMM_F16_VB
+}
+
+hipError_t launch(int config, const KernelArgs &a, int va, int vb, int64_t grid, hipStream_t s)
+{
+    switch (config) {
+    case 0: return launch_one<256, 256, 64, 2, 2, 2, true, 8, 8>(a, grid, s);
+    case 1: return launch_one<256, 128, 64, 2, 2, 3, true, 8, 8>(a, grid, s);
+    case 2: return launch_one<128, 128, 64, 2, 2, 3, true, 8, 8>(a, grid, s);
+    case 3: return launch_staged<128, 128, 32, 2, 2, 2>(a, va, vb, grid, s);
+    case 4: return launch_staged<64, 64, 64, 2, 2, 2>(a, va, vb, grid, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+} // namespace gemm_f16_impl
