@@ -18,6 +18,8 @@ const ConfigDesc kConfigs[kNumConfigs] = {
     {"128x128x64_s3_direct", 128, 128, 64, 3, true},
     {"128x128x32_s2_staged", 128, 128, 32, 2, false},
     {"64x64x64_s2_staged", 64, 64, 64, 2, false},
+    {"256x256x32_s4_direct", 256, 256, 32, 4, true},
+    {"256x256x32_s5_direct", 256, 256, 32, 5, true},
 };
 
 namespace {
@@ -73,7 +75,8 @@ double config_efficiency(int c)
     case 1: return 0.92;
     case 2: return 0.80;
     case 3: return 0.55;
-    default: return 0.35;
+    case 4: return 0.35;
+    default: return 0.0;   // not chosen automatically yet
     }
 }
 
@@ -112,7 +115,7 @@ int choose_config(int64_t M, int64_t N, int va, int vb)
     int best = -1;
     double best_t = 0.0;
     for (int c = 0; c < kNumConfigs; ++c) {
-        if (!config_fits(c, va, vb))
+        if (!config_fits(c, va, vb) || config_efficiency(c) <= 0.0)
             continue;
         const ConfigDesc &d = kConfigs[c];
         int64_t grid = ceil_div(M, d.block_m) * ceil_div(N, d.block_n);

@@ -29,7 +29,7 @@ struct ConfigDesc {
     bool direct;          // operands move global -> LDS with buffer_load ... lds
 };
 
-constexpr int kNumConfigs = 5;
+constexpr int kNumConfigs = 7;
 extern const ConfigDesc kConfigs[kNumConfigs];
 
 // Launch configuration `config` with `grid` workgroups of 256 threads on `s`.

@@ -74,30 +74,54 @@ __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// s_waitcnt vmcnt(n) lgkmcnt(0): global loads down to n outstanding and every
+// LDS access of this wave complete.
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));
+}
+
 // ---- LDS swizzles ---------------------------------------------------------
-// A tile: rows of BK halves = BK/8 chunks of 16 bytes.  ds_read_b128 of a
-// fragment touches 32 consecutive rows at one logical chunk; the XOR makes
-// any 8 consecutive rows land in 8 different 16-byte bank groups.
+// gfx950 LDS as measured: 64 banks of 4 bytes (a 256-byte window).  A
+// ds_read_b128 is served 16 lanes per pass and is conflict-free when those 16
+// lanes hit 16 different 16-byte slots of the window; 8-byte reads (plain or
+// transposing) are served 32 lanes per pass and are conflict-free when the
+// 32 lanes cover the window exactly.  Tiles are stored unpadded and the
+// 16-byte chunk index of each row is XOR-ed with a row-dependent value.
+//
+// A tile: rows of CHUNKS 16-byte chunks.  A fragment read takes one chunk from
+// each of 16 consecutive rows per pass; with W = 16 / CHUNKS rows per window
+// (rows of 256 bytes or more: W = 1) rows r and r + W must differ in the XOR.
 template <int CHUNKS>
 __device__ __forceinline__ int swz_a(int row)
 {
-    if constexpr (CHUNKS >= 8)
-        return row & 7;
+    if constexpr (CHUNKS >= 16)
+        return row & 15;
+    else if constexpr (CHUNKS == 8)
+        return (row >> 1) & 7;
     else if constexpr (CHUNKS == 4)
-        return (row >> 1) & 3;
+        return (row >> 2) & 3;
     else if constexpr (CHUNKS == 2)
-        return (row >> 2) & 1;
+        return (row >> 3) & 1;
     else
         return 0;
 }
 
-// B tile: rows of BN halves.  A transposing read covers 4 consecutive rows x
-// 32 bytes per 16-lane group; XOR-ing chunk bits 1-2 with the row's low two
-// bits puts those 16 eight-byte pieces on 16 different bank pairs.
+// B tile: rows of CHUNKS 16-byte chunks.  Each 32-lane half of a transposing
+// fragment read takes four 64-byte pieces (chunks 4q .. 4q+3) from four
+// consecutive rows; XOR-ing the chunk index with a multiple of 4 moves the
+// rows' pieces to different quarters of the window.
 template <int CHUNKS>
 __device__ __forceinline__ int swz_b(int row)
 {
-    return (2 * (row & 3)) & (CHUNKS - 1);
+    if constexpr (CHUNKS >= 16)
+        return 4 * (row & 3);              // one row spans >= 1 window
+    else if constexpr (CHUNKS == 8)
+        return 4 * ((row >> 1) & 1);       // two rows per window
+    else
+        return 0;                          // four rows per window already disjoint
 }
 
 // ---- tile index remap -----------------------------------------------------
@@ -136,6 +160,7 @@ struct Tile {
     static constexpr int CA = BK / 8;                // 16-byte chunks per A row in LDS
     static constexpr int CB = BN / 8;                // 16-byte chunks per B row in LDS
     static_assert(CB >= 4 && (CB & (CB - 1)) == 0, "B row chunks: power of two >= 4");
+    static_assert(CA >= 2, "A rows of at least 32 bytes");
     static_assert((CA & (CA - 1)) == 0, "A row chunks: power of two");
     static constexpr int A_STAGE = BM * BK;          // halves
     static constexpr int B_STAGE = BK * BN;
@@ -235,7 +260,7 @@ gemm_f16_kernel(KernelArgs args)
     // of the swizzle period), so one base offset plus a row stride covers all.
     constexpr int A_ROWS_PER_KB = 512 / BK;
     constexpr int B_ROWS_PER_KB = 512 / BN > 0 ? 512 / BN : 1;
-    static_assert(!DIRECT || (4 * A_ROWS_PER_KB) % 8 == 0, "A row step keeps the swizzle phase");
+    static_assert(!DIRECT || (4 * A_ROWS_PER_KB) % 16 == 0, "A row step keeps the swizzle phase");
     static_assert(!DIRECT || BN <= 512, "direct B rows fit in 1 KiB");
     static_assert(!DIRECT || (4 * 1024 / (BN * 2)) % 4 == 0, "B row step keeps the swizzle phase");
     uint32_t a_off0, b_off0;          // byte offset of this thread's first vector
@@ -292,10 +317,14 @@ gemm_f16_kernel(KernelArgs args)
     typename VecT<VA>::type a_reg[DIRECT ? 1 : T::A_VECS];
     typename VecT<VB>::type b_reg[DIRECT ? 1 : T::B_VECS];
 
+    // A tile index kt >= nk is allowed: its rows are all past K, so every
+    // load reads zeros (the direct pipeline issues such loads unconditionally
+    // at its tail instead of branching around them).
     auto issue_loads = [&](int kt, half_t *dst_a, half_t *dst_b) {
         const int k0 = kt * BK;
         const uint32_t a_shift = (uint32_t)k0 * 2u;
-        const int b_rows = min(BK, K - k0);
+        // uniform by construction; readfirstlane keeps the descriptor in SGPRs
+        const int b_rows = __builtin_amdgcn_readfirstlane(max(0, min(BK, K - k0)));
         const __amdgpu_buffer_rsrc_t b_rsrc =
             make_rsrc(args.B + (int64_t)k0 * N, (uint32_t)b_rows * (uint32_t)N * 2u);
         if constexpr (DIRECT) {
@@ -360,72 +389,137 @@ gemm_f16_kernel(KernelArgs args)
     const int xb_row = 8 * (xg >> 1) + (xj >> 2);
     const int xb_col = 16 * (xg & 1) + 4 * (xj & 3);
 
+    // Fragments of one 16-deep k step: x = B^T slices (one per 32-column
+    // block), y = A^T slices (one per 32-row block).
+    struct Frags {
+        half8 x[T::TN];
+        half8 y[T::TM];
+    };
+    auto load_frags = [&](Frags &f, const half_t *as, const half_t *bs, int ks) {
+#pragma unroll
+        for (int i = 0; i < T::TM; ++i) {
+            int r = wm0 + 32 * i + ya_row;
+            int c = 2 * ks + ya_chunk;
+            f.y[i] = *reinterpret_cast<const half8 *>(as + r * BK + ((c ^ swz_a<T::CA>(r)) * 8));
+        }
+#pragma unroll
+        for (int j = 0; j < T::TN; ++j) {
+            int n = wn0 + 32 * j + xb_col;
+            int r0 = 16 * ks + xb_row;
+            int r1 = r0 + 4;
+            const half_t *p0 = bs + r0 * BN + (((n >> 3) ^ swz_b<T::CB>(r0)) * 8) + (n & 7);
+            const half_t *p1 = bs + r1 * BN + (((n >> 3) ^ swz_b<T::CB>(r1)) * 8) + (n & 7);
+            short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS short4v *)p0);
+            short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS short4v *)p1);
+            half4 lo_h = __builtin_bit_cast(half4, lo);
+            half4 hi_h = __builtin_bit_cast(half4, hi);
+            f.x[j] = half8{lo_h[0], lo_h[1], lo_h[2], lo_h[3], hi_h[0], hi_h[1], hi_h[2], hi_h[3]};
+        }
+    };
+    auto mma = [&](const Frags &f) {
+#pragma unroll
+        for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+            for (int j = 0; j < T::TN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.x[j], f.y[i], acc[i][j], 0, 0, 0);
+    };
+    // Ask the scheduler to alternate the MFMAs of one step with the LDS reads
+    // of the next step (and, after a barrier, with the next tile's loads), so
+    // the matrix core keeps busy while those are in flight.
+    constexpr int kMfmaPerStep = T::TM * T::TN;
+    constexpr int kReadsPerStep = T::TM + 2 * T::TN;
+    auto interleave = [&](int n_vmem) {
+#pragma unroll
+        for (int i = 0; i < kMfmaPerStep; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // one MFMA
+            if (i < kReadsPerStep)
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // one LDS read
+            if (i < n_vmem)
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);      // one global load
+        }
+    };
+    // plain (non-pipelined) math on one stage, for the register-staged kernels
     auto compute = [&](const half_t *as, const half_t *bs) {
 #pragma unroll
         for (int ks = 0; ks < BK / 16; ++ks) {
-            half8 y[T::TM];
-            half8 x[T::TN];
-#pragma unroll
-            for (int i = 0; i < T::TM; ++i) {
-                int r = wm0 + 32 * i + ya_row;
-                int c = 2 * ks + ya_chunk;
-                y[i] = *reinterpret_cast<const half8 *>(as + r * BK + ((c ^ swz_a<T::CA>(r)) * 8));
-            }
-#pragma unroll
-            for (int j = 0; j < T::TN; ++j) {
-                int n = wn0 + 32 * j + xb_col;
-                int r0 = 16 * ks + xb_row;
-                int r1 = r0 + 4;
-                const half_t *p0 = bs + r0 * BN + (((n >> 3) ^ swz_b<T::CB>(r0)) * 8) + (n & 7);
-                const half_t *p1 = bs + r1 * BN + (((n >> 3) ^ swz_b<T::CB>(r1)) * 8) + (n & 7);
-                short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS short4v *)p0);
-                short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS short4v *)p1);
-                half4 lo_h = __builtin_bit_cast(half4, lo);
-                half4 hi_h = __builtin_bit_cast(half4, hi);
-                x[j] = half8{lo_h[0], lo_h[1], lo_h[2], lo_h[3], hi_h[0], hi_h[1], hi_h[2], hi_h[3]};
-            }
-#pragma unroll
-            for (int i = 0; i < T::TM; ++i)
-#pragma unroll
-                for (int j = 0; j < T::TN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(x[j], y[i], acc[i][j], 0, 0, 0);
+            Frags f;
+            load_frags(f, as, bs, ks);
+            mma(f);
         }
-    };
-
-    // One K step: start the loads of tile kt_next into (wr_a, wr_b) and do the
-    // math on the stage (rd_a, rd_b).  The restrict qualifiers tell the
-    // compiler that the stage being filled is not the stage being read, so it
-    // does not make the LDS reads wait for the loads just issued.
-    auto step = [&](const half_t *__restrict__ rd_a, const half_t *__restrict__ rd_b,
-                    half_t *__restrict__ wr_a, half_t *__restrict__ wr_b, int kt_next) {
-        if (kt_next < nk)
-            issue_loads(kt_next, wr_a, wr_b);
-        compute(rd_a, rd_b);
     };
 
     // ---- pipelined K loop ----
     if constexpr (DIRECT) {
+        // Software pipeline over the k steps of a tile with two fragment sets:
+        // the reads of step s+1 are in flight while step s multiplies.  The
+        // last step of a tile is multiplied after the next barrier, so that
+        // the first reads of the next tile overlap MFMA work too.
+        constexpr int NS = BK / 16;
+        static_assert(NS % 2 == 0, "an even number of k steps per tile");
+        Frags f0, f1;
+        // One tile: start the loads of tile kt_next into (wr_a, wr_b), then the
+        // math on stage (rd_a, rd_b); f1 holds the previous tile's last step
+        // when `pending`.  The restrict qualifiers tell the compiler that the
+        // stage being filled is not the stage being read, so it does not make
+        // the LDS reads wait for the loads just issued.
+        auto step = [&](const half_t *__restrict__ rd_a, const half_t *__restrict__ rd_b,
+                        half_t *__restrict__ wr_a, half_t *__restrict__ wr_b, int kt_next, bool pending) {
+            issue_loads(kt_next, wr_a, wr_b);   // past the last tile: zeros into a retired stage
+            load_frags(f0, rd_a, rd_b, 0);
+            if (pending)
+                mma(f1);
+            interleave(T::LOADS_PER_TILE);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int ks = 0; ks + 1 < NS; ks += 2) {
+                load_frags(f1, rd_a, rd_b, ks + 1);
+                mma(f0);
+                interleave(0);
+                __builtin_amdgcn_sched_barrier(0);
+                if (ks + 2 < NS) {
+                    load_frags(f0, rd_a, rd_b, ks + 2);
+                    mma(f1);
+                    interleave(0);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            // f1 now holds step NS-1 of this tile, multiplied by the next call
+        };
+        // wait until tile kt has landed in LDS for every wave, and this wave's
+        // reads of the stage about to be refilled have completed
+        auto tile_ready = [&](int kt) {
+            if (kt + STAGES - 2 < nk)
+                wait_vm_lgkm0<(STAGES - 2) * T::LOADS_PER_TILE>();
+            else
+                wait_vm_lgkm0<0>();
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+        };
 #pragma unroll
         for (int s = 0; s < STAGES - 1; ++s)
             if (s < nk)
                 issue_loads(s, As + s * T::A_STAGE, Bs + s * T::B_STAGE);
-        for (int kt0 = 0; kt0 < nk; kt0 += STAGES) {
+        if (nk > 0) {
+            tile_ready(0);
+            step(As, Bs, As + (STAGES - 1) * T::A_STAGE, Bs + (STAGES - 1) * T::B_STAGE, STAGES - 1, false);
+        }
+        // tiles 1 .. nk-1, unrolled so that every stage index is a constant
+        for (int kt0 = 1; kt0 < nk; kt0 += STAGES) {
 #pragma unroll
-            for (int s = 0; s < STAGES; ++s) {
-                const int kt = kt0 + s;
+            for (int u = 0; u < STAGES; ++u) {
+                const int kt = kt0 + u;
+                const int s = (1 + u) % STAGES;
+                const int w = (s + STAGES - 1) % STAGES;
                 if (kt < nk) {
-                    // tile kt is the oldest of (at most) STAGES-1 tiles in flight
-                    if (kt + STAGES - 2 < nk)
-                        wait_vmcnt<(STAGES - 2) * T::LOADS_PER_TILE>();
-                    else
-                        wait_vmcnt<0>();
-                    __syncthreads();
-                    const int w = (s + STAGES - 1) % STAGES;
+                    tile_ready(kt);
                     step(As + s * T::A_STAGE, Bs + s * T::B_STAGE, As + w * T::A_STAGE, Bs + w * T::B_STAGE,
-                         kt + STAGES - 1);
+                         kt + STAGES - 1, true);
                 }
             }
         }
+        if (nk > 0)
+            mma(f1);
+        wait_vmcnt<0>();   // the tail's zero-filling loads must land before the workgroup retires
     } else {
         // registers hold one tile in flight; LDS has STAGES stages (>= 2)
         if (nk > 0) {
@@ -532,6 +626,8 @@ hipError_t launch(int config, const KernelArgs &a, int va, int vb, int64_t grid,
     case 2: return launch_one<128, 128, 64, 2, 2, 3, true, 8, 8>(a, grid, s);
     case 3: return launch_staged<128, 128, 32, 2, 2, 2>(a, va, vb, grid, s);
     case 4: return launch_staged<64, 64, 64, 2, 2, 2>(a, va, vb, grid, s);
+    case 5: return launch_one<256, 256, 32, 2, 2, 4, true, 8, 8>(a, grid, s);
+    case 6: return launch_one<256, 256, 32, 2, 2, 5, true, 8, 8>(a, grid, s);
     default: return hipErrorInvalidValue;
     }
 }
