@@ -67,7 +67,8 @@ def cpu_baseline(a, b, w, budget_s: float):
     rows_all, cols_all = workloads.sample_indices(w)
     cols = cols_all.numpy()
     # calibrate on a small block, then size the timed block
-    n_cal = 64
+    n_cal = 128
+    oracle.gemm_sampled(A, B, rows_all[:16].numpy(), cols)            # warm the pages
     t0 = time.perf_counter()
     oracle.gemm_sampled(A, B, rows_all[:n_cal].numpy(), cols)
     t_cal = max(time.perf_counter() - t0, 1e-3)
@@ -87,6 +88,67 @@ def cpu_baseline(a, b, w, budget_s: float):
     }
 
 
+COPY_BYTES = 256 * 1024 * 1024
+
+
+def copy_calibration() -> int:
+    """A plain device-to-device copy of COPY_BYTES, three times: the reference
+    kernel whose FETCH_SIZE / WRITE_SIZE readings calibrate the counters."""
+    import torch
+
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES}), flush=True)
+    return 0
+
+
+def _counter_per_dispatch(csv_path: str, counter: str, kernel_substr: str):
+    import csv
+    import collections
+
+    per = collections.defaultdict(float)
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == counter and kernel_substr in r["Kernel_Name"]:
+                per[int(r["Dispatch_Id"])] += float(r["Counter_Value"])
+    return sorted(per.values())
+
+
+def traffic_from(directory: str, workload: str, config_name: str) -> int:
+    """Turn rocprofv3 --pmc CSVs into HBM bytes per GEMM launch, calibrated by
+    the copy kernel, and record them with the kernel source hash."""
+    import glob
+    import statistics
+
+    def one(sub, counter, kernel):
+        paths = glob.glob(os.path.join(directory, sub, "**", "*counter_collection.csv"), recursive=True)
+        if not paths:
+            raise SystemExit(f"no counter CSV under {directory}/{sub}")
+        vals = _counter_per_dispatch(paths[0], counter, kernel)
+        if not vals:
+            raise SystemExit(f"no {counter} rows for {kernel!r} in {paths[0]}")
+        return statistics.median(vals)
+
+    copy_fetch = one("copy_fetch", "FETCH_SIZE", "copyBuffer")
+    copy_write = one("copy_write", "WRITE_SIZE", "copyBuffer")
+    f_fetch = COPY_BYTES / (copy_fetch * 1024.0)
+    f_write = COPY_BYTES / (copy_write * 1024.0)
+    fetch = one("fetch", "FETCH_SIZE", "gemm_f16_kernel") * 1024.0 * f_fetch
+    write = one("write", "WRITE_SIZE", "gemm_f16_kernel") * 1024.0 * f_write
+    rec = {"workload": workload, "kernel_config": config_name, "kernel_sha256": kernel_source_hash(),
+           "fetch_bytes_per_launch": fetch, "write_bytes_per_launch": write,
+           "fetch_calibration": f_fetch, "write_calibration": f_write,
+           "copy_fetch_kib": copy_fetch, "copy_write_kib": copy_write}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -96,7 +158,15 @@ def main() -> int:
     ap.add_argument("--config", type=int, default=-1, help="kernel configuration (-1: automatic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the MFMA-only ceiling probe")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run the copy kernel used to calibrate FETCH_SIZE / WRITE_SIZE")
+    ap.add_argument("--traffic-from", metavar="DIR",
+                    help="only convert rocprofv3 counter CSVs under DIR/{fetch,write,copy_fetch,copy_write}")
     args = ap.parse_args()
+
+    if args.copy_calibration:
+        return copy_calibration()
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -115,6 +185,9 @@ def main() -> int:
         __graft_entry__.build()
 
     w = workloads.WORKLOADS[args.workload]
+    if args.traffic_from:
+        p = g.plan(w.M, w.N, w.K, 1 << 20, 1 << 20, 1 << 20, config=args.config)
+        return traffic_from(args.traffic_from, w.name, g.config_name(p["config"]))
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     a, b = workloads.make_inputs(w)
@@ -186,6 +259,14 @@ def main() -> int:
         },
         "spot_check": {"n": spot["n"], "pass": spot["pass"], "max_ulp_err": spot["max_ulp_err"]},
     }
+    if not args.no_ceiling:
+        # the matrix cores' sustained rate on register operands alone, for the
+        # same instruction mix, with constant and with changing random bits
+        rnd = g.probe_mfma_tflops(g.PROBE_RANDOM_CHANGING)
+        const = g.probe_mfma_tflops(g.PROBE_CONSTANT)
+        out["roofline"]["mfma_only_ceiling"] = {
+            "random_operands": round(rnd, 1), "constant_operands": round(const, 1), "unit": "TFLOP/s",
+            "achieved_over_random_ceiling": round(achieved / rnd, 3)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(a, b, w, args.cpu_budget)
     print(json.dumps(out), flush=True)

@@ -1,0 +1,52 @@
+/*
+ * gemm_f16_probe.h -- measurement probe shipped with the FP16 GEMM library
+ * (libgemm_f16_probe.so).  Not part of the GEMM itself.
+ *
+ * It runs the GEMM kernels' inner-loop instruction mix -- per wave a 4 x 4
+ * block of v_mfma_f32_32x32x16_f16 on 16 fp32 accumulator tiles, one wave
+ * per SIMD -- with register operands only and no memory traffic, to measure
+ * the matrix-core throughput the GPU sustains for a kind of operand data.
+ * The pages ask for the roofline to be worked out before tuning and compared
+ * with measurement ("TileLang：比 Triton 低一层的 tile 语言", section
+ * "工程上的几个注意点"); on MI355X the sustained MFMA clock depends on the
+ * data, so this gives the measured ceiling next to the nominal one.
+ */
+#ifndef GEMM_F16_PROBE_H
+#define GEMM_F16_PROBE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Operand kinds. */
+#define GEMM_F16_PROBE_CONSTANT 0          /* the same constant bits in every fragment */
+#define GEMM_F16_PROBE_RANDOM_FIXED 1      /* random halves, one fragment set reused */
+#define GEMM_F16_PROBE_RANDOM_CHANGING 2   /* random halves, two fragment sets alternating,
+                                              as the GEMM's k steps do */
+
+/* Number of 8-half (16-byte) vectors the `operands` buffer must hold. */
+#define GEMM_F16_PROBE_OPERAND_VECTORS 1024
+
+/*
+ * Enqueue the probe on `stream` (a hipStream_t, NULL = default stream).
+ *   mode     : one of the GEMM_F16_PROBE_* kinds.
+ *   iters    : loop trips; each trip issues 32 MFMAs per wave.
+ *   blocks   : workgroups of 256 threads (use a multiple of the CU count).
+ *   operands : device buffer of GEMM_F16_PROBE_OPERAND_VECTORS x 8 binary16
+ *              values (ignored for GEMM_F16_PROBE_CONSTANT).
+ *   out      : device buffer of blocks x 256 floats (written, to keep the
+ *              work observable).
+ *   flops    : if not NULL, receives the flops the launch performs.
+ * Returns 0 on success, 1 for bad arguments, 2 if the launch failed.
+ * Buffers belong to the caller; the call is asynchronous.
+ */
+int gemm_f16_probe_mfma(int mode, int iters, int64_t blocks, const void *operands, void *out,
+                        void *stream, double *flops);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GEMM_F16_PROBE_H */

@@ -21,7 +21,7 @@ FAKE = 1 << 20
 
 @pytest.fixture(scope="module", autouse=True)
 def built():
-    if not os.path.exists(g.LIB_PATH):
+    if not os.path.exists(g.LIB_PATH) or not os.path.exists(g.PROBE_LIB_PATH):
         import __graft_entry__
         __graft_entry__.build()
 
@@ -42,6 +42,20 @@ def test_every_declared_symbol_is_exported():
     assert set(g.SIGNATURES) == set(names)
 
 
+def test_probe_library_exports_its_header():
+    text = open(os.path.join(ROOT, "include", "gemm_f16_probe.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = sorted(set(re.findall(r"\b(gemm_f16_probe\w*)\s*\(", text)))
+    assert names == ["gemm_f16_probe_mfma"]
+    lib = ctypes.CDLL(g.PROBE_LIB_PATH)
+    for name in names:
+        assert hasattr(lib, name)
+    assert set(g.PROBE_SIGNATURES) == set(names)
+    # argument checks happen before any launch
+    assert g.probe_lib().gemm_f16_probe_mfma(7, 1, 1, None, FAKE, None, None) == 1
+    assert g.probe_lib().gemm_f16_probe_mfma(0, 1, 0, None, FAKE, None, None) == 1
+
+
 def test_status_strings():
     for st in range(0, 7):
         assert g.status_string(st) != "unknown status"
@@ -59,7 +73,7 @@ def test_config_table():
         assert p["config"] == c
         assert p["lds_bytes"] <= 163840                     # MI355X LDS per workgroup
         assert p["lds_bytes"] == g.stage_bytes(p["block_m"], p["block_n"], p["block_k"], p["stages"])
-        assert p["threads"] == 256
+        assert p["threads"] in (256, 512)
 
 
 def _golden_rows():

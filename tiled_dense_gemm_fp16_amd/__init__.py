@@ -16,6 +16,7 @@ import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgemm_f16.so")
+PROBE_LIB_PATH = os.path.join(_HERE, "libgemm_f16_probe.so")
 
 SUCCESS = 0
 EPILOGUE_NONE = 0
@@ -153,3 +154,63 @@ def gemm(a, b, epilogue: str = "none", out=None, config: int = CONFIG_AUTO, stre
     if st != SUCCESS:
         raise GemmError(st, "gemm_f16")
     return out
+
+
+# ---- measurement probe (libgemm_f16_probe.so, include/gemm_f16_probe.h) ----
+
+PROBE_CONSTANT, PROBE_RANDOM_FIXED, PROBE_RANDOM_CHANGING = 0, 1, 2
+PROBE_OPERAND_VECTORS = 1024
+PROBE_SIGNATURES = {
+    "gemm_f16_probe_mfma": ([_int, _int, _i64, _vp, _vp, _vp, ctypes.POINTER(ctypes.c_double)], _int),
+}
+_probe = None
+
+
+def probe_lib() -> ctypes.CDLL:
+    global _probe
+    if _probe is None:
+        if not os.path.exists(PROBE_LIB_PATH):
+            raise RuntimeError(f"{PROBE_LIB_PATH} is missing: build the HIP library first")
+        h = ctypes.CDLL(PROBE_LIB_PATH)
+        for name, (args, res) in PROBE_SIGNATURES.items():
+            fn = getattr(h, name)
+            fn.argtypes = args
+            fn.restype = res
+        _probe = h
+    return _probe
+
+
+def probe_mfma_tflops(mode: int, seconds: float = 0.3, seed: int = 0) -> float:
+    """Sustained MFMA TFLOP/s of the GEMM's inner-loop instruction mix on
+    register operands of the given kind (see include/gemm_f16_probe.h)."""
+    import torch
+
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    ops = (torch.randn(PROBE_OPERAND_VECTORS * 8, generator=g) * 0.5).to(torch.float16).cuda()
+    blocks = 256 * 4
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    flops = ctypes.c_double()
+
+    def launch(iters):
+        st = probe_lib().gemm_f16_probe_mfma(mode, iters, blocks, ops.data_ptr(), out.data_ptr(),
+                                             stream.cuda_stream, ctypes.byref(flops))
+        if st != 0:
+            raise RuntimeError(f"gemm_f16_probe_mfma failed ({st})")
+
+    launch(200)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    iters = 2000
+    s.record(stream)
+    launch(iters)
+    e.record(stream)
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e)
+    iters = max(200, int(iters * seconds * 1e3 / max(ms, 1e-3)))   # resize to ~`seconds`
+    s.record(stream)
+    launch(iters)
+    e.record(stream)
+    torch.cuda.synchronize()
+    return flops.value / (s.elapsed_time(e) * 1e-3) / 1e12

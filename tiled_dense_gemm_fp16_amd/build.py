@@ -8,6 +8,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libgemm_f16.so")
 SOURCES = [os.path.join(CSRC, "gemm_f16_api.cpp"), os.path.join(CSRC, "gemm_f16_kernels.hip")]
+PROBE_LIB = os.path.join(PKG, "libgemm_f16_probe.so")
+PROBE_SOURCES = [os.path.join(CSRC, "mfma_probe.hip")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -21,9 +23,16 @@ FLAGS = [
 
 
 def build(verbose: bool = False, extra_flags=None) -> str:
-    """Compile every source into libgemm_f16.so next to this file; return its path."""
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, *(extra_flags or []), "-I", INCLUDE, "-I", CSRC, "-x", "hip", *SOURCES,
+    """Compile libgemm_f16.so and the measurement probe libgemm_f16_probe.so next
+    to this file; return the GEMM library's path."""
+    _compile(SOURCES, LIB, verbose, extra_flags)
+    _compile(PROBE_SOURCES, PROBE_LIB, verbose, extra_flags)
+    return LIB
+
+
+def _compile(sources, lib, verbose, extra_flags):
+    tmp = lib + ".tmp"
+    cmd = [HIPCC, *FLAGS, *(extra_flags or []), "-I", INCLUDE, "-I", CSRC, "-x", "hip", *sources,
            "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -35,8 +44,7 @@ def build(verbose: bool = False, extra_flags=None) -> str:
         lines = [ln for ln in res.stderr.splitlines() if "packed-fp32-ops" not in ln]
         if lines:
             print("\n".join(lines), flush=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
 
 
 if __name__ == "__main__":

@@ -26,13 +26,14 @@ struct ConfigDesc {
     const char *name;
     int block_m, block_n, block_k;
     int stages;
+    int waves;            // wave64s per workgroup (4: one per SIMD, 8: two)
     bool direct;          // operands move global -> LDS with buffer_load ... lds
 };
 
-constexpr int kNumConfigs = 7;
+constexpr int kNumConfigs = 10;
 extern const ConfigDesc kConfigs[kNumConfigs];
 
-// Launch configuration `config` with `grid` workgroups of 256 threads on `s`.
+// Launch configuration `config` with `grid` workgroups on `s`.
 // va / vb: elements per global load of A / B (8, 4, 2 or 1; direct configs
 // require 8).  Returns the launch status.
 hipError_t launch(int config, const KernelArgs &a, int va, int vb, int64_t grid, hipStream_t s);

@@ -148,9 +148,9 @@ __device__ __forceinline__ void tile_coords(int wg, int grid, int tiles_m, int t
 // ---- the kernel -------------------------------------------------------------
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool DIRECT, int VA, int VB>
 struct Tile {
-    static constexpr int kThreads = 256;
-    static constexpr int kWaves = 4;
-    static_assert(WM * WN == kWaves, "4 waves");
+    static constexpr int kWaves = WM * WN;           // 4 (one per SIMD) or 8 (two per SIMD)
+    static constexpr int kThreads = 64 * kWaves;
+    static_assert(kWaves == 4 || kWaves == 8, "4 or 8 waves");
     static constexpr int WTM = BM / WM;              // wave sub-tile rows (m)
     static constexpr int WTN = BN / WN;              // wave sub-tile cols (n)
     static constexpr int TM = WTM / 32;              // 32x32 MFMA blocks per wave along m
@@ -219,8 +219,8 @@ __device__ __forceinline__ void lds_store(half_t *p, typename VecT<V>::type v)
 }
 
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool DIRECT, int VA, int VB>
-__global__ void __launch_bounds__(256)
-__attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(64 * WM * WN)
+__attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4)))
 gemm_f16_kernel(KernelArgs args)
 {
     using T = Tile<BM, BN, BK, WM, WN, STAGES, DIRECT, VA, VB>;
@@ -260,9 +260,9 @@ gemm_f16_kernel(KernelArgs args)
     // of the swizzle period), so one base offset plus a row stride covers all.
     constexpr int A_ROWS_PER_KB = 512 / BK;
     constexpr int B_ROWS_PER_KB = 512 / BN > 0 ? 512 / BN : 1;
-    static_assert(!DIRECT || (4 * A_ROWS_PER_KB) % 16 == 0, "A row step keeps the swizzle phase");
+    static_assert(!DIRECT || (T::kWaves * A_ROWS_PER_KB) % 16 == 0, "A row step keeps the swizzle phase");
     static_assert(!DIRECT || BN <= 512, "direct B rows fit in 1 KiB");
-    static_assert(!DIRECT || (4 * 1024 / (BN * 2)) % 4 == 0, "B row step keeps the swizzle phase");
+    static_assert(!DIRECT || (T::kWaves * 1024 / (BN * 2)) % 4 == 0, "B row step keeps the swizzle phase");
     uint32_t a_off0, b_off0;          // byte offset of this thread's first vector
     int a_col0;                       // tile column (halves) of A vectors (direct: same for all)
     int a_lds[DIRECT ? 1 : T::A_VECS];
@@ -309,8 +309,8 @@ gemm_f16_kernel(KernelArgs args)
         }
     }
     // byte distance between consecutive direct loads of one thread
-    const uint32_t a_step = (uint32_t)(4 * A_ROWS_PER_KB) * (uint32_t)K * 2u;
-    const uint32_t b_step = (uint32_t)(4 * 1024 / (BN * 2)) * (uint32_t)N * 2u;
+    const uint32_t a_step = (uint32_t)(T::kWaves * A_ROWS_PER_KB) * (uint32_t)K * 2u;
+    const uint32_t b_step = (uint32_t)(T::kWaves * 1024 / (BN * 2)) * (uint32_t)N * 2u;
     (void)B_ROWS_PER_KB;
 
     // Issue the global loads of k-tile kt into LDS stage s (direct) or into registers (staged).
@@ -595,7 +595,7 @@ template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool DIRECT, int V
 static hipError_t launch_one(const KernelArgs &a, int64_t grid, hipStream_t stream)
 {
     hipLaunchKernelGGL((gemm_f16_kernel<BM, BN, BK, WM, WN, STAGES, DIRECT, VA, VB>), dim3((unsigned)grid),
-                       dim3(256), 0, stream, a);
+                       dim3(64 * WM * WN), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -628,6 +628,9 @@ hipError_t launch(int config, const KernelArgs &a, int va, int vb, int64_t grid,
     case 4: return launch_staged<64, 64, 64, 2, 2, 2>(a, va, vb, grid, s);
     case 5: return launch_one<256, 256, 32, 2, 2, 4, true, 8, 8>(a, grid, s);
     case 6: return launch_one<256, 256, 32, 2, 2, 5, true, 8, 8>(a, grid, s);
+    case 7: return launch_one<256, 256, 64, 2, 4, 2, true, 8, 8>(a, grid, s);
+    case 8: return launch_one<256, 256, 32, 2, 4, 5, true, 8, 8>(a, grid, s);
+    case 9: return launch_one<256, 256, 64, 4, 2, 2, true, 8, 8>(a, grid, s);
     default: return hipErrorInvalidValue;
     }
 }

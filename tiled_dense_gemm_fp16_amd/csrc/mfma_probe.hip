@@ -1,0 +1,106 @@
+// mfma_probe.hip -- measurement probe: sustained v_mfma_f32_32x32x16_f16
+// throughput with no memory traffic, for operands of a chosen kind.
+//
+// The GEMM kernels are bound by the matrix cores.  Their nominal dense FP16
+// peak (256 CUs x 2.4 GHz x 4096 flop/clk) assumes the top clock, but the
+// clock the chip sustains under MFMA load depends on how much the operand
+// bits toggle.  This probe runs the GEMM's own instruction mix (a 4 x 4 block
+// of 32x32x16 MFMAs per wave, one wave per SIMD, 16 fp32 accumulator tiles)
+// with nothing but register operands, so its throughput is the practical
+// ceiling of the inner loop for that kind of data.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gemm_f16_probe.h"
+
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float float16v __attribute__((ext_vector_type(16)));
+
+template <int MODE>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+mfma_probe_kernel(const half8 *__restrict__ operands, float *__restrict__ out, int iters)
+{
+    const int t = blockIdx.x * blockDim.x + threadIdx.x;
+    const int lane = threadIdx.x & 63;
+    half8 x[2][4], y[2][4];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (MODE == GEMM_F16_PROBE_CONSTANT) {
+                for (int e = 0; e < 8; ++e) {
+                    x[s][i][e] = (_Float16)(0.001f * lane);
+                    y[s][i][e] = (_Float16)(0.01f * e);
+                }
+            } else {
+                // 2 x 8 distinct fragments per lane from the caller's random halves
+                x[s][i] = operands[((s * 8 + i) * 64 + lane) % GEMM_F16_PROBE_OPERAND_VECTORS];
+                y[s][i] = operands[((s * 8 + 4 + i) * 64 + lane) % GEMM_F16_PROBE_OPERAND_VECTORS];
+            }
+        }
+    if (MODE == GEMM_F16_PROBE_RANDOM_FIXED) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[1][i] = x[0][i];
+            y[1][i] = y[0][i];
+        }
+    }
+    float16v acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            acc[i][j] = float16v{};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(x[s][j], y[s][i], acc[i][j], 0, 0, 0);
+    }
+    float sum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                sum += acc[i][j][v];
+    out[t] = sum;
+}
+
+} // namespace
+
+extern "C" int gemm_f16_probe_mfma(int mode, int iters, int64_t blocks, const void *operands, void *out,
+                                   void *stream, double *flops)
+{
+    if (iters < 0 || blocks <= 0 || blocks > 0x7fffffff || !out || (mode != GEMM_F16_PROBE_CONSTANT && !operands))
+        return 1;
+    hipStream_t s = (hipStream_t)stream;
+    dim3 grid((unsigned)blocks), block(256);
+    switch (mode) {
+    case GEMM_F16_PROBE_CONSTANT:
+        hipLaunchKernelGGL(mfma_probe_kernel<GEMM_F16_PROBE_CONSTANT>, grid, block, 0, s, (const half8 *)operands,
+                           (float *)out, iters);
+        break;
+    case GEMM_F16_PROBE_RANDOM_FIXED:
+        hipLaunchKernelGGL(mfma_probe_kernel<GEMM_F16_PROBE_RANDOM_FIXED>, grid, block, 0, s,
+                           (const half8 *)operands, (float *)out, iters);
+        break;
+    case GEMM_F16_PROBE_RANDOM_CHANGING:
+        hipLaunchKernelGGL(mfma_probe_kernel<GEMM_F16_PROBE_RANDOM_CHANGING>, grid, block, 0, s,
+                           (const half8 *)operands, (float *)out, iters);
+        break;
+    default:
+        return 1;
+    }
+    if (hipGetLastError() != hipSuccess)
+        return 2;
+    if (flops)
+        *flops = (double)blocks * 4.0 /* waves */ * (double)iters * 32.0 /* MFMAs */ * 32768.0;
+    return 0;
+}
