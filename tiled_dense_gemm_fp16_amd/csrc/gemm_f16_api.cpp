@@ -13,21 +13,29 @@
 namespace gemm_f16_impl {
 
 const ConfigDesc kConfigs[kNumConfigs] = {
-    {"256x256x64_s2_direct", 256, 256, 64, 2, 4, true},
-    {"256x128x64_s3_direct", 256, 128, 64, 3, 4, true},
-    {"128x128x64_s3_direct", 128, 128, 64, 3, 4, true},
-    {"128x128x32_s2_staged", 128, 128, 32, 2, 4, false},
-    {"64x64x64_s2_staged", 64, 64, 64, 2, 4, false},
-    {"256x256x32_s4_direct", 256, 256, 32, 4, 4, true},
-    {"256x256x32_s5_direct", 256, 256, 32, 5, 4, true},
-    {"256x256x64_s2_direct_w8n", 256, 256, 64, 2, 8, true},
-    {"256x256x32_s5_direct_w8n", 256, 256, 32, 5, 8, true},
-    {"256x256x64_s2_direct_w8m", 256, 256, 64, 2, 8, true},
+    {"256x256x64_s2_direct", 256, 256, 64, 2, 4, true, 8},
+    {"256x128x64_s3_direct", 256, 128, 64, 3, 4, true, 8},
+    {"128x128x64_s3_direct", 128, 128, 64, 3, 4, true, 8},
+    {"128x128x32_s2_staged", 128, 128, 32, 2, 4, false, 1},
+    {"64x64x64_s2_staged", 64, 64, 64, 2, 4, false, 1},
+    {"256x256x32_s4_direct", 256, 256, 32, 4, 4, true, 8},
+    {"256x256x32_s5_direct", 256, 256, 32, 5, 4, true, 8},
+    {"256x256x64_s2_direct_w8n", 256, 256, 64, 2, 8, true, 8},
+    {"256x256x32_s5_direct_w8n", 256, 256, 32, 5, 8, true, 8},
+    {"256x256x64_s2_direct_w8m", 256, 256, 64, 2, 8, true, 8},
+    {"256x256x64_s2_staged_w8", 256, 256, 64, 2, 8, false, 4},
+    {"256x128x64_s2_staged", 256, 128, 64, 2, 4, false, 4},
 };
 
 namespace {
 
 constexpr int kComputeUnits = 256;   // MI355X
+
+// Tile rows walked together by the kernels' tile remap (L2 reuse); 4 measured
+// best on MI355X for 8192-row problems (8: -4 %, 16: -10 %).
+#ifndef GEMM_F16_GROUP_M
+#define GEMM_F16_GROUP_M 4
+#endif
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -76,19 +84,21 @@ gemm_f16_status_t validate(int64_t M, int64_t N, int64_t K, const void *A, const
 double config_efficiency(int c)
 {
     switch (c) {
-    case 7: return 1.00;   // 256x256x64, 8 waves
-    case 0: return 0.97;   // 256x256x64, 4 waves
-    case 1: return 0.90;   // 256x128x64
-    case 2: return 0.76;   // 128x128x64
-    case 3: return 0.52;   // 128x128x32 register-staged
-    case 4: return 0.30;   // 64x64x64 register-staged
+    case 7: return 1.00;    // 256x256x64 direct, 8 waves
+    case 0: return 0.97;    // 256x256x64 direct, 4 waves
+    case 1: return 0.90;    // 256x128x64 direct
+    case 10: return 0.85;   // 256x256x64 register-staged, 8 waves (vectors of 4 or 8)
+    case 2: return 0.76;    // 128x128x64 direct
+    case 11: return 0.66;   // 256x128x64 register-staged (vectors of 4 or 8)
+    case 3: return 0.46;    // 128x128x32 register-staged, any alignment
+    case 4: return 0.25;    // 64x64x64 register-staged, any alignment
     default: return 0.0;
     }
 }
 
 bool config_fits(int c, int va, int vb)
 {
-    return !kConfigs[c].direct || (va == 8 && vb == 8);
+    return va >= kConfigs[c].min_vec && vb >= kConfigs[c].min_vec;
 }
 
 void fill_plan(int c, int64_t M, int64_t N, int64_t K, int va, int vb, int vc, gemm_f16_plan_t *p)
@@ -102,8 +112,9 @@ void fill_plan(int c, int64_t M, int64_t N, int64_t K, int va, int vb, int vc, g
     p->stages = d.stages;
     p->threads = 64 * d.waves;
     p->direct_lds = d.direct ? 1 : 0;
-    p->vec_a = d.direct ? 8 : va;
-    p->vec_b = d.direct ? 8 : vb;
+    // wide staged tiles load vectors of 8 or 4 elements only
+    p->vec_a = d.direct ? 8 : (d.min_vec >= 4 ? (va >= 8 ? 8 : 4) : va);
+    p->vec_b = d.direct ? 8 : (d.min_vec >= 4 ? (vb >= 8 ? 8 : 4) : vb);
     p->vec_c = vc;
     p->tiles_m = ceil_div(M, d.block_m);
     p->tiles_n = ceil_div(N, d.block_n);
@@ -199,7 +210,7 @@ gemm_f16_status_t run(int64_t M, int64_t N, int64_t K, const void *A, const void
     a.K = (int)K;
     a.tiles_m = (int)plan.tiles_m;
     a.tiles_n = (int)plan.tiles_n;
-    a.group_m = 8;
+    a.group_m = GEMM_F16_GROUP_M;
     a.relu = epilogue == GEMM_F16_EPILOGUE_RELU ? 1 : 0;
     a.vec_c = plan.vec_c;
     hipError_t e = launch(plan.config, a, plan.vec_a, plan.vec_b, plan.grid, (hipStream_t)stream);

@@ -28,9 +28,10 @@ struct ConfigDesc {
     int stages;
     int waves;            // wave64s per workgroup (4: one per SIMD, 8: two)
     bool direct;          // operands move global -> LDS with buffer_load ... lds
+    int min_vec;          // smallest vector width (elements) of A and B loads it accepts
 };
 
-constexpr int kNumConfigs = 10;
+constexpr int kNumConfigs = 12;
 extern const ConfigDesc kConfigs[kNumConfigs];
 
 // Launch configuration `config` with `grid` workgroups on `s`.

@@ -39,6 +39,17 @@
 
 #include "gemm_f16_internal.h"
 
+// Build-time switches kept for tuning sweeps (defaults are the measured best):
+// GEMM_F16_SNAKE 1 walks each row of MFMA blocks in alternating direction so
+// that consecutive MFMAs share an operand (fewer operand bits toggle);
+// GEMM_F16_NO_XCD_REMAP 1 disables the XCD-aware tile order.
+#ifndef GEMM_F16_SNAKE
+#define GEMM_F16_SNAKE 1
+#endif
+#ifndef GEMM_F16_NO_XCD_REMAP
+#define GEMM_F16_NO_XCD_REMAP 0
+#endif
+
 namespace gemm_f16_impl {
 
 typedef _Float16 half_t;
@@ -81,6 +92,12 @@ __device__ __forceinline__ void wait_vm_lgkm0()
 {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));
+}
+
+// s_waitcnt lgkmcnt(0): every LDS access of this wave complete.
+__device__ __forceinline__ void wait_lgkm0()
+{
+    __builtin_amdgcn_s_waitcnt((0xF) | (0x3 << 14) | (0x7 << 4));
 }
 
 // ---- LDS swizzles ---------------------------------------------------------
@@ -132,10 +149,14 @@ __device__ __forceinline__ int swz_b(int row)
 __device__ __forceinline__ void tile_coords(int wg, int grid, int tiles_m, int tiles_n, int group_m,
                                             int &tm, int &tn)
 {
+#if GEMM_F16_NO_XCD_REMAP
+    int id = wg;
+#else
     constexpr int kXcds = 8;
     int per = grid / kXcds, rem = grid % kXcds;
     int xcd = wg % kXcds, local = wg / kXcds;
     int id = (xcd < rem) ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
+#endif
     int width = group_m * tiles_n;
     int group = id / width;
     int first_m = group * group_m;
@@ -356,16 +377,17 @@ gemm_f16_kernel(KernelArgs args)
             }
         }
     };
-    auto store_staged = [&](int s) {
+    auto store_staged = [&](half_t *dst_a, half_t *dst_b) {
         if constexpr (!DIRECT) {
 #pragma unroll
             for (int i = 0; i < T::A_VECS; ++i)
-                lds_store<VA>(As + s * T::A_STAGE + a_lds[i], a_reg[i]);
+                lds_store<VA>(dst_a + a_lds[i], a_reg[i]);
 #pragma unroll
             for (int i = 0; i < T::B_VECS; ++i)
-                lds_store<VB>(Bs + s * T::B_STAGE + b_lds[i], b_reg[i]);
+                lds_store<VB>(dst_b + b_lds[i], b_reg[i]);
         } else {
-            (void)s;
+            (void)dst_a;
+            (void)dst_b;
         }
     };
 
@@ -420,130 +442,135 @@ gemm_f16_kernel(KernelArgs args)
 #pragma unroll
         for (int i = 0; i < T::TM; ++i)
 #pragma unroll
-            for (int j = 0; j < T::TN; ++j)
+            for (int jj = 0; jj < T::TN; ++jj) {
+#if GEMM_F16_SNAKE
+                const int j = (i & 1) ? T::TN - 1 - jj : jj;
+#else
+                const int j = jj;
+#endif
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.x[j], f.y[i], acc[i][j], 0, 0, 0);
+            }
     };
     // Ask the scheduler to alternate the MFMAs of one step with the LDS reads
-    // of the next step (and, after a barrier, with the next tile's loads), so
-    // the matrix core keeps busy while those are in flight.
+    // of the next step (and, after a barrier, with the next tile's loads and
+    // LDS writes), so the matrix core keeps busy while those are in flight.
     constexpr int kMfmaPerStep = T::TM * T::TN;
     constexpr int kReadsPerStep = T::TM + 2 * T::TN;
-    auto interleave = [&](int n_vmem) {
+    auto interleave = [&](int n_vmem, int n_dswrite) {
 #pragma unroll
         for (int i = 0; i < kMfmaPerStep; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // one MFMA
             if (i < kReadsPerStep)
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // one LDS read
+            if (i < n_dswrite)
+                __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);      // one LDS write
             if (i < n_vmem)
                 __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);      // one global load
         }
     };
-    // plain (non-pipelined) math on one stage, for the register-staged kernels
-    auto compute = [&](const half_t *as, const half_t *bs) {
-#pragma unroll
-        for (int ks = 0; ks < BK / 16; ++ks) {
-            Frags f;
-            load_frags(f, as, bs, ks);
-            mma(f);
-        }
-    };
 
     // ---- pipelined K loop ----
-    if constexpr (DIRECT) {
-        // Software pipeline over the k steps of a tile with two fragment sets:
-        // the reads of step s+1 are in flight while step s multiplies.  The
-        // last step of a tile is multiplied after the next barrier, so that
-        // the first reads of the next tile overlap MFMA work too.
-        constexpr int NS = BK / 16;
-        static_assert(NS % 2 == 0, "an even number of k steps per tile");
-        Frags f0, f1;
-        // One tile: start the loads of tile kt_next into (wr_a, wr_b), then the
-        // math on stage (rd_a, rd_b); f1 holds the previous tile's last step
-        // when `pending`.  The restrict qualifiers tell the compiler that the
-        // stage being filled is not the stage being read, so it does not make
-        // the LDS reads wait for the loads just issued.
-        auto step = [&](const half_t *__restrict__ rd_a, const half_t *__restrict__ rd_b,
-                        half_t *__restrict__ wr_a, half_t *__restrict__ wr_b, int kt_next, bool pending) {
+    // Software pipeline over the k steps of a tile with two fragment sets:
+    // the reads of step s+1 are in flight while step s multiplies.  The last
+    // step of a tile is multiplied after the next barrier, so that the first
+    // reads of the next tile overlap MFMA work too.
+    //  direct:  stage ring of STAGES tiles filled by DMA, tile kt+STAGES-1
+    //           requested at step kt;
+    //  staged:  registers hold tile kt+1 at the start of step kt; the step
+    //           writes them to the free stage, requests tile kt+2 into the
+    //           registers, then multiplies tile kt (two LDS stages suffice).
+    constexpr int NS = BK / 16;
+    static_assert(NS % 2 == 0, "an even number of k steps per tile");
+    static_assert(DIRECT || STAGES == 2, "register-staged kernels use two LDS stages");
+    constexpr int LOOKAHEAD = DIRECT ? STAGES - 1 : 2;
+    Frags f0, f1;
+    // One tile: bring tile kt_next toward LDS -- (wr_a, wr_b) is the stage it
+    // (direct) or the register-held tile (staged) goes to -- then the math on
+    // stage (rd_a, rd_b); f1 holds the previous tile's last step when
+    // `pending`.  The restrict qualifiers tell the compiler that the stage
+    // being filled is not the stage being read, so it does not make the LDS
+    // reads wait for those loads or writes.
+    auto step = [&](const half_t *__restrict__ rd_a, const half_t *__restrict__ rd_b,
+                    half_t *__restrict__ wr_a, half_t *__restrict__ wr_b, int kt_next, bool pending) {
+        if constexpr (DIRECT) {
             issue_loads(kt_next, wr_a, wr_b);   // past the last tile: zeros into a retired stage
-            load_frags(f0, rd_a, rd_b, 0);
-            if (pending)
-                mma(f1);
-            interleave(T::LOADS_PER_TILE);
-            __builtin_amdgcn_sched_barrier(0);
+        } else {
+            wait_vmcnt<0>();                    // tile kt+1 is in the registers
+            store_staged(wr_a, wr_b);
+            issue_loads(kt_next, nullptr, nullptr);
+        }
+        load_frags(f0, rd_a, rd_b, 0);
+        if (pending)
+            mma(f1);
+        interleave(DIRECT ? T::LOADS_PER_TILE : 0, DIRECT ? 0 : T::A_VECS + T::B_VECS);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int ks = 0; ks + 1 < NS; ks += 2) {
-                load_frags(f1, rd_a, rd_b, ks + 1);
-                mma(f0);
-                interleave(0);
+        for (int ks = 0; ks + 1 < NS; ks += 2) {
+            load_frags(f1, rd_a, rd_b, ks + 1);
+            mma(f0);
+            interleave(0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            if (ks + 2 < NS) {
+                load_frags(f0, rd_a, rd_b, ks + 2);
+                mma(f1);
+                interleave(0, 0);
                 __builtin_amdgcn_sched_barrier(0);
-                if (ks + 2 < NS) {
-                    load_frags(f0, rd_a, rd_b, ks + 2);
-                    mma(f1);
-                    interleave(0);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
             }
-            // f1 now holds step NS-1 of this tile, multiplied by the next call
-        };
-        // wait until tile kt has landed in LDS for every wave, and this wave's
-        // reads of the stage about to be refilled have completed
-        auto tile_ready = [&](int kt) {
+        }
+        // f1 now holds step NS-1 of this tile, multiplied by the next call
+    };
+    // Wait until tile kt is in LDS for every wave: this wave's loads (direct)
+    // or LDS writes (staged) of it have completed, and so have its reads of
+    // the stage about to be refilled; then the workgroup barrier.
+    auto tile_ready = [&](int kt) {
+        if constexpr (DIRECT) {
             if (kt + STAGES - 2 < nk)
                 wait_vm_lgkm0<(STAGES - 2) * T::LOADS_PER_TILE>();
             else
                 wait_vm_lgkm0<0>();
-            __builtin_amdgcn_s_barrier();
-            __builtin_amdgcn_sched_barrier(0);
-        };
+        } else {
+            (void)kt;
+            wait_lgkm0();
+        }
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    if constexpr (DIRECT) {
 #pragma unroll
         for (int s = 0; s < STAGES - 1; ++s)
             if (s < nk)
                 issue_loads(s, As + s * T::A_STAGE, Bs + s * T::B_STAGE);
-        if (nk > 0) {
-            tile_ready(0);
-            step(As, Bs, As + (STAGES - 1) * T::A_STAGE, Bs + (STAGES - 1) * T::B_STAGE, STAGES - 1, false);
-        }
-        // tiles 1 .. nk-1, unrolled so that every stage index is a constant
-        for (int kt0 = 1; kt0 < nk; kt0 += STAGES) {
-#pragma unroll
-            for (int u = 0; u < STAGES; ++u) {
-                const int kt = kt0 + u;
-                const int s = (1 + u) % STAGES;
-                const int w = (s + STAGES - 1) % STAGES;
-                if (kt < nk) {
-                    tile_ready(kt);
-                    step(As + s * T::A_STAGE, Bs + s * T::B_STAGE, As + w * T::A_STAGE, Bs + w * T::B_STAGE,
-                         kt + STAGES - 1, true);
-                }
-            }
-        }
-        if (nk > 0)
-            mma(f1);
-        wait_vmcnt<0>();   // the tail's zero-filling loads must land before the workgroup retires
     } else {
-        // registers hold one tile in flight; LDS has STAGES stages (>= 2)
         if (nk > 0) {
             issue_loads(0, nullptr, nullptr);
-            store_staged(0);
-        }
-        if (nk > 1)
+            wait_vmcnt<0>();
+            store_staged(As, Bs);
             issue_loads(1, nullptr, nullptr);
-        __syncthreads();
-        for (int kt0 = 0; kt0 < nk; kt0 += STAGES) {
+        }
+    }
+    // the stage written during step kt is (kt + W_OFF) % STAGES
+    constexpr int W_OFF = DIRECT ? LOOKAHEAD : 1;
+    if (nk > 0) {
+        tile_ready(0);
+        step(As, Bs, As + (W_OFF % STAGES) * T::A_STAGE, Bs + (W_OFF % STAGES) * T::B_STAGE, LOOKAHEAD, false);
+    }
+    // tiles 1 .. nk-1, unrolled so that every stage index is a constant
+    for (int kt0 = 1; kt0 < nk; kt0 += STAGES) {
 #pragma unroll
-            for (int s = 0; s < STAGES; ++s) {
-                const int kt = kt0 + s;
-                if (kt < nk) {
-                    if (kt + 1 < nk)
-                        store_staged((s + 1) % STAGES);     // tile kt+1 -> the stage freed at kt-1
-                    if (kt + 2 < nk)
-                        issue_loads(kt + 2, nullptr, nullptr);
-                    compute(As + s * T::A_STAGE, Bs + s * T::B_STAGE);
-                    __syncthreads();
-                }
+        for (int u = 0; u < STAGES; ++u) {
+            const int kt = kt0 + u;
+            const int s = (1 + u) % STAGES;                 // stage holding tile kt
+            const int w = (s + W_OFF) % STAGES;
+            if (kt < nk) {
+                tile_ready(kt);
+                step(As + s * T::A_STAGE, Bs + s * T::B_STAGE, As + w * T::A_STAGE, Bs + w * T::B_STAGE,
+                     kt + LOOKAHEAD, true);
             }
         }
     }
+    if (nk > 0)
+        mma(f1);
+    wait_vmcnt<0>();   // the tail's zero-filling loads must land before the workgroup retires
 
     // ---- epilogue: optional ReLU, RNE to fp16, masked stores ----
     const int c_rows = min(BM, M - m0);
@@ -618,6 +645,18 @@ static hipError_t launch_staged(const KernelArgs &a, int va, int vb, int64_t gri
 #undef GEMM_F16_VB
 }
 
+// Wide register-staged tiles keep every vector width >= 4 (narrower vectors
+// would need more staging registers than a 256-wide tile leaves free).
+template <int BM, int BN, int BK, int WM, int WN, int STAGES>
+static hipError_t launch_staged_wide(const KernelArgs &a, int va, int vb, int64_t grid, hipStream_t s)
+{
+    if (va == 8)
+        return vb == 8 ? launch_one<BM, BN, BK, WM, WN, STAGES, false, 8, 8>(a, grid, s)
+                       : launch_one<BM, BN, BK, WM, WN, STAGES, false, 8, 4>(a, grid, s);
+    return vb == 8 ? launch_one<BM, BN, BK, WM, WN, STAGES, false, 4, 8>(a, grid, s)
+                   : launch_one<BM, BN, BK, WM, WN, STAGES, false, 4, 4>(a, grid, s);
+}
+
 hipError_t launch(int config, const KernelArgs &a, int va, int vb, int64_t grid, hipStream_t s)
 {
     switch (config) {
@@ -631,6 +670,8 @@ hipError_t launch(int config, const KernelArgs &a, int va, int vb, int64_t grid,
     case 7: return launch_one<256, 256, 64, 2, 4, 2, true, 8, 8>(a, grid, s);
     case 8: return launch_one<256, 256, 32, 2, 4, 5, true, 8, 8>(a, grid, s);
     case 9: return launch_one<256, 256, 64, 4, 2, 2, true, 8, 8>(a, grid, s);
+    case 10: return launch_staged_wide<256, 256, 64, 2, 4, 2>(a, va, vb, grid, s);
+    case 11: return launch_staged_wide<256, 128, 64, 2, 2, 2>(a, va, vb, grid, s);
     default: return hipErrorInvalidValue;
     }
 }
