@@ -152,8 +152,9 @@ def traffic_from(directory: str, workload: str, config_name: str) -> int:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=300,
+                    help="untimed calls first (about 0.3 s at 8192^3, so the clocks settle)")
     ap.add_argument("--workload", default="gemm_8192")
     ap.add_argument("--config", type=int, default=-1, help="kernel configuration (-1: automatic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")

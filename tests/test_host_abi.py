@@ -113,7 +113,7 @@ def test_plan_geometry_and_vector_widths():
     assert p["grid"] == p["tiles_m"] * p["tiles_n"]
     assert p["k_tiles"] == -(-4100 // p["block_k"])
     assert p["vec_a"] == 4                       # K = 4100: rows only 8-byte aligned
-    assert p["vec_b"] == 8 and p["vec_c"] == 4
+    assert p["vec_b"] == 8 and p["vec_c"] == 8          # N = 5000: 16-byte stores of C
     assert p["direct_lds"] == 0                  # 16-byte direct loads need 16-byte rows
     assert p["flops"] == 2.0 * 3000 * 5000 * 4100
     assert p["min_bytes"] == 2.0 * (3000 * 4100 + 4100 * 5000 + 3000 * 5000)
@@ -121,7 +121,9 @@ def test_plan_geometry_and_vector_widths():
     p = g.plan(33, 17, 9, FAKE + 2, FAKE + 6, FAKE + 2)
     assert (p["vec_a"], p["vec_b"], p["vec_c"]) == (1, 1, 1)
     p = g.plan(64, 64, 64, FAKE + 4, FAKE + 8, FAKE)
-    assert (p["vec_a"], p["vec_b"], p["vec_c"]) == (2, 4, 4)
+    assert (p["vec_a"], p["vec_b"], p["vec_c"]) == (2, 4, 8)
+    p = g.plan(64, 60, 64, FAKE, FAKE, FAKE + 8)
+    assert p["vec_c"] == 4
     # large aligned problems take a direct-to-LDS configuration
     assert g.plan(8192, 8192, 8192, FAKE, FAKE, FAKE)["direct_lds"] == 1
     # a direct configuration refuses a misaligned pitch

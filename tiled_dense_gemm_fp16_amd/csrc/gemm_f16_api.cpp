@@ -152,7 +152,7 @@ gemm_f16_status_t make_plan(int64_t M, int64_t N, int64_t K, const void *A, cons
     if (config != GEMM_F16_CONFIG_AUTO && (config < 0 || config >= kNumConfigs))
         return GEMM_F16_ERROR_INVALID_VALUE;
     const int va = vec_width(A, K), vb = vec_width(B, N);
-    const int vc = (N % 4 == 0 && (uintptr_t)C % 8 == 0) ? 4 : 1;
+    const int vc = (N % 8 == 0 && (uintptr_t)C % 16 == 0) ? 8 : (N % 4 == 0 && (uintptr_t)C % 8 == 0) ? 4 : 1;
     int c = config == GEMM_F16_CONFIG_AUTO ? choose_config(M, N, va, vb) : config;
     if (!config_fits(c, va, vb))
         return GEMM_F16_ERROR_INVALID_VALUE;

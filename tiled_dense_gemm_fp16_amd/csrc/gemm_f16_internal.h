@@ -18,7 +18,8 @@ struct KernelArgs {
     int tiles_m, tiles_n;
     int group_m;         // tile rows walked together by the tile remap
     int relu;            // 1: max(acc, 0) before the fp16 conversion
-    int vec_c;           // 4: 8-byte stores of C are aligned; 1: 2-byte stores
+    int vec_c;           // 8: 16-byte stores of C are aligned (LDS-staged write-back);
+                         // 4: 8-byte stores; 1: 2-byte stores
 };
 
 // Static description of one compiled kernel configuration.

@@ -572,12 +572,79 @@ gemm_f16_kernel(KernelArgs args)
         mma(f1);
     wait_vmcnt<0>();   // the tail's zero-filling loads must land before the workgroup retires
 
-    // ---- epilogue: optional ReLU, RNE to fp16, masked stores ----
+    // ---- epilogue: optional ReLU, RNE to fp16, store ----
     const int c_rows = min(BM, M - m0);
     half_t *c_base = args.C + (int64_t)m0 * N;
     const __amdgpu_buffer_rsrc_t c_rsrc = make_rsrc(c_base, (uint32_t)c_rows * (uint32_t)N * 2u);
     const bool relu = args.relu != 0;
     const int vec_c = args.vec_c;
+    // The four values a lane holds for MFMA block (i, j), register group g:
+    // row wm0 + 32 i + lane % 32, columns wn0 + 32 j + 8 g + 4 (lane / 32) .. +3.
+    auto out4 = [&](int i, int j, int g, half_t &h0, half_t &h1, half_t &h2, half_t &h3) {
+        float v0 = acc[i][j][4 * g + 0], v1 = acc[i][j][4 * g + 1];
+        float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
+        if (relu) {
+            v0 = __builtin_fmaxf(v0, 0.0f);
+            v1 = __builtin_fmaxf(v1, 0.0f);
+            v2 = __builtin_fmaxf(v2, 0.0f);
+            v3 = __builtin_fmaxf(v3, 0.0f);
+        }
+        // RNE conversions kept as scalars: hipcc mis-lowers a bit_cast of a
+        // single element of an fp16 ext_vector (it re-reads element 0)
+        h0 = (half_t)v0;
+        h1 = (half_t)v1;
+        h2 = (half_t)v2;
+        h3 = (half_t)v3;
+    };
+    static_assert(BM * BN * 2 <= T::LDS_BYTES, "the output tile fits in the LDS stages");
+    if (vec_c == 8) {
+        // N % 8 == 0 and C 16-byte aligned: stage the fp16 tile through the
+        // (now idle) LDS and write it as 16-byte pieces of consecutive
+        // columns, so that every row of the tile leaves as whole cache lines.
+        // LDS layout [BM][BN] with the 8-byte unit index XOR-ed with the row's
+        // low bits: the 32 lanes of a pass write 32 different rows of one
+        // column unit, and these land in 32 different bank pairs.
+        constexpr int UNITS = BN / 4;                       // 8-byte units per row
+        constexpr int UMASK = (UNITS < 32 ? UNITS : 32) - 1;
+        half_t *ct = lds;
+        wait_vmcnt<0>();
+        wait_lgkm0();
+        __builtin_amdgcn_s_barrier();                       // every wave is done with the stages
+#pragma unroll
+        for (int i = 0; i < T::TM; ++i) {
+            const int r = wm0 + 32 * i + (lane & 31);
+#pragma unroll
+            for (int j = 0; j < T::TN; ++j)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    half_t h0, h1, h2, h3;
+                    out4(i, j, g, h0, h1, h2, h3);
+                    const int u = (wn0 + 32 * j + 8 * g) / 4 + (lane >> 5);
+                    half4 h = {h0, h1, h2, h3};
+                    *reinterpret_cast<half4 *>(ct + r * BN + 4 * (u ^ (r & UMASK))) = h;
+                }
+        }
+        wait_lgkm0();
+        __builtin_amdgcn_s_barrier();
+        constexpr int CHUNKS_PER_ROW = BN / 8;
+        constexpr int PER_THREAD = BM * CHUNKS_PER_ROW / T::kThreads;
+        static_assert(BM * CHUNKS_PER_ROW % T::kThreads == 0, "output chunks split evenly");
+#pragma unroll
+        for (int q = 0; q < PER_THREAD; ++q) {
+            const int id = tid + q * T::kThreads;
+            const int r = id / CHUNKS_PER_ROW;
+            const int c = id % CHUNKS_PER_ROW;
+            const int sw = r & UMASK;
+            // units 2c and 2c+1 sit side by side at unit (2c ^ sw) & ~1, swapped when sw is odd
+            int4v v = *reinterpret_cast<const int4v *>(ct + r * BN + 4 * ((2 * c ^ sw) & ~1));
+            if (sw & 1)
+                v = int4v{v[2], v[3], v[0], v[1]};
+            const int n = n0 + 8 * c;
+            const uint32_t off = ((uint32_t)r * (uint32_t)N + (uint32_t)n) * 2u;
+            __builtin_amdgcn_raw_buffer_store_b128(v, c_rsrc, off | oob_unless(n < N), 0, 0);
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < T::TM; ++i) {
         const int r = wm0 + 32 * i + (lane & 31);            // row inside the panel
@@ -586,17 +653,8 @@ gemm_f16_kernel(KernelArgs args)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int n = n0 + wn0 + 32 * j + 8 * g + 4 * (lane >> 5);
-                float v0 = acc[i][j][4 * g + 0], v1 = acc[i][j][4 * g + 1];
-                float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
-                if (relu) {
-                    v0 = __builtin_fmaxf(v0, 0.0f);
-                    v1 = __builtin_fmaxf(v1, 0.0f);
-                    v2 = __builtin_fmaxf(v2, 0.0f);
-                    v3 = __builtin_fmaxf(v3, 0.0f);
-                }
-                // RNE conversions kept as scalars: hipcc mis-lowers a bit_cast of a
-                // single element of an fp16 ext_vector (it re-reads element 0)
-                const half_t h0 = (half_t)v0, h1 = (half_t)v1, h2 = (half_t)v2, h3 = (half_t)v3;
+                half_t h0, h1, h2, h3;
+                out4(i, j, g, h0, h1, h2, h3);
                 const uint32_t off = ((uint32_t)r * (uint32_t)N + (uint32_t)n) * 2u;
                 if (vec_c == 4) {
                     // N % 4 == 0: the four columns are all inside or all outside
