@@ -105,6 +105,23 @@ gemm_f16_status_t gemm_f16_ex(int64_t M, int64_t N, int64_t K,
                               const void *A, const void *B, void *C,
                               int epilogue, int config, void *stream);
 
+/*
+ * C = epi(op(A) . op(B)) with either operand given transposed: the
+ * "transpose_B" form of the pages' tile GEMM ("TileLang：比 Triton 低一层的
+ * tile 语言", section "FlashAttention：在线 softmax 写成 tile 代码", where the
+ * score block is Q . K^T) and its A-side counterpart.
+ *   trans_a = 0: A is M x K row-major (lda = K); 1: A is stored K x M
+ *                row-major (lda = M) and op(A) = A^T.
+ *   trans_b = 0: B is K x N row-major (ldb = N); 1: B is stored N x K
+ *                row-major (ldb = K) and op(B) = B^T.
+ * Other arguments, ownership and errors as gemm_f16_ex (config may be
+ * GEMM_F16_CONFIG_AUTO).  Transposed layouts run on a subset of the
+ * configurations; a trans flag other than 0 or 1 is INVALID_VALUE.
+ */
+gemm_f16_status_t gemm_f16_trans(int64_t M, int64_t N, int64_t K,
+                                 const void *A, int trans_a, const void *B, int trans_b,
+                                 void *C, int epilogue, int config, void *stream);
+
 /* How a call would run; filled by gemm_f16_plan without any HIP call. */
 typedef struct gemm_f16_plan {
     int32_t config;        /* configuration index actually chosen */
@@ -124,6 +141,8 @@ typedef struct gemm_f16_plan {
     int64_t lds_bytes;     /* LDS per workgroup */
     double flops;          /* 2 M N K: the algorithmic work of the call */
     double min_bytes;      /* 2 (M K + K N + M N): operands read once, C written once */
+    int32_t trans_a;       /* 1: A stored K x M */
+    int32_t trans_b;       /* 1: B stored N x K */
 } gemm_f16_plan_t;
 
 /*
@@ -135,6 +154,11 @@ typedef struct gemm_f16_plan {
 gemm_f16_status_t gemm_f16_plan(int64_t M, int64_t N, int64_t K,
                                 const void *A, const void *B, const void *C,
                                 int config, gemm_f16_plan_t *plan);
+
+/* As gemm_f16_plan, for the layouts of gemm_f16_trans. */
+gemm_f16_status_t gemm_f16_plan_trans(int64_t M, int64_t N, int64_t K,
+                                      const void *A, int trans_a, const void *B, int trans_b,
+                                      const void *C, int config, gemm_f16_plan_t *plan);
 
 /* Number of kernel configurations compiled into the library. */
 int gemm_f16_num_configs(void);

@@ -93,10 +93,18 @@ def encode(x) -> np.ndarray:
     return out
 
 
-def gemm(A, B, relu: bool = False, threads: int = 0) -> np.ndarray:
-    """C = rne16(epi(A . B)) for A (M x K) and B (K x N) binary16; returns uint16 (M x N)."""
+def gemm(A, B, relu: bool = False, threads: int = 0, trans_a: bool = False,
+         trans_b: bool = False) -> np.ndarray:
+    """C = rne16(epi(op(A) . op(B))) for binary16 operands; returns uint16 (M x N).
+
+    op(X) is X, or its transpose when the flag is set (A given K x M, B given
+    N x K); the transpose is a plain array copy before the product."""
     A = _as_bits(A, "A")
     B = _as_bits(B, "B")
+    if trans_a:
+        A = np.ascontiguousarray(A.T)
+    if trans_b:
+        B = np.ascontiguousarray(B.T)
     if A.ndim != 2 or B.ndim != 2 or A.shape[1] != B.shape[0]:
         raise ValueError(f"shape mismatch: A {A.shape}, B {B.shape}")
     M, K = A.shape

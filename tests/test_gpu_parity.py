@@ -41,12 +41,12 @@ def check(a, b, epilogue="none", config=g.CONFIG_AUTO, label=""):
     return res
 
 
-def configs_for(M, N, K):
-    """Every configuration that accepts this (aligned-pointer) shape."""
+def configs_for(M, N, K, trans_a=False, trans_b=False):
+    """Every configuration that accepts this (aligned-pointer) shape and layout."""
     out = []
     for c in range(g.num_configs()):
         try:
-            g.plan(M, N, K, 1 << 20, 1 << 20, 1 << 20, config=c)
+            g.plan(M, N, K, 1 << 20, 1 << 20, 1 << 20, config=c, trans_a=trans_a, trans_b=trans_b)
             out.append(c)
         except g.GemmError:
             pass
@@ -167,6 +167,56 @@ def test_deterministic():
     first = u16(g.gemm(ad, bd))
     for _ in range(3):
         assert np.array_equal(u16(g.gemm(ad, bd)), first)
+
+
+# ---- transposed operands: A given K x M and/or B given N x K ----
+
+LAYOUTS = [(False, True), (True, False), (True, True)]
+
+
+def check_trans(a_st, b_st, ta, tb, epilogue="none", config=g.CONFIG_AUTO):
+    print(f"[parity] trans_a={ta} trans_b={tb} {tuple(a_st.shape)} {tuple(b_st.shape)} config={config}",
+          flush=True)
+    c = g.gemm(a_st.to(DEV), b_st.to(DEV), epilogue=epilogue, config=config, trans_a=ta, trans_b=tb)
+    torch.cuda.synchronize()
+    ref = oracle.gemm(u16(a_st), u16(b_st), relu=(epilogue == "relu"), trans_a=ta, trans_b=tb)
+    res = oracle.compare(u16(c), ref)
+    assert res["pass"], (ta, tb, config, res)
+
+
+def stored(M, N, K, ta, tb, seed):
+    a, b = workloads.draw(M, N, K, "uniform", seed)
+    return (a.t().contiguous() if ta else a), (b.t().contiguous() if tb else b)
+
+
+@pytest.mark.parametrize("ta,tb", LAYOUTS)
+@pytest.mark.parametrize("shape", [(520, 392, 200), (256, 256, 64), (300, 264, 136), (64, 1040, 8)])
+def test_transposed_layouts_every_config(ta, tb, shape):
+    M, N, K = shape
+    a_st, b_st = stored(M, N, K, ta, tb, M + N + K)
+    cfgs = configs_for(M, N, K, ta, tb)
+    assert len(cfgs) >= 2
+    for c in cfgs:
+        check_trans(a_st, b_st, ta, tb, config=c)
+
+
+@pytest.mark.parametrize("ta,tb", LAYOUTS)
+@pytest.mark.parametrize("shape", [(37, 45, 53), (130, 129, 67), (65, 66, 34), (3, 5, 7)])
+@pytest.mark.parametrize("epilogue", ["none", "relu"])
+def test_transposed_layouts_ragged(ta, tb, shape, epilogue):
+    M, N, K = shape
+    a_st, b_st = stored(M, N, K, ta, tb, 5 * M + N + K)
+    check_trans(a_st, b_st, ta, tb, epilogue)
+    for c in configs_for(M, N, K, ta, tb):
+        check_trans(a_st, b_st, ta, tb, epilogue, config=c)
+
+
+def test_transposed_layout_large():
+    # Q . K^T-shaped product at a size that runs the 256x256 direct kernel
+    M, N, K = 2048, 2304, 1024
+    a, b_st = stored(M, N, K, False, True, 99)
+    assert g.plan(M, N, K, 1 << 20, 1 << 20, 1 << 20, trans_b=True)["direct_lds"] == 1
+    check_trans(a, b_st, False, True)
 
 
 # ---- the benchmark workloads, in the configuration the benchmark launches ----

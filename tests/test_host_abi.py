@@ -154,6 +154,35 @@ def test_invalid_arguments_rejected_before_any_launch(args, status):
     assert g.gemm_f16_raw(M, N, K, A, B, C, 0, config=0) == status
 
 
+def test_transposed_layout_planning():
+    # vector widths follow the pitch of each matrix as stored
+    p = g.plan(64, 48, 40, FAKE, FAKE, FAKE, trans_a=True)            # A stored 40 x 64: pitch M = 64
+    assert (p["vec_a"], p["trans_a"], p["trans_b"]) == (8, 1, 0)
+    p = g.plan(66, 48, 40, FAKE, FAKE, FAKE, trans_a=True)            # pitch 66: single elements
+    assert p["vec_a"] == 1 and p["direct_lds"] == 0
+    p = g.plan(64, 48, 36, FAKE, FAKE, FAKE, trans_b=True)            # B stored 48 x 36: pitch K = 36
+    assert p["vec_b"] == 1 and p["trans_b"] == 1
+    p = g.plan(8192, 8192, 8192, FAKE, FAKE, FAKE, trans_a=True, trans_b=True)
+    assert p["direct_lds"] == 1
+    # only some configurations are compiled for transposed layouts; the others refuse
+    ok = [c for c in range(g.num_configs()) if _plans(c, True)]
+    assert 2 <= len(ok) < g.num_configs()
+    for c in range(g.num_configs()):
+        assert _plans(c, False)
+    # flags other than 0 / 1
+    assert g.lib().gemm_f16_trans(4, 4, 4, FAKE, 2, FAKE * 3, 0, FAKE * 2, 0, -1, None) == 1
+    assert g.lib().gemm_f16_trans(4, 4, 4, FAKE, 0, FAKE * 3, -1, FAKE * 2, 0, -1, None) == 1
+    assert g.gemm_f16_raw(0, 4, 4, 0, FAKE, 0, 0, trans_a=True) == 0
+
+
+def _plans(c, trans):
+    try:
+        g.plan(4096, 4096, 4096, FAKE, FAKE, FAKE, config=c, trans_b=trans)
+        return True
+    except g.GemmError:
+        return False
+
+
 def test_bad_epilogue_and_config():
     assert g.gemm_f16_raw(4, 4, 4, FAKE, FAKE * 3, FAKE * 2, 2) == 1
     assert g.gemm_f16_raw(4, 4, 4, FAKE, FAKE * 3, FAKE * 2, -1) == 1

@@ -197,3 +197,15 @@ def test_output_moments_match_distribution(dist, K, var):
     c = oracle.decode(oracle.gemm(bits(A), bits(B)))
     assert abs(c.mean()) < 0.05 * np.sqrt(var)
     assert abs(c.var() / var - 1.0) < 0.08
+
+
+@pytest.mark.parametrize("ta,tb", [(False, True), (True, False), (True, True)])
+def test_transposed_operands_match_brute_force(ta, tb):
+    # op(A) . op(B) with A given K x M and/or B given N x K
+    rng = np.random.default_rng(int(ta) * 2 + int(tb))
+    M, N, K = 4, 5, 6
+    A = exact_range_operands(rng, (K, M) if ta else (M, K))
+    B = exact_range_operands(rng, (N, K) if tb else (K, N))
+    opA = np.ascontiguousarray(A.T) if ta else A
+    opB = np.ascontiguousarray(B.T) if tb else B
+    assert np.array_equal(oracle.gemm(A, B, trans_a=ta, trans_b=tb), brute_force.gemm(opA, opB))

@@ -37,6 +37,7 @@ class Plan(ctypes.Structure):
         ("vec_c", ctypes.c_int32), ("tiles_m", ctypes.c_int64), ("tiles_n", ctypes.c_int64),
         ("grid", ctypes.c_int64), ("k_tiles", ctypes.c_int64), ("lds_bytes", ctypes.c_int64),
         ("flops", ctypes.c_double), ("min_bytes", ctypes.c_double),
+        ("trans_a", ctypes.c_int32), ("trans_b", ctypes.c_int32),
     ]
 
     def as_dict(self) -> dict:
@@ -46,7 +47,9 @@ class Plan(ctypes.Structure):
 SIGNATURES = {
     "gemm_f16": ([_i64, _i64, _i64, _vp, _vp, _vp, _int, _vp], _int),
     "gemm_f16_ex": ([_i64, _i64, _i64, _vp, _vp, _vp, _int, _int, _vp], _int),
+    "gemm_f16_trans": ([_i64, _i64, _i64, _vp, _int, _vp, _int, _vp, _int, _int, _vp], _int),
     "gemm_f16_plan": ([_i64, _i64, _i64, _vp, _vp, _vp, _int, ctypes.POINTER(Plan)], _int),
+    "gemm_f16_plan_trans": ([_i64, _i64, _i64, _vp, _int, _vp, _int, _vp, _int, ctypes.POINTER(Plan)], _int),
     "gemm_f16_num_configs": ([], _int),
     "gemm_f16_config_name": ([_int], ctypes.c_char_p),
     "gemm_f16_stage_bytes": ([_i64, _i64, _i64, _i64], _i64),
@@ -96,33 +99,37 @@ def stage_bytes(block_m: int, block_n: int, block_k: int, stages: int) -> int:
 
 
 def plan(M: int, N: int, K: int, A_ptr: int = 0, B_ptr: int = 0, C_ptr: int = 0,
-         config: int = CONFIG_AUTO) -> dict:
+         config: int = CONFIG_AUTO, trans_a: bool = False, trans_b: bool = False) -> dict:
     """How gemm_f16 would run this shape (pure host logic, no GPU needed).
     Pointers only matter for alignment; 0 stands for an aligned buffer."""
     p = Plan()
-    st = lib().gemm_f16_plan(M, N, K, A_ptr or None, B_ptr or None, C_ptr or None, config,
-                             ctypes.byref(p))
+    st = lib().gemm_f16_plan_trans(M, N, K, A_ptr or None, int(trans_a), B_ptr or None, int(trans_b),
+                                   C_ptr or None, config, ctypes.byref(p))
     if st != SUCCESS:
         raise GemmError(st, "gemm_f16_plan")
     return p.as_dict()
 
 
 def gemm_f16_raw(M: int, N: int, K: int, A_ptr: int, B_ptr: int, C_ptr: int, epilogue: int = 0,
-                 stream: int = 0, config: int = CONFIG_AUTO) -> int:
-    """Call the C entry point with raw device addresses; returns the status code."""
+                 stream: int = 0, config: int = CONFIG_AUTO, trans_a: bool = False,
+                 trans_b: bool = False) -> int:
+    """Call the C entry points with raw device addresses; returns the status code."""
+    A, B, C, S = A_ptr or None, B_ptr or None, C_ptr or None, stream or None
+    if trans_a or trans_b:
+        return int(lib().gemm_f16_trans(M, N, K, A, int(trans_a), B, int(trans_b), C, epilogue, config, S))
     if config == CONFIG_AUTO:
-        return int(lib().gemm_f16(M, N, K, A_ptr or None, B_ptr or None, C_ptr or None, epilogue,
-                                  stream or None))
-    return int(lib().gemm_f16_ex(M, N, K, A_ptr or None, B_ptr or None, C_ptr or None, epilogue,
-                                 config, stream or None))
+        return int(lib().gemm_f16(M, N, K, A, B, C, epilogue, S))
+    return int(lib().gemm_f16_ex(M, N, K, A, B, C, epilogue, config, S))
 
 
-def gemm(a, b, epilogue: str = "none", out=None, config: int = CONFIG_AUTO, stream=None):
-    """C = epi(a @ b) for 2-D contiguous float16 CUDA (HIP) tensors a (M x K), b (K x N).
+def gemm(a, b, epilogue: str = "none", out=None, config: int = CONFIG_AUTO, stream=None,
+         trans_a: bool = False, trans_b: bool = False):
+    """C = epi(op(a) @ op(b)) for 2-D contiguous float16 GPU tensors.
 
-    Returns ``out`` (allocated as an M x N float16 tensor when not given).  The
-    kernel is enqueued on ``stream`` (default: torch's current stream) and the
-    call returns without synchronising.
+    a is M x K (or K x M with ``trans_a``), b is K x N (or N x K with
+    ``trans_b``).  Returns ``out`` (allocated as an M x N float16 tensor when
+    not given).  The kernel is enqueued on ``stream`` (default: torch's
+    current stream) and the call returns without synchronising.
     """
     import torch
 
@@ -135,10 +142,11 @@ def gemm(a, b, epilogue: str = "none", out=None, config: int = CONFIG_AUTO, stre
             raise ValueError(f"{name} must be on the GPU")
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous (row-major)")
-    M, K = a.shape
-    K2, N = b.shape
+    K, M = a.shape if trans_a else (a.shape[1], a.shape[0])
+    N, K2 = b.shape if trans_b else (b.shape[1], b.shape[0])
     if K != K2:
-        raise ValueError(f"inner dimensions differ: a is {tuple(a.shape)}, b is {tuple(b.shape)}")
+        raise ValueError(f"inner dimensions differ: a is {tuple(a.shape)} (trans_a={trans_a}), "
+                         f"b is {tuple(b.shape)} (trans_b={trans_b})")
     if a.device != b.device:
         raise ValueError("a and b are on different devices")
     if out is None:
@@ -150,7 +158,7 @@ def gemm(a, b, epilogue: str = "none", out=None, config: int = CONFIG_AUTO, stre
         stream = torch.cuda.current_stream(a.device)
     with torch.cuda.device(a.device):
         st = gemm_f16_raw(M, N, K, a.data_ptr(), b.data_ptr(), out.data_ptr(), _EPILOGUES[epilogue],
-                          stream.cuda_stream, config)
+                          stream.cuda_stream, config, trans_a, trans_b)
     if st != SUCCESS:
         raise GemmError(st, "gemm_f16")
     return out

@@ -13,18 +13,18 @@
 namespace gemm_f16_impl {
 
 const ConfigDesc kConfigs[kNumConfigs] = {
-    {"256x256x64_s2_direct", 256, 256, 64, 2, 4, true, 8},
-    {"256x128x64_s3_direct", 256, 128, 64, 3, 4, true, 8},
-    {"128x128x64_s3_direct", 128, 128, 64, 3, 4, true, 8},
-    {"128x128x32_s2_staged", 128, 128, 32, 2, 4, false, 1},
-    {"64x64x64_s2_staged", 64, 64, 64, 2, 4, false, 1},
-    {"256x256x32_s4_direct", 256, 256, 32, 4, 4, true, 8},
-    {"256x256x32_s5_direct", 256, 256, 32, 5, 4, true, 8},
-    {"256x256x64_s2_direct_w8n", 256, 256, 64, 2, 8, true, 8},
-    {"256x256x32_s5_direct_w8n", 256, 256, 32, 5, 8, true, 8},
-    {"256x256x64_s2_direct_w8m", 256, 256, 64, 2, 8, true, 8},
-    {"256x256x64_s2_staged_w8", 256, 256, 64, 2, 8, false, 4},
-    {"256x128x64_s2_staged", 256, 128, 64, 2, 4, false, 4},
+    {"256x256x64_s2_direct", 256, 256, 64, 2, 4, true, 8, false},
+    {"256x128x64_s3_direct", 256, 128, 64, 3, 4, true, 8, false},
+    {"128x128x64_s3_direct", 128, 128, 64, 3, 4, true, 8, true},
+    {"128x128x32_s2_staged", 128, 128, 32, 2, 4, false, 1, true},
+    {"64x64x64_s2_staged", 64, 64, 64, 2, 4, false, 1, true},
+    {"256x256x32_s4_direct", 256, 256, 32, 4, 4, true, 8, false},
+    {"256x256x32_s5_direct", 256, 256, 32, 5, 4, true, 8, false},
+    {"256x256x64_s2_direct_w8n", 256, 256, 64, 2, 8, true, 8, true},
+    {"256x256x32_s5_direct_w8n", 256, 256, 32, 5, 8, true, 8, false},
+    {"256x256x64_s2_direct_w8m", 256, 256, 64, 2, 8, true, 8, false},
+    {"256x256x64_s2_staged_w8", 256, 256, 64, 2, 8, false, 4, false},
+    {"256x128x64_s2_staged", 256, 128, 64, 2, 4, false, 4, false},
 };
 
 namespace {
@@ -96,14 +96,30 @@ double config_efficiency(int c)
     }
 }
 
-bool config_fits(int c, int va, int vb)
+bool config_fits(int c, int va, int vb, bool transposed)
 {
+    if (transposed && !kConfigs[c].transposed)
+        return false;
     return va >= kConfigs[c].min_vec && vb >= kConfigs[c].min_vec;
 }
 
-void fill_plan(int c, int64_t M, int64_t N, int64_t K, int va, int vb, int vc, gemm_f16_plan_t *p)
+// Vector width a configuration loads with, given the widest the pitch allows.
+int kernel_vec(const ConfigDesc &d, int v, bool transposed)
+{
+    if (d.direct)
+        return 8;
+    if (transposed)
+        return v >= 8 ? 8 : 1;              // transposed layouts: 16-byte vectors or single elements
+    if (d.min_vec >= 4)
+        return v >= 8 ? 8 : 4;              // wide register-staged tiles
+    return v;
+}
+
+void fill_plan(int c, int64_t M, int64_t N, int64_t K, int va, int vb, int vc, bool ta, bool tb,
+               gemm_f16_plan_t *p)
 {
     const ConfigDesc &d = kConfigs[c];
+    const bool tr = ta || tb;
     memset(p, 0, sizeof(*p));
     p->config = c;
     p->block_m = d.block_m;
@@ -112,9 +128,8 @@ void fill_plan(int c, int64_t M, int64_t N, int64_t K, int va, int vb, int vc, g
     p->stages = d.stages;
     p->threads = 64 * d.waves;
     p->direct_lds = d.direct ? 1 : 0;
-    // wide staged tiles load vectors of 8 or 4 elements only
-    p->vec_a = d.direct ? 8 : (d.min_vec >= 4 ? (va >= 8 ? 8 : 4) : va);
-    p->vec_b = d.direct ? 8 : (d.min_vec >= 4 ? (vb >= 8 ? 8 : 4) : vb);
+    p->vec_a = kernel_vec(d, va, tr);
+    p->vec_b = kernel_vec(d, vb, tr);
     p->vec_c = vc;
     p->tiles_m = ceil_div(M, d.block_m);
     p->tiles_n = ceil_div(N, d.block_n);
@@ -123,16 +138,18 @@ void fill_plan(int c, int64_t M, int64_t N, int64_t K, int va, int vb, int vc, g
     p->lds_bytes = gemm_f16_stage_bytes(d.block_m, d.block_n, d.block_k, d.stages);
     p->flops = 2.0 * (double)M * (double)N * (double)K;
     p->min_bytes = 2.0 * ((double)M * K + (double)K * N + (double)M * N);
+    p->trans_a = ta ? 1 : 0;
+    p->trans_b = tb ? 1 : 0;
 }
 
 // Pick the configuration with the lowest modelled time: full rounds of
 // workgroups over the 256 CUs times the tile's work at its efficiency.
-int choose_config(int64_t M, int64_t N, int va, int vb)
+int choose_config(int64_t M, int64_t N, int va, int vb, bool transposed)
 {
     int best = -1;
     double best_t = 0.0;
     for (int c = 0; c < kNumConfigs; ++c) {
-        if (!config_fits(c, va, vb) || config_efficiency(c) <= 0.0)
+        if (!config_fits(c, va, vb, transposed) || config_efficiency(c) <= 0.0)
             continue;
         const ConfigDesc &d = kConfigs[c];
         int64_t grid = ceil_div(M, d.block_m) * ceil_div(N, d.block_n);
@@ -146,17 +163,20 @@ int choose_config(int64_t M, int64_t N, int va, int vb)
     return best;
 }
 
-gemm_f16_status_t make_plan(int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *C,
-                            int config, gemm_f16_plan_t *plan)
+gemm_f16_status_t make_plan(int64_t M, int64_t N, int64_t K, const void *A, bool ta, const void *B, bool tb,
+                            const void *C, int config, gemm_f16_plan_t *plan)
 {
     if (config != GEMM_F16_CONFIG_AUTO && (config < 0 || config >= kNumConfigs))
         return GEMM_F16_ERROR_INVALID_VALUE;
-    const int va = vec_width(A, K), vb = vec_width(B, N);
+    // row pitches of the matrices as stored
+    const int64_t lda = ta ? M : K, ldb = tb ? K : N;
+    const int va = vec_width(A, lda), vb = vec_width(B, ldb);
     const int vc = (N % 8 == 0 && (uintptr_t)C % 16 == 0) ? 8 : (N % 4 == 0 && (uintptr_t)C % 8 == 0) ? 4 : 1;
-    int c = config == GEMM_F16_CONFIG_AUTO ? choose_config(M, N, va, vb) : config;
-    if (!config_fits(c, va, vb))
+    const bool tr = ta || tb;
+    int c = config == GEMM_F16_CONFIG_AUTO ? choose_config(M, N, va, vb, tr) : config;
+    if (c < 0 || !config_fits(c, va, vb, tr))
         return GEMM_F16_ERROR_INVALID_VALUE;
-    fill_plan(c, M, N, K, va, vb, vc, plan);
+    fill_plan(c, M, N, K, va, vb, vc, ta, tb, plan);
     if (plan->grid > 0x7fffffff)
         return GEMM_F16_ERROR_UNSUPPORTED_SIZE;
     return GEMM_F16_SUCCESS;
@@ -184,8 +204,8 @@ gemm_f16_status_t check_device()
     return g_dev_state[dev] == 1 ? GEMM_F16_SUCCESS : GEMM_F16_ERROR_UNSUPPORTED_DEVICE;
 }
 
-gemm_f16_status_t run(int64_t M, int64_t N, int64_t K, const void *A, const void *B, void *C, int epilogue,
-                      int config, void *stream)
+gemm_f16_status_t run(int64_t M, int64_t N, int64_t K, const void *A, bool ta, const void *B, bool tb, void *C,
+                      int epilogue, int config, void *stream)
 {
     gemm_f16_status_t st = validate(M, N, K, A, B, C, true);
     if (st != GEMM_F16_SUCCESS)
@@ -193,7 +213,7 @@ gemm_f16_status_t run(int64_t M, int64_t N, int64_t K, const void *A, const void
     if (epilogue != GEMM_F16_EPILOGUE_NONE && epilogue != GEMM_F16_EPILOGUE_RELU)
         return GEMM_F16_ERROR_INVALID_VALUE;
     gemm_f16_plan_t plan;
-    st = make_plan(M, N, K, A, B, C, config, &plan);
+    st = make_plan(M, N, K, A, ta, B, tb, C, config, &plan);
     if (st != GEMM_F16_SUCCESS)
         return st;
     if (M == 0 || N == 0)
@@ -213,7 +233,7 @@ gemm_f16_status_t run(int64_t M, int64_t N, int64_t K, const void *A, const void
     a.group_m = GEMM_F16_GROUP_M;
     a.relu = epilogue == GEMM_F16_EPILOGUE_RELU ? 1 : 0;
     a.vec_c = plan.vec_c;
-    hipError_t e = launch(plan.config, a, plan.vec_a, plan.vec_b, plan.grid, (hipStream_t)stream);
+    hipError_t e = launch(plan.config, a, plan.vec_a, plan.vec_b, ta, tb, plan.grid, (hipStream_t)stream);
     return e == hipSuccess ? GEMM_F16_SUCCESS : GEMM_F16_ERROR_LAUNCH_FAILED;
 }
 
@@ -227,24 +247,39 @@ extern "C" {
 gemm_f16_status_t gemm_f16(int64_t M, int64_t N, int64_t K, const void *A, const void *B, void *C,
                            int epilogue, void *stream)
 {
-    return run(M, N, K, A, B, C, epilogue, GEMM_F16_CONFIG_AUTO, stream);
+    return run(M, N, K, A, false, B, false, C, epilogue, GEMM_F16_CONFIG_AUTO, stream);
 }
 
 gemm_f16_status_t gemm_f16_ex(int64_t M, int64_t N, int64_t K, const void *A, const void *B, void *C,
                               int epilogue, int config, void *stream)
 {
-    return run(M, N, K, A, B, C, epilogue, config, stream);
+    return run(M, N, K, A, false, B, false, C, epilogue, config, stream);
+}
+
+gemm_f16_status_t gemm_f16_trans(int64_t M, int64_t N, int64_t K, const void *A, int trans_a, const void *B,
+                                 int trans_b, void *C, int epilogue, int config, void *stream)
+{
+    if ((trans_a != 0 && trans_a != 1) || (trans_b != 0 && trans_b != 1))
+        return GEMM_F16_ERROR_INVALID_VALUE;
+    return run(M, N, K, A, trans_a != 0, B, trans_b != 0, C, epilogue, config, stream);
 }
 
 gemm_f16_status_t gemm_f16_plan(int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *C,
                                 int config, gemm_f16_plan_t *plan)
 {
-    if (!plan)
+    return gemm_f16_plan_trans(M, N, K, A, 0, B, 0, C, config, plan);
+}
+
+gemm_f16_status_t gemm_f16_plan_trans(int64_t M, int64_t N, int64_t K, const void *A, int trans_a,
+                                      const void *B, int trans_b, const void *C, int config,
+                                      gemm_f16_plan_t *plan)
+{
+    if (!plan || (trans_a != 0 && trans_a != 1) || (trans_b != 0 && trans_b != 1))
         return GEMM_F16_ERROR_INVALID_VALUE;
     gemm_f16_status_t st = validate(M, N, K, A, B, C, false);
     if (st != GEMM_F16_SUCCESS)
         return st;
-    return make_plan(M, N, K, A, B, C, config, plan);
+    return make_plan(M, N, K, A, trans_a != 0, B, trans_b != 0, C, config, plan);
 }
 
 int gemm_f16_num_configs(void) { return kNumConfigs; }

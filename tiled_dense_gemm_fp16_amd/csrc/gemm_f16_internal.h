@@ -30,6 +30,7 @@ struct ConfigDesc {
     int waves;            // wave64s per workgroup (4: one per SIMD, 8: two)
     bool direct;          // operands move global -> LDS with buffer_load ... lds
     int min_vec;          // smallest vector width (elements) of A and B loads it accepts
+    bool transposed;      // also compiled for A given K x M and/or B given N x K
 };
 
 constexpr int kNumConfigs = 12;
@@ -37,8 +38,11 @@ extern const ConfigDesc kConfigs[kNumConfigs];
 
 // Launch configuration `config` with `grid` workgroups on `s`.
 // va / vb: elements per global load of A / B (8, 4, 2 or 1; direct configs
-// require 8).  Returns the launch status.
-hipError_t launch(int config, const KernelArgs &a, int va, int vb, int64_t grid, hipStream_t s);
+// require 8, transposed layouts of register-staged configs 8 or 1).
+// trans_a: A is stored K x M; trans_b: B is stored N x K.  Returns the
+// launch status.
+hipError_t launch(int config, const KernelArgs &a, int va, int vb, bool trans_a, bool trans_b, int64_t grid,
+                  hipStream_t s);
 
 } // namespace gemm_f16_impl
 

@@ -19,11 +19,13 @@
 //    is a 32(n) x 16(k) slice of B^T and its second a 16(k) x 32(m) slice of
 //    A^T, so every lane ends up holding four consecutive n of one output row
 //    and writes them with one 8-byte store.
-//  * A is staged in LDS as [m][k] (k contiguous) and read with ds_read_b128.
-//    B is staged as it lies in memory, [k][n] (n contiguous), and read with
-//    gfx950's transposing ds_read_b64_tr_b16, which hands each lane four k
-//    values of one column n.  Both LDS tiles are XOR-swizzled in 16-byte
-//    chunks (no padding) to spread the reads over the LDS banks.
+//  * Each operand is staged in LDS the way it lies in memory.  An operand
+//    whose rows run along k (A as M x K; B given transposed as N x K) gives
+//    its fragments with ds_read_b128; one whose rows run along m or n (B as
+//    K x N; A given transposed as K x M) with gfx950's transposing
+//    ds_read_b64_tr_b16, which hands each lane four k values of one column.
+//    LDS tiles are XOR-swizzled in 16-byte chunks (no padding) so that the
+//    reads spread over the LDS banks.
 //  * "direct" kernels move operands global -> LDS with 16-byte
 //    buffer_load ... lds (no registers, no LDS-write instructions); "staged"
 //    kernels load through registers with 16/8/4/2-byte vectors and serve
@@ -166,41 +168,7 @@ __device__ __forceinline__ void tile_coords(int wg, int grid, int tiles_m, int t
     tn = in_group / gm;
 }
 
-// ---- the kernel -------------------------------------------------------------
-template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool DIRECT, int VA, int VB>
-struct Tile {
-    static constexpr int kWaves = WM * WN;           // 4 (one per SIMD) or 8 (two per SIMD)
-    static constexpr int kThreads = 64 * kWaves;
-    static_assert(kWaves == 4 || kWaves == 8, "4 or 8 waves");
-    static constexpr int WTM = BM / WM;              // wave sub-tile rows (m)
-    static constexpr int WTN = BN / WN;              // wave sub-tile cols (n)
-    static constexpr int TM = WTM / 32;              // 32x32 MFMA blocks per wave along m
-    static constexpr int TN = WTN / 32;              // ... along n
-    static_assert(TM >= 1 && TN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
-    static_assert(BK % 16 == 0, "BK multiple of the MFMA depth");
-    static constexpr int CA = BK / 8;                // 16-byte chunks per A row in LDS
-    static constexpr int CB = BN / 8;                // 16-byte chunks per B row in LDS
-    static_assert(CB >= 4 && (CB & (CB - 1)) == 0, "B row chunks: power of two >= 4");
-    static_assert(CA >= 2, "A rows of at least 32 bytes");
-    static_assert((CA & (CA - 1)) == 0, "A row chunks: power of two");
-    static constexpr int A_STAGE = BM * BK;          // halves
-    static constexpr int B_STAGE = BK * BN;
-    static constexpr int LDS_BYTES = STAGES * (A_STAGE + B_STAGE) * 2;
-    static_assert(LDS_BYTES <= 163840, "LDS budget");
-    // direct loads: one wave instruction fills 1 KiB of LDS
-    static constexpr int A_DMA = A_STAGE * 2 / (kThreads * 16);   // per thread per k-tile
-    static constexpr int B_DMA = B_STAGE * 2 / (kThreads * 16);
-    static_assert(!DIRECT || (A_STAGE * 2 % (kThreads * 16) == 0 && B_STAGE * 2 % (kThreads * 16) == 0),
-                  "direct tiles must be whole 4 KiB block-wide loads");
-    static_assert(!DIRECT || (VA == 8 && VB == 8), "direct loads move 16-byte chunks");
-    // staged loads: vectors of VA / VB halves
-    static constexpr int A_VECS = A_STAGE / VA / kThreads;
-    static constexpr int B_VECS = B_STAGE / VB / kThreads;
-    static_assert(DIRECT || (A_STAGE % (VA * kThreads) == 0 && B_STAGE % (VB * kThreads) == 0),
-                  "staged tiles must split evenly over 256 threads");
-    static constexpr int LOADS_PER_TILE = DIRECT ? (A_DMA + B_DMA) : (A_VECS + B_VECS);
-};
-
+// ---- operands ----------------------------------------------------------------
 template <int V>
 struct VecT;
 template <>
@@ -239,15 +207,202 @@ __device__ __forceinline__ void lds_store(half_t *p, typename VecT<V>::type v)
     *reinterpret_cast<typename VecT<V>::type *>(p) = v;
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool DIRECT, int VA, int VB>
+// One operand of the product as a workgroup stages it: a BMN x BK slice per
+// K step (BMN = bM for A, bN for B).
+//
+// ROWS_K: the stored matrix's rows run along k -- A given as M x K, or B given
+// transposed as N x K.  The LDS tile is [BMN][BK] and an MFMA fragment (8 k
+// of one m or n per lane) is one 16-byte read.  The workgroup's BMN rows form
+// one buffer descriptor (rows past the matrix read as 0); columns past K are
+// masked, since they would read the next row.
+//
+// Otherwise the stored rows run along m or n -- A given transposed as K x M,
+// or B given as K x N.  The LDS tile is [BK][BMN] (as in memory) and a
+// fragment comes from two transposing reads: in each 16-lane group g (which
+// covers half g % 2 of the 32 m or n and k half g / 2) lane j supplies the
+// address of row 8 (g / 2) + j / 4 (+4 for the second read), columns
+// 16 (g % 2) + 4 (j % 4) .. +3, and lane j receives column 16 (g % 2) + j.
+// Each k slice is one buffer descriptor (rows past K read as 0); columns past
+// the matrix edge are not masked: they only reach output rows or columns
+// that are never stored.
+template <bool ROWS_K, int BMN, int BK, int THREADS, bool DIRECT, int V>
+struct Operand {
+    static constexpr int STAGE = BMN * BK;                   // halves per LDS stage
+    static constexpr int ROW = ROWS_K ? BK : BMN;            // halves per LDS tile row
+    static constexpr int CHUNKS = ROW / 8;                   // 16-byte chunks per row
+    static constexpr int WAVES = THREADS / 64;
+    static_assert(CHUNKS >= 2 && (CHUNKS & (CHUNKS - 1)) == 0, "rows of a power-of-two number of chunks");
+    // direct: one wave instruction fills 1 KiB of LDS, lane l at byte 16 l
+    static constexpr int DMA = STAGE * 2 / (THREADS * 16);   // loads per thread per stage
+    static_assert(!DIRECT || STAGE * 2 % (THREADS * 16) == 0, "whole block-wide 16-byte loads");
+    static_assert(!DIRECT || V == 8, "direct loads move 16-byte chunks");
+    static_assert(!DIRECT || ROW * 2 <= 1024, "a row fits in one wave's KiB");
+    static constexpr int ROWS_PER_KB = DIRECT ? 1024 / (ROW * 2) : 1;
+    // consecutive direct loads of a thread are ROW_STEP rows apart, a multiple
+    // of the swizzle period, so they share one column and one base offset
+    static constexpr int ROW_STEP = WAVES * ROWS_PER_KB;
+    static_assert(!DIRECT || ROW_STEP % (ROWS_K ? 16 : 4) == 0, "row step keeps the swizzle phase");
+    // staged: vectors of V halves through registers
+    static constexpr int VECS = STAGE / V / THREADS;
+    static_assert(DIRECT || STAGE % (V * THREADS) == 0, "staged tiles split evenly over the threads");
+    static constexpr int LOADS = DIRECT ? DMA : VECS;
+    static constexpr int VEC_DIV = DIRECT ? 1 : VECS;
+
+    __device__ __forceinline__ static int swz(int row)
+    {
+        if constexpr (ROWS_K)
+            return swz_a<CHUNKS>(row);
+        else
+            return swz_b<CHUNKS>(row);
+    }
+
+    const half_t *X;       // the stored matrix
+    int ld;                // its row pitch (elements)
+    int mn0;               // first m (A) or n (B) of the workgroup's tile
+    int K;
+    __amdgpu_buffer_rsrc_t panel;   // ROWS_K: the workgroup's BMN rows
+    uint32_t off0, step;   // direct: byte offset of the first chunk, distance between loads
+    int kcol0;             // direct, ROWS_K: k column of the thread's chunks
+    uint32_t offv[VEC_DIV];
+    int kcolv[VEC_DIV];
+    int ldsv[VEC_DIV];
+    typename VecT<V>::type reg[VEC_DIV];
+
+    __device__ __forceinline__ void init(const half_t *x, int ld_, int mn0_, int mn_total, int K_, int tid,
+                                         int wave, int lane)
+    {
+        X = x;
+        ld = ld_;
+        mn0 = mn0_;
+        K = K_;
+        if constexpr (ROWS_K) {
+            const int rows = min(BMN, mn_total - mn0);
+            panel = make_rsrc(X + (int64_t)mn0 * ld, (uint32_t)rows * (uint32_t)ld * 2u);
+        }
+        if constexpr (DIRECT) {
+            const int byte = wave * 1024 + lane * 16;
+            const int r = byte / (ROW * 2);
+            const int c = (((byte % (ROW * 2)) / 16) ^ swz(r)) * 8;
+            kcol0 = c;
+            off0 = ((uint32_t)r * (uint32_t)ld + (uint32_t)(ROWS_K ? c : mn0 + c)) * 2u;
+            step = (uint32_t)ROW_STEP * (uint32_t)ld * 2u;
+        } else {
+#pragma unroll
+            for (int i = 0; i < VECS; ++i) {
+                const int v = tid + THREADS * i;
+                const int r = v / (ROW / V);
+                const int c = (v % (ROW / V)) * V;
+                kcolv[i] = c;
+                offv[i] = ((uint32_t)r * (uint32_t)ld + (uint32_t)(ROWS_K ? c : mn0 + c)) * 2u;
+                ldsv[i] = r * ROW + (((c / 8) ^ swz(r)) * 8) + (c % 8);
+            }
+        }
+    }
+
+    // Start the loads of k slice kt: into LDS at dst (direct) or into the
+    // registers (staged).  kt past the last slice is allowed and reads zeros.
+    __device__ __forceinline__ void issue(int kt, half_t *dst, int wave)
+    {
+        const int k0 = kt * BK;
+        __amdgpu_buffer_rsrc_t rs;
+        uint32_t shift = 0;
+        if constexpr (ROWS_K) {
+            rs = panel;
+            shift = (uint32_t)k0 * 2u;
+        } else {
+            // uniform by construction; readfirstlane keeps the descriptor in SGPRs
+            const int rows = __builtin_amdgcn_readfirstlane(max(0, min(BK, K - k0)));
+            rs = make_rsrc(X + (int64_t)k0 * ld, (uint32_t)rows * (uint32_t)ld * 2u);
+        }
+        if constexpr (DIRECT) {
+            // ROWS_K: K % 8 == 0, so a chunk is wholly inside or wholly past the row end
+            const uint32_t mask = ROWS_K ? oob_unless(k0 + kcol0 < K) : 0u;
+#pragma unroll
+            for (int i = 0; i < DMA; ++i) {
+                const uint32_t off = (off0 + shift + (uint32_t)i * step) | mask;
+                LDS_AS void *d = (LDS_AS void *)(dst + (wave + WAVES * i) * 512);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d, 16, off, 0, 0, 0);
+            }
+        } else {
+            (void)dst;
+            (void)wave;
+#pragma unroll
+            for (int i = 0; i < VECS; ++i) {
+                // ROWS_K: K % V == 0, so a vector is wholly inside or wholly past the row end
+                const uint32_t mask = ROWS_K ? oob_unless(k0 + kcolv[i] < K) : 0u;
+                reg[i] = buf_load<V>(rs, (offv[i] + shift) | mask);
+            }
+        }
+    }
+
+    // staged: write the register-held slice into LDS at dst
+    __device__ __forceinline__ void store(half_t *dst)
+    {
+        if constexpr (!DIRECT) {
+#pragma unroll
+            for (int i = 0; i < VECS; ++i)
+                lds_store<V>(dst + ldsv[i], reg[i]);
+        } else {
+            (void)dst;
+        }
+    }
+
+    // MFMA fragment for the 32 m (or n) starting at mnb of k step ks: lane l
+    // gets 8 k values 16 ks + 8 (l / 32) .. +7 of m (or n) mnb + l % 32.
+    __device__ __forceinline__ half8 frag(const half_t *stage, int mnb, int ks, int lane) const
+    {
+        if constexpr (ROWS_K) {
+            const int r = mnb + (lane & 31);
+            const int c = 2 * ks + (lane >> 5);
+            return *reinterpret_cast<const half8 *>(stage + r * ROW + ((c ^ swz(r)) * 8));
+        } else {
+            const int g = lane >> 4, j = lane & 15;
+            const int r0 = 16 * ks + 8 * (g >> 1) + (j >> 2);
+            const int r1 = r0 + 4;
+            const int col = mnb + 16 * (g & 1) + 4 * (j & 3);
+            const half_t *p0 = stage + r0 * ROW + (((col >> 3) ^ swz(r0)) * 8) + (col & 7);
+            const half_t *p1 = stage + r1 * ROW + (((col >> 3) ^ swz(r1)) * 8) + (col & 7);
+            short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS short4v *)p0);
+            short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS short4v *)p1);
+            half4 lo_h = __builtin_bit_cast(half4, lo);
+            half4 hi_h = __builtin_bit_cast(half4, hi);
+            return half8{lo_h[0], lo_h[1], lo_h[2], lo_h[3], hi_h[0], hi_h[1], hi_h[2], hi_h[3]};
+        }
+    }
+};
+
+// ---- the kernel -------------------------------------------------------------
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool DIRECT, int VA, int VB, bool A_ROWS_K,
+          bool B_ROWS_K>
+struct Tile {
+    static constexpr int kWaves = WM * WN;           // 4 (one per SIMD) or 8 (two per SIMD)
+    static constexpr int kThreads = 64 * kWaves;
+    static_assert(kWaves == 4 || kWaves == 8, "4 or 8 waves");
+    static constexpr int WTM = BM / WM;              // wave sub-tile rows (m)
+    static constexpr int WTN = BN / WN;              // wave sub-tile cols (n)
+    static constexpr int TM = WTM / 32;              // 32x32 MFMA blocks per wave along m
+    static constexpr int TN = WTN / 32;              // ... along n
+    static_assert(TM >= 1 && TN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
+    static_assert(BK % 16 == 0, "BK multiple of the MFMA depth");
+    using OpA = Operand<A_ROWS_K, BM, BK, kThreads, DIRECT, VA>;
+    using OpB = Operand<B_ROWS_K, BN, BK, kThreads, DIRECT, VB>;
+    static constexpr int A_STAGE = OpA::STAGE;
+    static constexpr int B_STAGE = OpB::STAGE;
+    static constexpr int LDS_BYTES = STAGES * (A_STAGE + B_STAGE) * 2;
+    static_assert(LDS_BYTES <= 163840, "LDS budget");
+    static constexpr int LOADS_PER_TILE = OpA::LOADS + OpB::LOADS;
+};
+
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool DIRECT, int VA, int VB, bool A_ROWS_K,
+          bool B_ROWS_K>
 __global__ void __launch_bounds__(64 * WM * WN)
 __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4)))
 gemm_f16_kernel(KernelArgs args)
 {
-    using T = Tile<BM, BN, BK, WM, WN, STAGES, DIRECT, VA, VB>;
+    using T = Tile<BM, BN, BK, WM, WN, STAGES, DIRECT, VA, VB, A_ROWS_K, B_ROWS_K>;
     __shared__ __attribute__((aligned(1024))) half_t lds[T::LDS_BYTES / 2];
-    half_t *const As = lds;                                  // STAGES x [BM][BK]
-    half_t *const Bs = lds + STAGES * T::A_STAGE;            // STAGES x [BK][BN]
+    half_t *const As = lds;                                  // STAGES A stages
+    half_t *const Bs = lds + STAGES * T::A_STAGE;            // STAGES B stages
 
     const int M = args.M, N = args.N, K = args.K;
     int tm, tn;
@@ -260,135 +415,22 @@ gemm_f16_kernel(KernelArgs args)
     const int wm0 = (wave / WN) * T::WTM;                   // wave sub-tile origin in the tile
     const int wn0 = (wave % WN) * T::WTN;
 
-    // A panel: rows m0 .. m0+BM-1 (rows past M are outside the descriptor -> 0)
-    const int a_rows = min(BM, M - m0);
-    const half_t *a_base = args.A + (int64_t)m0 * K;
-    const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(a_base, (uint32_t)a_rows * (uint32_t)K * 2u);
-
     const int nk = (K + BK - 1) / BK;
 
-    // ---- per-thread load assignments (fixed over the K loop) ----
-    // A: element (r, c) of the tile is A[m0 + r][k0 + c]
-    // B: element (r, c) of the tile is B[k0 + r][n0 + c]
-    // Masking: A rows past M and B rows past K lie outside their descriptors
-    // and read as 0.  A columns past K would read the next row and are masked:
-    // they meet B rows past K, which are 0, but a non-finite value there would
-    // turn 0 into NaN.  B columns past N are not masked: they only feed
-    // output columns past N, which are never stored.
-    // Direct: instruction i of this wave fills LDS bytes [(wave + 4 i) KiB, +1 KiB)
-    // of the stage and lane l lands at byte 16 l of that KiB.  Consecutive
-    // instructions of a thread are a fixed number of rows apart (a multiple
-    // of the swizzle period), so one base offset plus a row stride covers all.
-    constexpr int A_ROWS_PER_KB = 512 / BK;
-    constexpr int B_ROWS_PER_KB = 512 / BN > 0 ? 512 / BN : 1;
-    static_assert(!DIRECT || (T::kWaves * A_ROWS_PER_KB) % 16 == 0, "A row step keeps the swizzle phase");
-    static_assert(!DIRECT || BN <= 512, "direct B rows fit in 1 KiB");
-    static_assert(!DIRECT || (T::kWaves * 1024 / (BN * 2)) % 4 == 0, "B row step keeps the swizzle phase");
-    uint32_t a_off0, b_off0;          // byte offset of this thread's first vector
-    int a_col0;                       // tile column (halves) of A vectors (direct: same for all)
-    int a_lds[DIRECT ? 1 : T::A_VECS];
-    int a_colv[DIRECT ? 1 : T::A_VECS];
-    int b_lds[DIRECT ? 1 : T::B_VECS];
-    uint32_t a_offv[DIRECT ? 1 : T::A_VECS];
-    uint32_t b_offv[DIRECT ? 1 : T::B_VECS];
+    // A is M x K (lda = K) or, given transposed, K x M (lda = M); B is K x N
+    // (ldb = N) or, given transposed, N x K (ldb = K).
+    typename T::OpA opa;
+    typename T::OpB opb;
+    opa.init(args.A, A_ROWS_K ? K : M, m0, M, K, tid, wave, lane);
+    opb.init(args.B, B_ROWS_K ? K : N, n0, N, K, tid, wave, lane);
 
-    if constexpr (DIRECT) {
-        {
-            int byte = wave * 1024 + lane * 16;
-            int r = byte / (BK * 2);
-            int pc = (byte % (BK * 2)) / 16;
-            int c = pc ^ swz_a<T::CA>(r);
-            a_col0 = c * 8;
-            a_off0 = ((uint32_t)r * (uint32_t)K + (uint32_t)(c * 8)) * 2u;
-        }
-        {
-            int byte = wave * 1024 + lane * 16;
-            int r = byte / (BN * 2);
-            int pc = (byte % (BN * 2)) / 16;
-            int c = pc ^ swz_b<T::CB>(r);
-            b_off0 = ((uint32_t)r * (uint32_t)N + (uint32_t)(n0 + c * 8)) * 2u;
-        }
-    } else {
-        a_col0 = 0;
-        a_off0 = b_off0 = 0;
-#pragma unroll
-        for (int i = 0; i < T::A_VECS; ++i) {
-            int v = tid + T::kThreads * i;
-            int r = v / (BK / VA);
-            int c = (v % (BK / VA)) * VA;                 // column in halves
-            a_colv[i] = c;
-            a_offv[i] = ((uint32_t)r * (uint32_t)K + (uint32_t)c) * 2u;
-            a_lds[i] = r * BK + (((c / 8) ^ swz_a<T::CA>(r)) * 8) + (c % 8);
-        }
-#pragma unroll
-        for (int i = 0; i < T::B_VECS; ++i) {
-            int v = tid + T::kThreads * i;
-            int r = v / (BN / VB);
-            int c = (v % (BN / VB)) * VB;
-            b_offv[i] = ((uint32_t)r * (uint32_t)N + (uint32_t)(n0 + c)) * 2u;
-            b_lds[i] = r * BN + (((c / 8) ^ swz_b<T::CB>(r)) * 8) + (c % 8);
-        }
-    }
-    // byte distance between consecutive direct loads of one thread
-    const uint32_t a_step = (uint32_t)(T::kWaves * A_ROWS_PER_KB) * (uint32_t)K * 2u;
-    const uint32_t b_step = (uint32_t)(T::kWaves * 1024 / (BN * 2)) * (uint32_t)N * 2u;
-    (void)B_ROWS_PER_KB;
-
-    // Issue the global loads of k-tile kt into LDS stage s (direct) or into registers (staged).
-    typename VecT<VA>::type a_reg[DIRECT ? 1 : T::A_VECS];
-    typename VecT<VB>::type b_reg[DIRECT ? 1 : T::B_VECS];
-
-    // A tile index kt >= nk is allowed: its rows are all past K, so every
-    // load reads zeros (the direct pipeline issues such loads unconditionally
-    // at its tail instead of branching around them).
     auto issue_loads = [&](int kt, half_t *dst_a, half_t *dst_b) {
-        const int k0 = kt * BK;
-        const uint32_t a_shift = (uint32_t)k0 * 2u;
-        // uniform by construction; readfirstlane keeps the descriptor in SGPRs
-        const int b_rows = __builtin_amdgcn_readfirstlane(max(0, min(BK, K - k0)));
-        const __amdgpu_buffer_rsrc_t b_rsrc =
-            make_rsrc(args.B + (int64_t)k0 * N, (uint32_t)b_rows * (uint32_t)N * 2u);
-        if constexpr (DIRECT) {
-            // K % 8 == 0: a chunk is wholly inside or wholly past the row end
-            const uint32_t a_mask = oob_unless(k0 + a_col0 < K);
-#pragma unroll
-            for (int i = 0; i < T::A_DMA; ++i) {
-                uint32_t off = (a_off0 + a_shift + (uint32_t)i * a_step) | a_mask;
-                LDS_AS void *dst = (LDS_AS void *)(dst_a + (wave + T::kWaves * i) * 512);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, dst, 16, off, 0, 0, 0);
-            }
-#pragma unroll
-            for (int i = 0; i < T::B_DMA; ++i) {
-                uint32_t off = b_off0 + (uint32_t)i * b_step;
-                LDS_AS void *dst = (LDS_AS void *)(dst_b + (wave + T::kWaves * i) * 512);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, dst, 16, off, 0, 0, 0);
-            }
-        } else {
-            (void)dst_a;
-            (void)dst_b;
-#pragma unroll
-            for (int i = 0; i < T::A_VECS; ++i) {
-                uint32_t off = (a_offv[i] + a_shift) | oob_unless(k0 + a_colv[i] < K);
-                a_reg[i] = buf_load<VA>(a_rsrc, off);
-            }
-#pragma unroll
-            for (int i = 0; i < T::B_VECS; ++i) {
-                b_reg[i] = buf_load<VB>(b_rsrc, b_offv[i]);
-            }
-        }
+        opa.issue(kt, dst_a, wave);
+        opb.issue(kt, dst_b, wave);
     };
     auto store_staged = [&](half_t *dst_a, half_t *dst_b) {
-        if constexpr (!DIRECT) {
-#pragma unroll
-            for (int i = 0; i < T::A_VECS; ++i)
-                lds_store<VA>(dst_a + a_lds[i], a_reg[i]);
-#pragma unroll
-            for (int i = 0; i < T::B_VECS; ++i)
-                lds_store<VB>(dst_b + b_lds[i], b_reg[i]);
-        } else {
-            (void)dst_a;
-            (void)dst_b;
-        }
+        opa.store(dst_a);
+        opb.store(dst_b);
     };
 
     float16v acc[T::TM][T::TN];
@@ -398,19 +440,6 @@ gemm_f16_kernel(KernelArgs args)
         for (int j = 0; j < T::TN; ++j)
             acc[i][j] = float16v{};
 
-    // Fragment addressing inside one stage (in halves).
-    // Second MFMA operand (A^T, 16 k x 32 m): lane l reads row m = l % 32 of
-    // the block, logical chunk 2 ks + l / 32 (8 consecutive k).
-    const int ya_row = lane & 31;
-    const int ya_chunk = lane >> 5;
-    // First MFMA operand (B^T, 32 n x 16 k) via two transposing reads: in its
-    // 16-lane group g (n half g % 2, k half g / 2) lane j supplies the address
-    // of row k = 8 (g / 2) + j / 4 (+4 for the second read), columns
-    // 16 (g % 2) + 4 (j % 4) .. +3; lane j then receives column 16 (g % 2) + j.
-    const int xg = lane >> 4, xj = lane & 15;
-    const int xb_row = 8 * (xg >> 1) + (xj >> 2);
-    const int xb_col = 16 * (xg & 1) + 4 * (xj & 3);
-
     // Fragments of one 16-deep k step: x = B^T slices (one per 32-column
     // block), y = A^T slices (one per 32-row block).
     struct Frags {
@@ -419,24 +448,11 @@ gemm_f16_kernel(KernelArgs args)
     };
     auto load_frags = [&](Frags &f, const half_t *as, const half_t *bs, int ks) {
 #pragma unroll
-        for (int i = 0; i < T::TM; ++i) {
-            int r = wm0 + 32 * i + ya_row;
-            int c = 2 * ks + ya_chunk;
-            f.y[i] = *reinterpret_cast<const half8 *>(as + r * BK + ((c ^ swz_a<T::CA>(r)) * 8));
-        }
+        for (int i = 0; i < T::TM; ++i)
+            f.y[i] = opa.frag(as, wm0 + 32 * i, ks, lane);
 #pragma unroll
-        for (int j = 0; j < T::TN; ++j) {
-            int n = wn0 + 32 * j + xb_col;
-            int r0 = 16 * ks + xb_row;
-            int r1 = r0 + 4;
-            const half_t *p0 = bs + r0 * BN + (((n >> 3) ^ swz_b<T::CB>(r0)) * 8) + (n & 7);
-            const half_t *p1 = bs + r1 * BN + (((n >> 3) ^ swz_b<T::CB>(r1)) * 8) + (n & 7);
-            short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS short4v *)p0);
-            short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS short4v *)p1);
-            half4 lo_h = __builtin_bit_cast(half4, lo);
-            half4 hi_h = __builtin_bit_cast(half4, hi);
-            f.x[j] = half8{lo_h[0], lo_h[1], lo_h[2], lo_h[3], hi_h[0], hi_h[1], hi_h[2], hi_h[3]};
-        }
+        for (int j = 0; j < T::TN; ++j)
+            f.x[j] = opb.frag(bs, wn0 + 32 * j, ks, lane);
     };
     auto mma = [&](const Frags &f) {
 #pragma unroll
@@ -502,7 +518,7 @@ gemm_f16_kernel(KernelArgs args)
         load_frags(f0, rd_a, rd_b, 0);
         if (pending)
             mma(f1);
-        interleave(DIRECT ? T::LOADS_PER_TILE : 0, DIRECT ? 0 : T::A_VECS + T::B_VECS);
+        interleave(DIRECT ? T::LOADS_PER_TILE : 0, DIRECT ? 0 : T::LOADS_PER_TILE);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int ks = 0; ks + 1 < NS; ks += 2) {
@@ -676,23 +692,24 @@ gemm_f16_kernel(KernelArgs args)
 
 // ---- launchers ----------------------------------------------------------------
 
-template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool DIRECT, int VA, int VB>
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool DIRECT, int VA, int VB, bool AR, bool BR>
 static hipError_t launch_one(const KernelArgs &a, int64_t grid, hipStream_t stream)
 {
-    hipLaunchKernelGGL((gemm_f16_kernel<BM, BN, BK, WM, WN, STAGES, DIRECT, VA, VB>), dim3((unsigned)grid),
-                       dim3(64 * WM * WN), 0, stream, a);
+    hipLaunchKernelGGL((gemm_f16_kernel<BM, BN, BK, WM, WN, STAGES, DIRECT, VA, VB, AR, BR>),
+                       dim3((unsigned)grid), dim3(64 * WM * WN), 0, stream, a);
     return hipGetLastError();
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int STAGES>
+// register-staged kernels for every vector width (8, 4, 2 or 1 elements)
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool AR, bool BR>
 static hipError_t launch_staged(const KernelArgs &a, int va, int vb, int64_t grid, hipStream_t s)
 {
-#define GEMM_F16_VB(VA_)                                                                   \
-    switch (vb) {                                                                          \
-    case 8: return launch_one<BM, BN, BK, WM, WN, STAGES, false, VA_, 8>(a, grid, s);      \
-    case 4: return launch_one<BM, BN, BK, WM, WN, STAGES, false, VA_, 4>(a, grid, s);      \
-    case 2: return launch_one<BM, BN, BK, WM, WN, STAGES, false, VA_, 2>(a, grid, s);      \
-    default: return launch_one<BM, BN, BK, WM, WN, STAGES, false, VA_, 1>(a, grid, s);     \
+#define GEMM_F16_VB(VA_)                                                                          \
+    switch (vb) {                                                                                 \
+    case 8: return launch_one<BM, BN, BK, WM, WN, STAGES, false, VA_, 8, AR, BR>(a, grid, s);     \
+    case 4: return launch_one<BM, BN, BK, WM, WN, STAGES, false, VA_, 4, AR, BR>(a, grid, s);     \
+    case 2: return launch_one<BM, BN, BK, WM, WN, STAGES, false, VA_, 2, AR, BR>(a, grid, s);     \
+    default: return launch_one<BM, BN, BK, WM, WN, STAGES, false, VA_, 1, AR, BR>(a, grid, s);    \
     }
     switch (va) {
     case 8: GEMM_F16_VB(8)
@@ -705,31 +722,67 @@ static hipError_t launch_staged(const KernelArgs &a, int va, int vb, int64_t gri
 
 // Wide register-staged tiles keep every vector width >= 4 (narrower vectors
 // would need more staging registers than a 256-wide tile leaves free).
-template <int BM, int BN, int BK, int WM, int WN, int STAGES>
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool AR, bool BR>
 static hipError_t launch_staged_wide(const KernelArgs &a, int va, int vb, int64_t grid, hipStream_t s)
 {
     if (va == 8)
-        return vb == 8 ? launch_one<BM, BN, BK, WM, WN, STAGES, false, 8, 8>(a, grid, s)
-                       : launch_one<BM, BN, BK, WM, WN, STAGES, false, 8, 4>(a, grid, s);
-    return vb == 8 ? launch_one<BM, BN, BK, WM, WN, STAGES, false, 4, 8>(a, grid, s)
-                   : launch_one<BM, BN, BK, WM, WN, STAGES, false, 4, 4>(a, grid, s);
+        return vb == 8 ? launch_one<BM, BN, BK, WM, WN, STAGES, false, 8, 8, AR, BR>(a, grid, s)
+                       : launch_one<BM, BN, BK, WM, WN, STAGES, false, 8, 4, AR, BR>(a, grid, s);
+    return vb == 8 ? launch_one<BM, BN, BK, WM, WN, STAGES, false, 4, 8, AR, BR>(a, grid, s)
+                   : launch_one<BM, BN, BK, WM, WN, STAGES, false, 4, 4, AR, BR>(a, grid, s);
 }
 
-hipError_t launch(int config, const KernelArgs &a, int va, int vb, int64_t grid, hipStream_t s)
+// Register-staged tiles for the transposed layouts: 16-byte vectors when the
+// pitch allows them, else single elements.
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool AR, bool BR>
+static hipError_t launch_staged_8or1(const KernelArgs &a, int va, int vb, int64_t grid, hipStream_t s)
+{
+    if (va == 8)
+        return vb == 8 ? launch_one<BM, BN, BK, WM, WN, STAGES, false, 8, 8, AR, BR>(a, grid, s)
+                       : launch_one<BM, BN, BK, WM, WN, STAGES, false, 8, 1, AR, BR>(a, grid, s);
+    return vb == 8 ? launch_one<BM, BN, BK, WM, WN, STAGES, false, 1, 8, AR, BR>(a, grid, s)
+                   : launch_one<BM, BN, BK, WM, WN, STAGES, false, 1, 1, AR, BR>(a, grid, s);
+}
+
+// Configurations of the transposed layouts (A given K x M and/or B given N x K).
+template <bool AR, bool BR>
+static hipError_t launch_transposed(int config, const KernelArgs &a, int va, int vb, int64_t grid,
+                                    hipStream_t s)
 {
     switch (config) {
-    case 0: return launch_one<256, 256, 64, 2, 2, 2, true, 8, 8>(a, grid, s);
-    case 1: return launch_one<256, 128, 64, 2, 2, 3, true, 8, 8>(a, grid, s);
-    case 2: return launch_one<128, 128, 64, 2, 2, 3, true, 8, 8>(a, grid, s);
-    case 3: return launch_staged<128, 128, 32, 2, 2, 2>(a, va, vb, grid, s);
-    case 4: return launch_staged<64, 64, 64, 2, 2, 2>(a, va, vb, grid, s);
-    case 5: return launch_one<256, 256, 32, 2, 2, 4, true, 8, 8>(a, grid, s);
-    case 6: return launch_one<256, 256, 32, 2, 2, 5, true, 8, 8>(a, grid, s);
-    case 7: return launch_one<256, 256, 64, 2, 4, 2, true, 8, 8>(a, grid, s);
-    case 8: return launch_one<256, 256, 32, 2, 4, 5, true, 8, 8>(a, grid, s);
-    case 9: return launch_one<256, 256, 64, 4, 2, 2, true, 8, 8>(a, grid, s);
-    case 10: return launch_staged_wide<256, 256, 64, 2, 4, 2>(a, va, vb, grid, s);
-    case 11: return launch_staged_wide<256, 128, 64, 2, 2, 2>(a, va, vb, grid, s);
+    case 2: return launch_one<128, 128, 64, 2, 2, 3, true, 8, 8, AR, BR>(a, grid, s);
+    case 3: return launch_staged_8or1<128, 128, 32, 2, 2, 2, AR, BR>(a, va, vb, grid, s);
+    case 4: return launch_staged_8or1<64, 64, 64, 2, 2, 2, AR, BR>(a, va, vb, grid, s);
+    case 7: return launch_one<256, 256, 64, 2, 4, 2, true, 8, 8, AR, BR>(a, grid, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch(int config, const KernelArgs &a, int va, int vb, bool trans_a, bool trans_b, int64_t grid,
+                  hipStream_t s)
+{
+    if (trans_a || trans_b) {
+        if (trans_a && trans_b)
+            return launch_transposed<false, true>(config, a, va, vb, grid, s);
+        if (trans_a)
+            return launch_transposed<false, false>(config, a, va, vb, grid, s);
+        return launch_transposed<true, true>(config, a, va, vb, grid, s);
+    }
+    // A as M x K, B as K x N: every configuration
+    constexpr bool AR = true, BR = false;
+    switch (config) {
+    case 0: return launch_one<256, 256, 64, 2, 2, 2, true, 8, 8, AR, BR>(a, grid, s);
+    case 1: return launch_one<256, 128, 64, 2, 2, 3, true, 8, 8, AR, BR>(a, grid, s);
+    case 2: return launch_one<128, 128, 64, 2, 2, 3, true, 8, 8, AR, BR>(a, grid, s);
+    case 3: return launch_staged<128, 128, 32, 2, 2, 2, AR, BR>(a, va, vb, grid, s);
+    case 4: return launch_staged<64, 64, 64, 2, 2, 2, AR, BR>(a, va, vb, grid, s);
+    case 5: return launch_one<256, 256, 32, 2, 2, 4, true, 8, 8, AR, BR>(a, grid, s);
+    case 6: return launch_one<256, 256, 32, 2, 2, 5, true, 8, 8, AR, BR>(a, grid, s);
+    case 7: return launch_one<256, 256, 64, 2, 4, 2, true, 8, 8, AR, BR>(a, grid, s);
+    case 8: return launch_one<256, 256, 32, 2, 4, 5, true, 8, 8, AR, BR>(a, grid, s);
+    case 9: return launch_one<256, 256, 64, 4, 2, 2, true, 8, 8, AR, BR>(a, grid, s);
+    case 10: return launch_staged_wide<256, 256, 64, 2, 4, 2, AR, BR>(a, va, vb, grid, s);
+    case 11: return launch_staged_wide<256, 128, 64, 2, 2, 2, AR, BR>(a, va, vb, grid, s);
     default: return hipErrorInvalidValue;
     }
 }
