@@ -25,13 +25,17 @@ extern "C" {
 #define GEMM_F16_PROBE_RANDOM_FIXED 1      /* random halves, one fragment set reused */
 #define GEMM_F16_PROBE_RANDOM_CHANGING 2   /* random halves, two fragment sets alternating,
                                               as the GEMM's k steps do */
+/* Added to a kind: the same work with v_mfma_f32_16x16x32_f16 (an 8 x 8 block
+ * of 16x16 tiles per wave) instead of 32x32x16. */
+#define GEMM_F16_PROBE_MFMA16 3
 
 /* Number of 8-half (16-byte) vectors the `operands` buffer must hold. */
 #define GEMM_F16_PROBE_OPERAND_VECTORS 1024
 
 /*
  * Enqueue the probe on `stream` (a hipStream_t, NULL = default stream).
- *   mode     : one of the GEMM_F16_PROBE_* kinds.
+ *   mode     : one of the GEMM_F16_PROBE_* kinds, plus GEMM_F16_PROBE_MFMA16
+ *              for the 16x16x32 instruction.
  *   iters    : loop trips; each trip issues 32 MFMAs per wave.
  *   blocks   : workgroups of 256 threads (use a multiple of the CU count).
  *   operands : device buffer of GEMM_F16_PROBE_OPERAND_VECTORS x 8 binary16

@@ -190,7 +190,7 @@ def stored(M, N, K, ta, tb, seed):
 
 
 @pytest.mark.parametrize("ta,tb", LAYOUTS)
-@pytest.mark.parametrize("shape", [(520, 392, 200), (256, 256, 64), (300, 264, 136), (64, 1040, 8)])
+@pytest.mark.parametrize("shape", [(520, 392, 200), (256, 256, 64), (300, 264, 136), (64, 1040, 8), (300, 268, 132)])
 def test_transposed_layouts_every_config(ta, tb, shape):
     M, N, K = shape
     a_st, b_st = stored(M, N, K, ta, tb, M + N + K)

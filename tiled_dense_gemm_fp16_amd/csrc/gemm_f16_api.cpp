@@ -23,7 +23,7 @@ const ConfigDesc kConfigs[kNumConfigs] = {
     {"256x256x64_s2_direct_w8n", 256, 256, 64, 2, 8, true, 8, true},
     {"256x256x32_s5_direct_w8n", 256, 256, 32, 5, 8, true, 8, false},
     {"256x256x64_s2_direct_w8m", 256, 256, 64, 2, 8, true, 8, false},
-    {"256x256x64_s2_staged_w8", 256, 256, 64, 2, 8, false, 4, false},
+    {"256x256x64_s2_staged_w8", 256, 256, 64, 2, 8, false, 4, true},
     {"256x128x64_s2_staged", 256, 128, 64, 2, 4, false, 4, false},
 };
 
@@ -108,10 +108,10 @@ int kernel_vec(const ConfigDesc &d, int v, bool transposed)
 {
     if (d.direct)
         return 8;
-    if (transposed)
-        return v >= 8 ? 8 : 1;              // transposed layouts: 16-byte vectors or single elements
     if (d.min_vec >= 4)
         return v >= 8 ? 8 : 4;              // wide register-staged tiles
+    if (transposed)
+        return v >= 8 ? 8 : 1;              // transposed layouts, narrow tiles: 16-byte vectors or elements
     return v;
 }
 

@@ -754,6 +754,7 @@ static hipError_t launch_transposed(int config, const KernelArgs &a, int va, int
     case 3: return launch_staged_8or1<128, 128, 32, 2, 2, 2, AR, BR>(a, va, vb, grid, s);
     case 4: return launch_staged_8or1<64, 64, 64, 2, 2, 2, AR, BR>(a, va, vb, grid, s);
     case 7: return launch_one<256, 256, 64, 2, 4, 2, true, 8, 8, AR, BR>(a, grid, s);
+    case 10: return launch_staged_wide<256, 256, 64, 2, 4, 2, AR, BR>(a, va, vb, grid, s);
     default: return hipErrorInvalidValue;
     }
 }

@@ -17,6 +17,7 @@ namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float float16v __attribute__((ext_vector_type(16)));
+typedef float float4v __attribute__((ext_vector_type(4)));
 
 template <int MODE>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -73,15 +74,100 @@ mfma_probe_kernel(const half8 *__restrict__ operands, float *__restrict__ out, i
     out[t] = sum;
 }
 
+// The same work with v_mfma_f32_16x16x32_f16: per wave an 8 x 8 block of
+// 16x16 accumulator tiles (the same 128 x 128 outputs), 8 + 8 fragments per
+// 32-deep k step, two fragment sets alternating.
+template <int MODE>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+mfma16_probe_kernel(const half8 *__restrict__ operands, float *__restrict__ out, int iters)
+{
+    const int t = blockIdx.x * blockDim.x + threadIdx.x;
+    const int lane = threadIdx.x & 63;
+    half8 x[2][8], y[2][8];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if (MODE == GEMM_F16_PROBE_CONSTANT) {
+                for (int e = 0; e < 8; ++e) {
+                    x[s][i][e] = (_Float16)(0.001f * lane);
+                    y[s][i][e] = (_Float16)(0.01f * e);
+                }
+            } else {
+                x[s][i] = operands[((s * 16 + i) * 64 + lane) % GEMM_F16_PROBE_OPERAND_VECTORS];
+                y[s][i] = operands[((s * 16 + 8 + i) * 64 + lane) % GEMM_F16_PROBE_OPERAND_VECTORS];
+            }
+        }
+    if (MODE == GEMM_F16_PROBE_RANDOM_FIXED) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            x[1][i] = x[0][i];
+            y[1][i] = y[0][i];
+        }
+    }
+    float4v acc[8][8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            acc[i][j] = float4v{};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(x[s][j], y[s][i], acc[i][j], 0, 0, 0);
+    }
+    float sum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                sum += acc[i][j][v];
+    out[t] = sum;
+}
+
 } // namespace
 
 extern "C" int gemm_f16_probe_mfma(int mode, int iters, int64_t blocks, const void *operands, void *out,
                                    void *stream, double *flops)
 {
-    if (iters < 0 || blocks <= 0 || blocks > 0x7fffffff || !out || (mode != GEMM_F16_PROBE_CONSTANT && !operands))
+    const int kind = mode % GEMM_F16_PROBE_MFMA16;
+    if (iters < 0 || blocks <= 0 || blocks > 0x7fffffff || !out || mode < 0 ||
+        mode >= 2 * GEMM_F16_PROBE_MFMA16 || (kind != GEMM_F16_PROBE_CONSTANT && !operands))
         return 1;
     hipStream_t s = (hipStream_t)stream;
     dim3 grid((unsigned)blocks), block(256);
+    const bool m16 = mode >= GEMM_F16_PROBE_MFMA16;
+    if (m16)
+        mode -= GEMM_F16_PROBE_MFMA16;
+    if (m16) {
+        switch (mode) {
+        case GEMM_F16_PROBE_CONSTANT:
+            hipLaunchKernelGGL(mfma16_probe_kernel<GEMM_F16_PROBE_CONSTANT>, grid, block, 0, s,
+                               (const half8 *)operands, (float *)out, iters);
+            break;
+        case GEMM_F16_PROBE_RANDOM_FIXED:
+            hipLaunchKernelGGL(mfma16_probe_kernel<GEMM_F16_PROBE_RANDOM_FIXED>, grid, block, 0, s,
+                               (const half8 *)operands, (float *)out, iters);
+            break;
+        case GEMM_F16_PROBE_RANDOM_CHANGING:
+            hipLaunchKernelGGL(mfma16_probe_kernel<GEMM_F16_PROBE_RANDOM_CHANGING>, grid, block, 0, s,
+                               (const half8 *)operands, (float *)out, iters);
+            break;
+        default:
+            return 1;
+        }
+        if (hipGetLastError() != hipSuccess)
+            return 2;
+        if (flops)
+            *flops = (double)blocks * 4.0 * (double)iters * 128.0 /* MFMAs */ * 16384.0;
+        return 0;
+    }
     switch (mode) {
     case GEMM_F16_PROBE_CONSTANT:
         hipLaunchKernelGGL(mfma_probe_kernel<GEMM_F16_PROBE_CONSTANT>, grid, block, 0, s, (const half8 *)operands,
