@@ -209,3 +209,36 @@ def test_python_wrapper_argument_checks():
         g.gemm(a, a)                                           # CPU tensors
     with pytest.raises(ValueError):
         g.gemm(a.float(), a)
+
+
+TUNED = os.path.join(ROOT, "tiled_dense_gemm_fp16_amd", "csrc", "gemm_f16_tuned.inc")
+
+
+def tuned_entries():
+    rows = []
+    for line in open(TUNED):
+        m = re.match(r"\{\s*(-?\d+(?:\s*,\s*-?\d+){6})\s*,\s*([\d.]+)\s*\},", line)
+        if m:
+            rows.append(tuple(int(x) for x in m.group(1).split(",")))
+    return rows
+
+
+def test_tuned_table_drives_the_automatic_choice():
+    """Every entry of the measured table names a configuration that accepts
+    its shape, and the planner picks it for exactly that shape."""
+    rows = tuned_entries()
+    assert rows, "the measured configuration table is empty"
+    seen = set()
+    for lm, ln, lk, ta, tb, aligned, cfg in rows:
+        assert 0 <= cfg < g.num_configs()
+        key = (lm, ln, lk, ta, tb, aligned)
+        assert key not in seen
+        seen.add(key)
+        pad = 0 if aligned else 4
+        M, N, K = (1 << lm) + pad, (1 << ln) + pad, (1 << lk) + pad
+        p = g.plan(M, N, K, FAKE, FAKE, FAKE, trans_a=bool(ta), trans_b=bool(tb))
+        assert p["config"] == cfg, (key, p["config"])
+        assert (p["vec_a"] == 8 and p["vec_b"] == 8) == bool(aligned)
+    # far from every swept shape the analytic model decides (no table hit)
+    p = g.plan(24, 24, 1 << 20, FAKE, FAKE, FAKE)
+    assert p["config"] == 4

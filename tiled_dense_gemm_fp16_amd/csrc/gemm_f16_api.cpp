@@ -5,6 +5,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <math.h>
+
 #include <mutex>
 
 #include "gemm_f16.h"
@@ -142,6 +144,43 @@ void fill_plan(int c, int64_t M, int64_t N, int64_t K, int va, int vb, int vc, b
     p->trans_b = tb ? 1 : 0;
 }
 
+// Measured table (tiled_dense_gemm_fp16_amd/tune.py): for swept shapes,
+// layouts and pitch alignments, the configuration that ran fastest.
+struct TunedEntry {
+    int lm, ln, lk;        // log2 of the swept M, N, K
+    int trans_a, trans_b;
+    int aligned;           // 1: pitches allowed 16-byte loads of both operands
+    int config;
+    double tflops;
+};
+const TunedEntry kTuned[] = {
+#include "gemm_f16_tuned.inc"
+    {-1, -1, -1, -1, -1, -1, -1, 0.0}   // end marker
+};
+
+// The tuned configuration for the nearest swept shape (in log2 M, N, K) with
+// the same layout and alignment, if one lies within a factor of two overall;
+// -1 otherwise.
+int tuned_config(int64_t M, int64_t N, int64_t K, bool ta, bool tb, bool aligned, int va, int vb)
+{
+    const double lm = log2((double)(M > 0 ? M : 1)), ln = log2((double)(N > 0 ? N : 1));
+    const double lk = log2((double)(K > 0 ? K : 1));
+    int best = -1;
+    double best_d = 1.0 + 1e-9;
+    for (const TunedEntry &e : kTuned) {
+        if (e.config < 0)
+            break;
+        if (e.trans_a != (int)ta || e.trans_b != (int)tb || e.aligned != (int)aligned)
+            continue;
+        const double d = sqrt((lm - e.lm) * (lm - e.lm) + (ln - e.ln) * (ln - e.ln) + (lk - e.lk) * (lk - e.lk));
+        if (d < best_d && e.config < kNumConfigs && config_fits(e.config, va, vb, ta || tb)) {
+            best = e.config;
+            best_d = d;
+        }
+    }
+    return best;
+}
+
 // Pick the configuration with the lowest modelled time: full rounds of
 // workgroups over the 256 CUs times the tile's work at its efficiency.
 int choose_config(int64_t M, int64_t N, int va, int vb, bool transposed)
@@ -173,7 +212,12 @@ gemm_f16_status_t make_plan(int64_t M, int64_t N, int64_t K, const void *A, bool
     const int va = vec_width(A, lda), vb = vec_width(B, ldb);
     const int vc = (N % 8 == 0 && (uintptr_t)C % 16 == 0) ? 8 : (N % 4 == 0 && (uintptr_t)C % 8 == 0) ? 4 : 1;
     const bool tr = ta || tb;
-    int c = config == GEMM_F16_CONFIG_AUTO ? choose_config(M, N, va, vb, tr) : config;
+    int c = config;
+    if (c == GEMM_F16_CONFIG_AUTO) {
+        c = tuned_config(M, N, K, ta, tb, va == 8 && vb == 8, va, vb);
+        if (c < 0)
+            c = choose_config(M, N, va, vb, tr);
+    }
     if (c < 0 || !config_fits(c, va, vb, tr))
         return GEMM_F16_ERROR_INVALID_VALUE;
     fill_plan(c, M, N, K, va, vb, vc, ta, tb, plan);

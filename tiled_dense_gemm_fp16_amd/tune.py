@@ -1,0 +1,154 @@
+"""Offline tuning sweep -> frozen configuration table.
+
+The pages recommend searching tile sizes and stage counts with the
+autotuner, freezing the result per machine and power limit, and re-running
+the search on new hardware ("TileLang：比 Triton 低一层的 tile 语言",
+section "工程上的几个注意点"; "5分钟上手TileLang：GPU内核开发指南", section
+"避坑与调参").  This script is that search for this library: on a GPU it
+times every configuration that accepts each shape of a grid (three sizes per
+dimension, four layouts, aligned and misaligned pitches) and writes
+``csrc/gemm_f16_tuned.inc``, a table the host planner consults before its
+analytic model.  Rebuild the library afterwards.
+
+    python -m tiled_dense_gemm_fp16_amd.tune [--quick] [--out PATH]
+"""
+from __future__ import annotations
+
+import argparse
+import datetime
+import json
+import math
+import os
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+OUT = os.path.join(HERE, "csrc", "gemm_f16_tuned.inc")
+
+SIZES_MN = [512, 2048, 8192]
+SIZES_K = [512, 2048, 8192]
+LAYOUTS = [(False, False), (False, True), (True, False), (True, True)]
+
+
+def _time(fn, flops, target_s=0.03):
+    """TFLOP/s of fn() (one GEMM launch on torch's current stream).
+
+    Launches are captured into a HIP graph of several calls and the graph is
+    replayed, so that small shapes are timed on the GPU rather than at the
+    rate Python can issue them."""
+    import torch
+
+    fn()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(4):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    one = max(s.elapsed_time(e) / 4, 1e-3)   # ms, an upper bound for small shapes
+    per_graph = max(1, min(64, int(2.0 / one)))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            for _ in range(per_graph):
+                fn()
+    torch.cuda.current_stream().wait_stream(side)
+    graph.replay()
+    torch.cuda.synchronize()
+    s.record()
+    graph.replay()
+    e.record()
+    torch.cuda.synchronize()
+    g_ms = max(s.elapsed_time(e), 1e-3)
+    reps = max(2, min(100, int(target_s * 1e3 / g_ms)))
+    s.record()
+    for _ in range(reps):
+        graph.replay()
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / (reps * per_graph)
+    del graph
+    return flops / (ms * 1e-3) / 1e12
+
+
+def sweep(sizes_mn, sizes_k, layouts, log):
+    import torch
+
+    import tiled_dense_gemm_fp16_amd as g
+
+    rows = []
+    for aligned in (True, False):
+        for M in sizes_mn:
+            for N in sizes_mn:
+                for K in sizes_k:
+                    # misaligned: every pitch odd by 4 elements (8-byte rows only)
+                    m, n, k = (M, N, K) if aligned else (M + 4, N + 4, K + 4)
+                    for ta, tb in layouts:
+                        a = torch.randn((k, m) if ta else (m, k), device="cuda").half()
+                        b = (torch.randn((n, k) if tb else (k, n), device="cuda") / math.sqrt(k)).half()
+                        c = torch.empty((m, n), device="cuda", dtype=torch.float16)
+                        best = None
+                        results = {}
+                        for cfg in range(g.num_configs()):
+                            try:
+                                g.plan(m, n, k, a.data_ptr(), b.data_ptr(), c.data_ptr(), config=cfg,
+                                       trans_a=ta, trans_b=tb)
+                            except g.GemmError:
+                                continue
+                            tf = _time(lambda: g.gemm(a, b, out=c, config=cfg, trans_a=ta, trans_b=tb),
+                                       2.0 * m * n * k)
+                            results[cfg] = round(tf, 1)
+                            if best is None or tf > results[best]:
+                                best = cfg
+                        rec = {"M": m, "N": n, "K": k, "trans_a": int(ta), "trans_b": int(tb),
+                               "aligned": int(aligned), "best": best, "tflops": results}
+                        rows.append(rec)
+                        print(json.dumps(rec), file=log, flush=True)
+                        del a, b, c
+    return rows
+
+
+def write_table(rows, path, note):
+    lines = [
+        "// gemm_f16_tuned.inc -- measured configuration table, written by",
+        "// tiled_dense_gemm_fp16_amd/tune.py; do not edit by hand.",
+        f"// {note}",
+        "// fields: log2 M, log2 N, log2 K (of the swept shape), trans_a, trans_b,",
+        "// pitches aligned to 16 bytes (1) or not (0), best configuration, its TFLOP/s",
+    ]
+    for r in rows:
+        if r["best"] is None:
+            continue
+        lm, ln, lk = (round(math.log2(r[x])) for x in ("M", "N", "K"))
+        lines.append(f"{{{lm}, {ln}, {lk}, {r['trans_a']}, {r['trans_b']}, {r['aligned']}, {r['best']}, "
+                     f"{r['tflops'][r['best']]:.1f}}},")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--quick", action="store_true", help="NN layout only")
+    ap.add_argument("--out", default=OUT)
+    ap.add_argument("--log", default=None, help="also write every measurement (JSON lines) here")
+    args = ap.parse_args()
+    import torch
+
+    if not torch.cuda.is_available():
+        print("tune.py needs a GPU", file=sys.stderr)
+        return 2
+    log = open(args.log, "w") if args.log else sys.stdout
+    layouts = LAYOUTS[:1] if args.quick else LAYOUTS
+    rows = sweep(SIZES_MN, SIZES_K, layouts, log)
+    dev = torch.cuda.get_device_properties(0)
+    note = (f"swept {datetime.date.today().isoformat()} on {dev.name} "
+            f"({getattr(dev, 'gcnArchName', '?')}, {dev.multi_processor_count} CUs)")
+    write_table(rows, args.out, note)
+    print(f"wrote {args.out} ({len(rows)} shapes)", flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
