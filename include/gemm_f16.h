@@ -23,14 +23,33 @@
  * N multiples of 8) selects the fastest kernels, other shapes run a slower
  * path that gives the same results (never an error).
  *
- * Ownership: all three buffers belong to the caller.  The library allocates
- * no device memory per call and keeps no per-call state; it is safe to call
- * from several host threads.
+ * Ownership: all three buffers belong to the caller.  The only device memory
+ * the library itself allocates is a split-K workspace (below), one buffer
+ * per device and stream, grown on demand and kept until
+ * gemm_f16_release_workspaces().  It is safe to call from several host
+ * threads.
+ *
+ * Split-K: when a problem has too few output tiles to fill the GPU's 256
+ * CUs, the K loop of each tile may be divided into `splits` ranges run by
+ * separate workgroups ("TileLang：比 Triton 低一层的 tile 语言", section
+ * "工程上的几个注意点", names persistent / stream-K scheduling as the remedy
+ * for grids smaller than the machine).  Each range writes fp32 partial sums
+ * to a workspace of splits x M x N fp32; a second kernel adds the partials
+ * in split order, applies the epilogue and rounds once to binary16.  The
+ * automatic choice (gemm_f16, and CONFIG_AUTO in gemm_f16_ex /
+ * gemm_f16_trans) may split and then uses the library's workspace for the
+ * stream; if that buffer would have to grow while the stream is being
+ * captured into a graph, or cannot be allocated, the call runs unsplit.  A
+ * graph that captured a split call holds that buffer's address: keep the
+ * graph's stream from needing a larger buffer, and do not call
+ * gemm_f16_release_workspaces(), while the graph may still be launched.
  *
  * Execution: asynchronous on the given HIP stream (a hipStream_t passed as
- * void*; NULL is the default stream).  No host synchronisation.  The result
- * is deterministic: no atomics, so it is bitwise reproducible run to run for
- * a given shape and kernel configuration.
+ * void*; NULL is the default stream).  No host synchronisation, except that
+ * growing the library's workspace waits for the stream's earlier work.  The
+ * result is deterministic: no atomics, and split partials are added in a
+ * fixed order, so it is bitwise reproducible run to run for a given shape,
+ * kernel configuration and split count.
  *
  * Errors: arguments are validated before any HIP call; on error nothing is
  * launched and C is untouched.  A launch error is reported as
@@ -52,7 +71,8 @@ typedef enum gemm_f16_status {
     /* negative dimension, null pointer with a nonzero extent, unknown
      * epilogue or configuration, C overlapping A or B */
     GEMM_F16_ERROR_INVALID_VALUE = 1,
-    /* a pointer that is not 2-byte aligned */
+    /* a pointer that is not 2-byte aligned (a caller's split-K workspace:
+     * not 16-byte aligned) */
     GEMM_F16_ERROR_MISALIGNED = 2,
     /* no HIP device is visible */
     GEMM_F16_ERROR_NO_DEVICE = 3,
@@ -61,7 +81,13 @@ typedef enum gemm_f16_status {
     /* the kernel launch itself failed */
     GEMM_F16_ERROR_LAUNCH_FAILED = 5,
     /* a dimension beyond the library's limits (see GEMM_F16_MAX_*) */
-    GEMM_F16_ERROR_UNSUPPORTED_SIZE = 6
+    GEMM_F16_ERROR_UNSUPPORTED_SIZE = 6,
+    /* gemm_f16_split: the caller's workspace is smaller than the plan's
+     * workspace_bytes, or the library's could not be allocated (or would
+     * have to grow during graph capture) */
+    GEMM_F16_ERROR_WORKSPACE = 7,
+    /* a HIP runtime call other than a launch failed (workspace management) */
+    GEMM_F16_ERROR_RUNTIME = 8
 } gemm_f16_status_t;
 
 typedef enum gemm_f16_epilogue {
@@ -78,6 +104,11 @@ typedef enum gemm_f16_epilogue {
 
 /* Automatic kernel choice for gemm_f16_ex / gemm_f16_plan. */
 #define GEMM_F16_CONFIG_AUTO (-1)
+
+/* Automatic split count for gemm_f16_split / gemm_f16_plan_split, and the
+ * largest count accepted. */
+#define GEMM_F16_SPLITS_AUTO 0
+#define GEMM_F16_MAX_SPLITS 64
 
 /*
  * C = epi(A . B) for A (M x K), B (K x N), C (M x N), all binary16 row-major.
@@ -98,7 +129,8 @@ gemm_f16_status_t gemm_f16(int64_t M, int64_t N, int64_t K,
  * As gemm_f16, with an explicit kernel configuration: an index in
  * [0, gemm_f16_num_configs()) or GEMM_F16_CONFIG_AUTO.  A configuration that
  * cannot run this shape or alignment (gemm_f16_plan says why) returns
- * GEMM_F16_ERROR_INVALID_VALUE.  Intended for tests and tuning sweeps; every
+ * GEMM_F16_ERROR_INVALID_VALUE.  An explicit configuration runs unsplit (one
+ * kernel, no workspace).  Intended for tests and tuning sweeps; every
  * configuration computes the same function.
  */
 gemm_f16_status_t gemm_f16_ex(int64_t M, int64_t N, int64_t K,
@@ -122,6 +154,39 @@ gemm_f16_status_t gemm_f16_trans(int64_t M, int64_t N, int64_t K,
                                  const void *A, int trans_a, const void *B, int trans_b,
                                  void *C, int epilogue, int config, void *stream);
 
+/*
+ * C = epi(op(A) . op(B)) with an explicit K split (layouts as
+ * gemm_f16_trans).
+ *   config          : a configuration index or GEMM_F16_CONFIG_AUTO.
+ *   splits          : GEMM_F16_SPLITS_AUTO, or 1 .. GEMM_F16_MAX_SPLITS.  The
+ *                     count is rounded down so that no split is empty and
+ *                     every split spans whole K tiles (gemm_f16_plan_split
+ *                     reports the count used; 1 means one kernel and no
+ *                     workspace).
+ *   workspace       : NULL for the library's buffer for this device and
+ *                     stream, or a caller-owned device buffer of
+ *                     workspace_bytes bytes, 16-byte aligned, overlapping
+ *                     none of A, B, C, and at least the plan's
+ *                     workspace_bytes long (else GEMM_F16_ERROR_WORKSPACE).
+ *                     Its contents are scratch; calls that share one buffer
+ *                     must be ordered (one stream).
+ *   workspace_bytes : size of the caller's buffer; 0 when workspace is NULL.
+ * Unlike the automatic path this never falls back to an unsplit run: a
+ * library workspace that cannot be obtained returns
+ * GEMM_F16_ERROR_WORKSPACE.  Other arguments and errors as gemm_f16_trans.
+ */
+gemm_f16_status_t gemm_f16_split(int64_t M, int64_t N, int64_t K,
+                                 const void *A, int trans_a, const void *B, int trans_b,
+                                 void *C, int epilogue, int config, int splits,
+                                 void *workspace, int64_t workspace_bytes, void *stream);
+
+/*
+ * Free the library's split-K workspaces on every device (waiting for each
+ * device's work first).  Later calls allocate again when they need to.
+ * Returns GEMM_F16_ERROR_RUNTIME if a HIP call failed.
+ */
+gemm_f16_status_t gemm_f16_release_workspaces(void);
+
 /* How a call would run; filled by gemm_f16_plan without any HIP call. */
 typedef struct gemm_f16_plan {
     int32_t config;        /* configuration index actually chosen */
@@ -136,13 +201,16 @@ typedef struct gemm_f16_plan {
     int32_t vec_c;         /* binary16 elements per store of C */
     int64_t tiles_m;       /* ceil(M / bM) */
     int64_t tiles_n;       /* ceil(N / bN) */
-    int64_t grid;          /* workgroups launched (tiles_m * tiles_n) */
-    int64_t k_tiles;       /* K-loop trip count ceil(K / bK) */
+    int64_t grid;          /* workgroups launched (tiles_m * tiles_n * splits) */
+    int64_t k_tiles;       /* K-loop trip count of one workgroup: ceil(k_split / bK) */
     int64_t lds_bytes;     /* LDS per workgroup */
     double flops;          /* 2 M N K: the algorithmic work of the call */
     double min_bytes;      /* 2 (M K + K N + M N): operands read once, C written once */
     int32_t trans_a;       /* 1: A stored K x M */
     int32_t trans_b;       /* 1: B stored N x K */
+    int32_t splits;        /* K splits (1: unsplit, no reduction kernel) */
+    int64_t k_split;       /* K elements per split (K when unsplit) */
+    int64_t workspace_bytes; /* splits * M * N * 4 when split, else 0 */
 } gemm_f16_plan_t;
 
 /*
@@ -159,6 +227,11 @@ gemm_f16_status_t gemm_f16_plan(int64_t M, int64_t N, int64_t K,
 gemm_f16_status_t gemm_f16_plan_trans(int64_t M, int64_t N, int64_t K,
                                       const void *A, int trans_a, const void *B, int trans_b,
                                       const void *C, int config, gemm_f16_plan_t *plan);
+
+/* As gemm_f16_plan_trans, for gemm_f16_split with the given split request. */
+gemm_f16_status_t gemm_f16_plan_split(int64_t M, int64_t N, int64_t K,
+                                      const void *A, int trans_a, const void *B, int trans_b,
+                                      const void *C, int config, int splits, gemm_f16_plan_t *plan);
 
 /* Number of kernel configurations compiled into the library. */
 int gemm_f16_num_configs(void);

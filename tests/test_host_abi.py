@@ -217,7 +217,7 @@ TUNED = os.path.join(ROOT, "tiled_dense_gemm_fp16_amd", "csrc", "gemm_f16_tuned.
 def tuned_entries():
     rows = []
     for line in open(TUNED):
-        m = re.match(r"\{\s*(-?\d+(?:\s*,\s*-?\d+){6})\s*,\s*([\d.]+)\s*\},", line)
+        m = re.match(r"\{\s*(-?\d+(?:\s*,\s*-?\d+){7})\s*,\s*([\d.]+)\s*\},", line)
         if m:
             rows.append(tuple(int(x) for x in m.group(1).split(",")))
     return rows
@@ -225,12 +225,13 @@ def tuned_entries():
 
 def test_tuned_table_drives_the_automatic_choice():
     """Every entry of the measured table names a configuration that accepts
-    its shape, and the planner picks it for exactly that shape."""
+    its shape, and the planner picks it (and its split count) for exactly
+    that shape."""
     rows = tuned_entries()
     assert rows, "the measured configuration table is empty"
     seen = set()
-    for lm, ln, lk, ta, tb, aligned, cfg in rows:
-        assert 0 <= cfg < g.num_configs()
+    for lm, ln, lk, ta, tb, aligned, cfg, splits in rows:
+        assert 0 <= cfg < g.num_configs() and 1 <= splits <= g.MAX_SPLITS
         key = (lm, ln, lk, ta, tb, aligned)
         assert key not in seen
         seen.add(key)
@@ -238,7 +239,58 @@ def test_tuned_table_drives_the_automatic_choice():
         M, N, K = (1 << lm) + pad, (1 << ln) + pad, (1 << lk) + pad
         p = g.plan(M, N, K, FAKE, FAKE, FAKE, trans_a=bool(ta), trans_b=bool(tb))
         assert p["config"] == cfg, (key, p["config"])
+        want = g.plan(M, N, K, FAKE, FAKE, FAKE, config=cfg, trans_a=bool(ta), trans_b=bool(tb), splits=splits)
+        assert p["splits"] == want["splits"] and p["k_split"] == want["k_split"], key
         assert (p["vec_a"] == 8 and p["vec_b"] == 8) == bool(aligned)
-    # far from every swept shape the analytic model decides (no table hit)
+    # far from every swept shape the analytic model decides (no table hit):
+    # a deep K under a one-tile output is split
     p = g.plan(24, 24, 1 << 20, FAKE, FAKE, FAKE)
-    assert p["config"] == 4
+    assert p["splits"] > 1 and p["workspace_bytes"] == p["splits"] * 24 * 24 * 4
+
+
+# ---- split-K planning and workspace validation (host logic only) ----
+
+def test_split_geometry():
+    # 128x128x64 tiles, K = 1000: 16 k tiles
+    base = dict(config=2, splits=1)
+    p = g.plan(256, 256, 1000, FAKE, FAKE, FAKE, **base)
+    assert (p["splits"], p["k_split"], p["workspace_bytes"], p["grid"]) == (1, 1000, 0, 4)
+    for req, splits, k_split in [(2, 2, 512), (3, 3, 384), (5, 4, 256), (16, 16, 64), (64, 16, 64)]:
+        p = g.plan(256, 256, 1000, FAKE, FAKE, FAKE, config=2, splits=req)
+        assert (p["splits"], p["k_split"]) == (splits, k_split), req
+        assert p["grid"] == 4 * splits and p["k_tiles"] == k_split // 64
+        assert p["workspace_bytes"] == splits * 256 * 256 * 4
+        # no split is empty and the splits cover K exactly
+        assert (splits - 1) * k_split < 1000 <= splits * k_split
+    # one k tile (or none) cannot be split
+    assert g.plan(256, 256, 64, FAKE, FAKE, FAKE, config=2, splits=4)["splits"] == 1
+    assert g.plan(256, 256, 0, FAKE, FAKE, FAKE, config=2, splits=4)["splits"] == 1
+    # the explicit-config entry points never split
+    assert g.plan(64, 64, 1 << 20, FAKE, FAKE, FAKE, config=4)["splits"] == 1
+    # split counts outside [0, 64] are rejected
+    for bad in (-1, g.MAX_SPLITS + 1):
+        with pytest.raises(g.GemmError):
+            g.plan(256, 256, 1000, FAKE, FAKE, FAKE, config=2, splits=bad)
+    # a workgroup's workspace slice must stay addressable: 256 rows x N fp32 < 2 GiB
+    with pytest.raises(g.GemmError) as e:
+        g.plan(256, 1 << 21, 1024, FAKE, FAKE, FAKE, config=0, splits=2)
+    assert e.value.status == 6
+    assert g.plan(64, 1 << 21, 1024, FAKE, FAKE, FAKE, config=4, splits=2)["splits"] == 2
+
+
+def _split_call(ws, ws_bytes, C=FAKE * 2, splits=4):
+    return g.lib().gemm_f16_split(256, 256, 1000, FAKE, 0, FAKE * 3, 0, C, 0, 2, splits, ws, ws_bytes, None)
+
+
+def test_split_workspace_validation_before_any_launch():
+    need = 4 * 256 * 256 * 4
+    WS = FAKE * 8
+    assert _split_call(WS, need - 1) == 7                     # too small
+    assert _split_call(WS + 8, need) == 2                     # not 16-byte aligned
+    assert _split_call(FAKE * 2 - 16, need) == 1              # overlaps C
+    assert _split_call(FAKE, need) == 1                       # overlaps A
+    assert _split_call(None, 16) == 1                         # size without a buffer
+    assert _split_call(WS, -1) == 1                           # negative size
+    assert _split_call(WS, need, splits=65) == 1              # split count beyond the maximum
+    # (valid arguments are not tried here: on a GPU host they would launch
+    # on these stand-in addresses)

@@ -22,6 +22,8 @@ SUCCESS = 0
 EPILOGUE_NONE = 0
 EPILOGUE_RELU = 1
 CONFIG_AUTO = -1
+SPLITS_AUTO = 0
+MAX_SPLITS = 64
 _EPILOGUES = {"none": EPILOGUE_NONE, "relu": EPILOGUE_RELU}
 
 # exported symbols and their ctypes signatures (mirrors include/gemm_f16.h)
@@ -38,6 +40,7 @@ class Plan(ctypes.Structure):
         ("grid", ctypes.c_int64), ("k_tiles", ctypes.c_int64), ("lds_bytes", ctypes.c_int64),
         ("flops", ctypes.c_double), ("min_bytes", ctypes.c_double),
         ("trans_a", ctypes.c_int32), ("trans_b", ctypes.c_int32),
+        ("splits", ctypes.c_int32), ("k_split", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64),
     ]
 
     def as_dict(self) -> dict:
@@ -49,7 +52,11 @@ SIGNATURES = {
     "gemm_f16_ex": ([_i64, _i64, _i64, _vp, _vp, _vp, _int, _int, _vp], _int),
     "gemm_f16_trans": ([_i64, _i64, _i64, _vp, _int, _vp, _int, _vp, _int, _int, _vp], _int),
     "gemm_f16_plan": ([_i64, _i64, _i64, _vp, _vp, _vp, _int, ctypes.POINTER(Plan)], _int),
+    "gemm_f16_split": ([_i64, _i64, _i64, _vp, _int, _vp, _int, _vp, _int, _int, _int, _vp, _i64, _vp], _int),
+    "gemm_f16_release_workspaces": ([], _int),
     "gemm_f16_plan_trans": ([_i64, _i64, _i64, _vp, _int, _vp, _int, _vp, _int, ctypes.POINTER(Plan)], _int),
+    "gemm_f16_plan_split": ([_i64, _i64, _i64, _vp, _int, _vp, _int, _vp, _int, _int, ctypes.POINTER(Plan)],
+                            _int),
     "gemm_f16_num_configs": ([], _int),
     "gemm_f16_config_name": ([_int], ctypes.c_char_p),
     "gemm_f16_stage_bytes": ([_i64, _i64, _i64, _i64], _i64),
@@ -99,12 +106,19 @@ def stage_bytes(block_m: int, block_n: int, block_k: int, stages: int) -> int:
 
 
 def plan(M: int, N: int, K: int, A_ptr: int = 0, B_ptr: int = 0, C_ptr: int = 0,
-         config: int = CONFIG_AUTO, trans_a: bool = False, trans_b: bool = False) -> dict:
-    """How gemm_f16 would run this shape (pure host logic, no GPU needed).
-    Pointers only matter for alignment; 0 stands for an aligned buffer."""
+         config: int = CONFIG_AUTO, trans_a: bool = False, trans_b: bool = False,
+         splits: int | None = None) -> dict:
+    """How a call would run this shape (pure host logic, no GPU needed):
+    gemm_f16 / gemm_f16_trans when ``splits`` is None, else gemm_f16_split
+    with that request.  Pointers only matter for alignment; 0 stands for an
+    aligned buffer."""
     p = Plan()
-    st = lib().gemm_f16_plan_trans(M, N, K, A_ptr or None, int(trans_a), B_ptr or None, int(trans_b),
-                                   C_ptr or None, config, ctypes.byref(p))
+    if splits is None:
+        st = lib().gemm_f16_plan_trans(M, N, K, A_ptr or None, int(trans_a), B_ptr or None, int(trans_b),
+                                       C_ptr or None, config, ctypes.byref(p))
+    else:
+        st = lib().gemm_f16_plan_split(M, N, K, A_ptr or None, int(trans_a), B_ptr or None, int(trans_b),
+                                       C_ptr or None, config, int(splits), ctypes.byref(p))
     if st != SUCCESS:
         raise GemmError(st, "gemm_f16_plan")
     return p.as_dict()
@@ -122,14 +136,25 @@ def gemm_f16_raw(M: int, N: int, K: int, A_ptr: int, B_ptr: int, C_ptr: int, epi
     return int(lib().gemm_f16_ex(M, N, K, A, B, C, epilogue, config, S))
 
 
+def release_workspaces() -> None:
+    """Free the library's split-K workspaces (gemm_f16_release_workspaces)."""
+    st = lib().gemm_f16_release_workspaces()
+    if st != SUCCESS:
+        raise GemmError(st, "gemm_f16_release_workspaces")
+
+
 def gemm(a, b, epilogue: str = "none", out=None, config: int = CONFIG_AUTO, stream=None,
-         trans_a: bool = False, trans_b: bool = False):
+         trans_a: bool = False, trans_b: bool = False, splits: int | None = None, workspace=None):
     """C = epi(op(a) @ op(b)) for 2-D contiguous float16 GPU tensors.
 
     a is M x K (or K x M with ``trans_a``), b is K x N (or N x K with
     ``trans_b``).  Returns ``out`` (allocated as an M x N float16 tensor when
     not given).  The kernel is enqueued on ``stream`` (default: torch's
     current stream) and the call returns without synchronising.
+
+    ``splits`` (None: the automatic choice of gemm_f16 / gemm_f16_trans, or
+    SPLITS_AUTO / a count) and ``workspace`` (None: the library's buffer, or
+    a contiguous GPU tensor used as scratch) go to gemm_f16_split.
     """
     import torch
 
@@ -154,11 +179,24 @@ def gemm(a, b, epilogue: str = "none", out=None, config: int = CONFIG_AUTO, stre
     elif (out.dtype != torch.float16 or tuple(out.shape) != (M, N) or not out.is_contiguous()
           or out.device != a.device):
         raise ValueError(f"out must be a contiguous float16 tensor of shape {(M, N)} on {a.device}")
+    if workspace is not None:
+        if not isinstance(workspace, torch.Tensor) or not workspace.is_cuda or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous GPU tensor")
+        if workspace.device != a.device:
+            raise ValueError("workspace is on another device")
     if stream is None:
         stream = torch.cuda.current_stream(a.device)
     with torch.cuda.device(a.device):
-        st = gemm_f16_raw(M, N, K, a.data_ptr(), b.data_ptr(), out.data_ptr(), _EPILOGUES[epilogue],
-                          stream.cuda_stream, config, trans_a, trans_b)
+        if splits is None and workspace is None:
+            st = gemm_f16_raw(M, N, K, a.data_ptr(), b.data_ptr(), out.data_ptr(), _EPILOGUES[epilogue],
+                              stream.cuda_stream, config, trans_a, trans_b)
+        else:
+            ws_ptr = workspace.data_ptr() if workspace is not None else None
+            ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+            st = lib().gemm_f16_split(M, N, K, a.data_ptr() or None, int(trans_a), b.data_ptr() or None,
+                                      int(trans_b), out.data_ptr() or None, _EPILOGUES[epilogue], config,
+                                      SPLITS_AUTO if splits is None else int(splits), ws_ptr or None,
+                                      ws_bytes, stream.cuda_stream or None)
     if st != SUCCESS:
         raise GemmError(st, "gemm_f16")
     return out

@@ -7,26 +7,30 @@
 
 #include <math.h>
 
+#include <algorithm>
 #include <mutex>
+#include <vector>
 
 #include "gemm_f16.h"
 #include "gemm_f16_internal.h"
 
 namespace gemm_f16_impl {
 
+// occupancy: workgroups per CU as limited by LDS (160 KiB) and by registers
+// (512 per lane per SIMD, VGPRs + AGPRs as the compiler reports them).
 const ConfigDesc kConfigs[kNumConfigs] = {
-    {"256x256x64_s2_direct", 256, 256, 64, 2, 4, true, 8, false},
-    {"256x128x64_s3_direct", 256, 128, 64, 3, 4, true, 8, false},
-    {"128x128x64_s3_direct", 128, 128, 64, 3, 4, true, 8, true},
-    {"128x128x32_s2_staged", 128, 128, 32, 2, 4, false, 1, true},
-    {"64x64x64_s2_staged", 64, 64, 64, 2, 4, false, 1, true},
-    {"256x256x32_s4_direct", 256, 256, 32, 4, 4, true, 8, false},
-    {"256x256x32_s5_direct", 256, 256, 32, 5, 4, true, 8, false},
-    {"256x256x64_s2_direct_w8n", 256, 256, 64, 2, 8, true, 8, true},
-    {"256x256x32_s5_direct_w8n", 256, 256, 32, 5, 8, true, 8, false},
-    {"256x256x64_s2_direct_w8m", 256, 256, 64, 2, 8, true, 8, false},
-    {"256x256x64_s2_staged_w8", 256, 256, 64, 2, 8, false, 4, true},
-    {"256x128x64_s2_staged", 256, 128, 64, 2, 4, false, 4, false},
+    {"256x256x64_s2_direct", 256, 256, 64, 2, 4, true, 8, false, 1},
+    {"256x128x64_s3_direct", 256, 128, 64, 3, 4, true, 8, false, 1},
+    {"128x128x64_s3_direct", 128, 128, 64, 3, 4, true, 8, true, 1},
+    {"128x128x32_s2_staged", 128, 128, 32, 2, 4, false, 1, true, 2},
+    {"64x64x64_s2_staged", 64, 64, 64, 2, 4, false, 1, true, 5},
+    {"256x256x32_s4_direct", 256, 256, 32, 4, 4, true, 8, false, 1},
+    {"256x256x32_s5_direct", 256, 256, 32, 5, 4, true, 8, false, 1},
+    {"256x256x64_s2_direct_w8n", 256, 256, 64, 2, 8, true, 8, true, 1},
+    {"256x256x32_s5_direct_w8n", 256, 256, 32, 5, 8, true, 8, false, 1},
+    {"256x256x64_s2_direct_w8m", 256, 256, 64, 2, 8, true, 8, false, 1},
+    {"256x256x64_s2_staged_w8", 256, 256, 64, 2, 8, false, 4, true, 1},
+    {"256x128x64_s2_staged", 256, 128, 64, 2, 4, false, 4, false, 1},
 };
 
 namespace {
@@ -117,7 +121,32 @@ int kernel_vec(const ConfigDesc &d, int v, bool transposed)
     return v;
 }
 
-void fill_plan(int c, int64_t M, int64_t N, int64_t K, int va, int vb, int vc, bool ta, bool tb,
+// K splits: the K loop of every output tile divided into `splits` ranges of
+// k_split elements (a multiple of the tile depth), each run by a workgroup of
+// its own.  The fp32 partial sums go to a workspace and a second kernel adds
+// them in split order and applies the epilogue.
+struct Split {
+    int splits;
+    int64_t k_split;   // K when not split
+};
+
+Split split_geometry(const ConfigDesc &d, int64_t K, int requested)
+{
+    const int64_t nk = ceil_div(K, d.block_k);
+    if (requested <= 1 || nk <= 1)
+        return {1, K};
+    const int64_t per = ceil_div(nk, requested);   // k tiles per split
+    const int s = (int)ceil_div(nk, per);          // no empty split
+    if (s <= 1)
+        return {1, K};
+    return {s, per * d.block_k};
+}
+
+// A workgroup's slice of the workspace (block_m rows of N fp32) must be
+// addressable with the kernels' 31-bit buffer offsets.
+bool split_addressable(const ConfigDesc &d, int64_t N) { return (int64_t)d.block_m * N * 4 < ((int64_t)1 << 31); }
+
+void fill_plan(int c, int64_t M, int64_t N, int64_t K, int va, int vb, int vc, bool ta, bool tb, const Split &sp,
                gemm_f16_plan_t *p)
 {
     const ConfigDesc &d = kConfigs[c];
@@ -135,37 +164,43 @@ void fill_plan(int c, int64_t M, int64_t N, int64_t K, int va, int vb, int vc, b
     p->vec_c = vc;
     p->tiles_m = ceil_div(M, d.block_m);
     p->tiles_n = ceil_div(N, d.block_n);
-    p->grid = p->tiles_m * p->tiles_n;
-    p->k_tiles = ceil_div(K, d.block_k);
+    p->grid = p->tiles_m * p->tiles_n * sp.splits;
+    p->k_tiles = ceil_div(sp.splits > 1 ? sp.k_split : K, d.block_k);
     p->lds_bytes = gemm_f16_stage_bytes(d.block_m, d.block_n, d.block_k, d.stages);
     p->flops = 2.0 * (double)M * (double)N * (double)K;
     p->min_bytes = 2.0 * ((double)M * K + (double)K * N + (double)M * N);
     p->trans_a = ta ? 1 : 0;
     p->trans_b = tb ? 1 : 0;
+    p->splits = sp.splits;
+    p->k_split = sp.splits > 1 ? sp.k_split : K;
+    p->workspace_bytes = sp.splits > 1 ? (int64_t)sp.splits * M * N * 4 : 0;
 }
 
+// ---- automatic choice ---------------------------------------------------------
 // Measured table (tiled_dense_gemm_fp16_amd/tune.py): for swept shapes,
-// layouts and pitch alignments, the configuration that ran fastest.
+// layouts and pitch alignments, the configuration and split count that ran
+// fastest.
 struct TunedEntry {
     int lm, ln, lk;        // log2 of the swept M, N, K
     int trans_a, trans_b;
     int aligned;           // 1: pitches allowed 16-byte loads of both operands
     int config;
+    int splits;
     double tflops;
 };
 const TunedEntry kTuned[] = {
 #include "gemm_f16_tuned.inc"
-    {-1, -1, -1, -1, -1, -1, -1, 0.0}   // end marker
+    {-1, -1, -1, -1, -1, -1, -1, 0, 0.0}   // end marker
 };
 
-// The tuned configuration for the nearest swept shape (in log2 M, N, K) with
-// the same layout and alignment, if one lies within a factor of two overall;
-// -1 otherwise.
-int tuned_config(int64_t M, int64_t N, int64_t K, bool ta, bool tb, bool aligned, int va, int vb)
+// The tuned entry for the nearest swept shape (in log2 M, N, K) with the same
+// layout and alignment, if one lies within a factor of two overall; null
+// otherwise.
+const TunedEntry *tuned_entry(int64_t M, int64_t N, int64_t K, bool ta, bool tb, bool aligned, int va, int vb)
 {
     const double lm = log2((double)(M > 0 ? M : 1)), ln = log2((double)(N > 0 ? N : 1));
     const double lk = log2((double)(K > 0 ? K : 1));
-    int best = -1;
+    const TunedEntry *best = nullptr;
     double best_d = 1.0 + 1e-9;
     for (const TunedEntry &e : kTuned) {
         if (e.config < 0)
@@ -174,38 +209,97 @@ int tuned_config(int64_t M, int64_t N, int64_t K, bool ta, bool tb, bool aligned
             continue;
         const double d = sqrt((lm - e.lm) * (lm - e.lm) + (ln - e.ln) * (ln - e.ln) + (lk - e.lk) * (lk - e.lk));
         if (d < best_d && e.config < kNumConfigs && config_fits(e.config, va, vb, ta || tb)) {
-            best = e.config;
+            best = &e;
             best_d = d;
         }
     }
     return best;
 }
 
-// Pick the configuration with the lowest modelled time: full rounds of
-// workgroups over the 256 CUs times the tile's work at its efficiency.
-int choose_config(int64_t M, int64_t N, int va, int vb, bool transposed)
+// Time model used where the table has no nearby entry.  A workgroup's k tile
+// costs its flops at the configuration's sustained per-CU rate divided among
+// the workgroups sharing the CU (at most its occupancy); each workgroup adds
+// a fixed cost (pipeline fill, write-back) of a few k tiles; workgroups run
+// in rounds of CUs x occupancy.  Splitting adds the partial sums' round trip
+// through HBM (written 4 bytes, read 4 bytes per split and element) and a
+// second launch.
+constexpr double kCuFlops = 5.0e12;        // fp16 flop/s of one CU at efficiency 1 (about 1290 TF/s chip-wide)
+constexpr double kWgFixedTiles = 3.0;      // per-workgroup overhead in k-tile times
+constexpr double kStreamBytes = 4.5e12;    // bytes/s of a streaming kernel
+constexpr double kLaunchSeconds = 3e-6;    // one more kernel on the stream
+constexpr int64_t kAutoWorkspaceMax = (int64_t)256 << 20;
+
+double model_seconds(int c, int64_t M, int64_t N, int64_t K, const Split &sp)
+{
+    const ConfigDesc &d = kConfigs[c];
+    const double units = (double)(ceil_div(M, d.block_m) * ceil_div(N, d.block_n)) * sp.splits;
+    const double rounds = ceil(units / ((double)kComputeUnits * d.occupancy));
+    const double sharing = std::min((double)d.occupancy, ceil(units / kComputeUnits));
+    const double kt = (double)ceil_div(sp.splits > 1 ? sp.k_split : K, d.block_k);
+    const double t_kt = 2.0 * d.block_m * d.block_n * d.block_k * sharing / (kCuFlops * config_efficiency(c));
+    double t = rounds * (kt + kWgFixedTiles) * t_kt;
+    if (sp.splits > 1)
+        t += kLaunchSeconds + (8.0 * sp.splits + 2.0) * (double)M * (double)N / kStreamBytes;
+    return t;
+}
+
+const int kSplitCandidates[] = {1, 2, 3, 4, 6, 8, 12, 16, 24, 32};
+
+// Best split of configuration c by the model: every split keeps at least two
+// k tiles, and more splits must win by 3 %.  requested > 0 fixes the count.
+Split model_split(int c, int64_t M, int64_t N, int64_t K, int requested, double *seconds)
+{
+    const ConfigDesc &d = kConfigs[c];
+    Split best = {1, K};
+    double best_t = model_seconds(c, M, N, K, best);
+    if (requested > 0) {
+        best = split_geometry(d, K, requested);
+        best_t = model_seconds(c, M, N, K, best);
+    } else if (split_addressable(d, N)) {
+        const int64_t nk = ceil_div(K, d.block_k);
+        for (int s : kSplitCandidates) {
+            if (s == 1 || 2 * s > nk)
+                continue;
+            const Split sp = split_geometry(d, K, s);
+            if (sp.splits <= 1 || (int64_t)sp.splits * M * N * 4 > kAutoWorkspaceMax)
+                continue;
+            const double t = model_seconds(c, M, N, K, sp);
+            if (t < best_t * 0.97) {
+                best = sp;
+                best_t = t;
+            }
+        }
+    }
+    if (seconds)
+        *seconds = best_t;
+    return best;
+}
+
+// Configuration (and split) with the lowest modelled time.
+int choose_config(int64_t M, int64_t N, int64_t K, int va, int vb, bool transposed, int requested, Split *split)
 {
     int best = -1;
     double best_t = 0.0;
     for (int c = 0; c < kNumConfigs; ++c) {
         if (!config_fits(c, va, vb, transposed) || config_efficiency(c) <= 0.0)
             continue;
-        const ConfigDesc &d = kConfigs[c];
-        int64_t grid = ceil_div(M, d.block_m) * ceil_div(N, d.block_n);
-        double rounds = (double)ceil_div(grid, kComputeUnits);
-        double t = rounds * (double)d.block_m * (double)d.block_n / config_efficiency(c);
+        double t;
+        const Split sp = model_split(c, M, N, K, requested, &t);
         if (best < 0 || t < best_t * 0.999) {
             best = c;
             best_t = t;
+            *split = sp;
         }
     }
     return best;
 }
 
 gemm_f16_status_t make_plan(int64_t M, int64_t N, int64_t K, const void *A, bool ta, const void *B, bool tb,
-                            const void *C, int config, gemm_f16_plan_t *plan)
+                            const void *C, int config, int splits, gemm_f16_plan_t *plan)
 {
     if (config != GEMM_F16_CONFIG_AUTO && (config < 0 || config >= kNumConfigs))
+        return GEMM_F16_ERROR_INVALID_VALUE;
+    if (splits < 0 || splits > GEMM_F16_MAX_SPLITS)
         return GEMM_F16_ERROR_INVALID_VALUE;
     // row pitches of the matrices as stored
     const int64_t lda = ta ? M : K, ldb = tb ? K : N;
@@ -213,14 +307,26 @@ gemm_f16_status_t make_plan(int64_t M, int64_t N, int64_t K, const void *A, bool
     const int vc = (N % 8 == 0 && (uintptr_t)C % 16 == 0) ? 8 : (N % 4 == 0 && (uintptr_t)C % 8 == 0) ? 4 : 1;
     const bool tr = ta || tb;
     int c = config;
+    Split sp = {1, K};
     if (c == GEMM_F16_CONFIG_AUTO) {
-        c = tuned_config(M, N, K, ta, tb, va == 8 && vb == 8, va, vb);
-        if (c < 0)
-            c = choose_config(M, N, va, vb, tr);
+        const TunedEntry *e = tuned_entry(M, N, K, ta, tb, va == 8 && vb == 8, va, vb);
+        if (e && (splits == GEMM_F16_SPLITS_AUTO || splits == e->splits)) {
+            c = e->config;
+            sp = split_geometry(kConfigs[c], K, e->splits);
+            if (sp.splits > 1 && ((int64_t)sp.splits * M * N * 4 > kAutoWorkspaceMax ||
+                                  !split_addressable(kConfigs[c], N)))
+                sp = {1, K};
+        } else {
+            c = choose_config(M, N, K, va, vb, tr, splits, &sp);
+        }
+    } else if (config_fits(c, va, vb, tr)) {
+        sp = model_split(c, M, N, K, splits, nullptr);
     }
     if (c < 0 || !config_fits(c, va, vb, tr))
         return GEMM_F16_ERROR_INVALID_VALUE;
-    fill_plan(c, M, N, K, va, vb, vc, ta, tb, plan);
+    if (sp.splits > 1 && !split_addressable(kConfigs[c], N))
+        return GEMM_F16_ERROR_UNSUPPORTED_SIZE;
+    fill_plan(c, M, N, K, va, vb, vc, ta, tb, sp, plan);
     if (plan->grid > 0x7fffffff)
         return GEMM_F16_ERROR_UNSUPPORTED_SIZE;
     return GEMM_F16_SUCCESS;
@@ -231,13 +337,14 @@ constexpr int kMaxDevices = 64;
 std::mutex g_dev_mutex;
 int g_dev_state[kMaxDevices];   // 0 unknown, 1 gfx950, 2 other
 
-gemm_f16_status_t check_device()
+gemm_f16_status_t check_device(int *device)
 {
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0)
         return GEMM_F16_ERROR_NO_DEVICE;
     if (dev >= kMaxDevices)
         return GEMM_F16_ERROR_UNSUPPORTED_DEVICE;
+    *device = dev;
     std::lock_guard<std::mutex> lock(g_dev_mutex);
     if (g_dev_state[dev] == 0) {
         hipDeviceProp_t prop;
@@ -248,23 +355,62 @@ gemm_f16_status_t check_device()
     return g_dev_state[dev] == 1 ? GEMM_F16_SUCCESS : GEMM_F16_ERROR_UNSUPPORTED_DEVICE;
 }
 
-gemm_f16_status_t run(int64_t M, int64_t N, int64_t K, const void *A, bool ta, const void *B, bool tb, void *C,
-                      int epilogue, int config, void *stream)
+// ---- library-owned split-K workspaces -----------------------------------------
+// One buffer per (device, stream): work on one stream runs in order, so calls
+// on a stream can share its buffer; calls on different streams never do.
+struct OwnedWorkspace {
+    int dev;
+    hipStream_t stream;
+    void *ptr;
+    int64_t bytes;
+};
+std::mutex g_ws_mutex;                 // held from lookup until the kernels are enqueued
+std::vector<OwnedWorkspace> g_ws;
+
+// With g_ws_mutex held: the buffer of (dev, s), grown to at least `bytes`.
+// Growing first waits for the stream's queued work (which may still use the
+// old buffer); it is refused while the stream is being captured into a graph.
+gemm_f16_status_t owned_workspace(int dev, hipStream_t s, int64_t bytes, void **out)
 {
-    gemm_f16_status_t st = validate(M, N, K, A, B, C, true);
-    if (st != GEMM_F16_SUCCESS)
-        return st;
-    if (epilogue != GEMM_F16_EPILOGUE_NONE && epilogue != GEMM_F16_EPILOGUE_RELU)
-        return GEMM_F16_ERROR_INVALID_VALUE;
-    gemm_f16_plan_t plan;
-    st = make_plan(M, N, K, A, ta, B, tb, C, config, &plan);
-    if (st != GEMM_F16_SUCCESS)
-        return st;
-    if (M == 0 || N == 0)
+    OwnedWorkspace *w = nullptr;
+    for (OwnedWorkspace &x : g_ws)
+        if (x.dev == dev && x.stream == s) {
+            w = &x;
+            break;
+        }
+    if (w && w->bytes >= bytes) {
+        *out = w->ptr;
         return GEMM_F16_SUCCESS;
-    st = check_device();
-    if (st != GEMM_F16_SUCCESS)
-        return st;
+    }
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone)
+        return GEMM_F16_ERROR_WORKSPACE;
+    if (!w) {
+        g_ws.push_back({dev, s, nullptr, 0});
+        w = &g_ws.back();
+    }
+    if (w->ptr) {
+        if (hipStreamSynchronize(s) != hipSuccess || hipFree(w->ptr) != hipSuccess)
+            return GEMM_F16_ERROR_RUNTIME;
+        w->ptr = nullptr;
+        w->bytes = 0;
+    }
+    const int64_t want = ceil_div(bytes, (int64_t)2 << 20) * ((int64_t)2 << 20);
+    void *p = nullptr;
+    if (hipMalloc(&p, (size_t)want) != hipSuccess) {
+        (void)hipGetLastError();
+        return GEMM_F16_ERROR_WORKSPACE;
+    }
+    w->ptr = p;
+    w->bytes = want;
+    *out = p;
+    return GEMM_F16_SUCCESS;
+}
+
+// Enqueue a planned call; W is the split-K workspace (plan->splits > 1).
+gemm_f16_status_t launch_plan(const gemm_f16_plan_t &plan, int64_t M, int64_t N, int64_t K, const void *A,
+                              bool ta, const void *B, bool tb, void *C, int epilogue, void *W, hipStream_t s)
+{
     KernelArgs a;
     a.A = (const _Float16 *)A;
     a.B = (const _Float16 *)B;
@@ -277,8 +423,62 @@ gemm_f16_status_t run(int64_t M, int64_t N, int64_t K, const void *A, bool ta, c
     a.group_m = GEMM_F16_GROUP_M;
     a.relu = epilogue == GEMM_F16_EPILOGUE_RELU ? 1 : 0;
     a.vec_c = plan.vec_c;
-    hipError_t e = launch(plan.config, a, plan.vec_a, plan.vec_b, ta, tb, plan.grid, (hipStream_t)stream);
+    a.k_split = (int)plan.k_split;
+    a.W = plan.splits > 1 ? (float *)W : nullptr;
+    hipError_t e = launch(plan.config, a, plan.vec_a, plan.vec_b, ta, tb, plan.grid, s);
+    if (e == hipSuccess && plan.splits > 1)
+        e = launch_reduce((const float *)W, (_Float16 *)C, M, N, plan.splits, a.relu, plan.vec_c >= 4, s);
     return e == hipSuccess ? GEMM_F16_SUCCESS : GEMM_F16_ERROR_LAUNCH_FAILED;
+}
+
+// workspace: the caller's buffer (workspace_bytes long) or null for the
+// library's own.  fallback: if the library's buffer cannot be had (graph
+// capture, allocation failure), run unsplit instead of failing.
+gemm_f16_status_t run(int64_t M, int64_t N, int64_t K, const void *A, bool ta, const void *B, bool tb, void *C,
+                      int epilogue, int config, int splits, void *workspace, int64_t workspace_bytes,
+                      bool fallback, void *stream)
+{
+    gemm_f16_status_t st = validate(M, N, K, A, B, C, true);
+    if (st != GEMM_F16_SUCCESS)
+        return st;
+    if (epilogue != GEMM_F16_EPILOGUE_NONE && epilogue != GEMM_F16_EPILOGUE_RELU)
+        return GEMM_F16_ERROR_INVALID_VALUE;
+    if (workspace_bytes < 0 || (!workspace && workspace_bytes != 0))
+        return GEMM_F16_ERROR_INVALID_VALUE;
+    gemm_f16_plan_t plan;
+    st = make_plan(M, N, K, A, ta, B, tb, C, config, splits, &plan);
+    if (st != GEMM_F16_SUCCESS)
+        return st;
+    if (M == 0 || N == 0)
+        return GEMM_F16_SUCCESS;
+    if (plan.splits > 1 && workspace) {
+        if ((uintptr_t)workspace % 16 != 0)
+            return GEMM_F16_ERROR_MISALIGNED;
+        if (workspace_bytes < plan.workspace_bytes)
+            return GEMM_F16_ERROR_WORKSPACE;
+        if (overlaps(workspace, plan.workspace_bytes, A, 2 * M * K) ||
+            overlaps(workspace, plan.workspace_bytes, B, 2 * K * N) ||
+            overlaps(workspace, plan.workspace_bytes, C, 2 * M * N))
+            return GEMM_F16_ERROR_INVALID_VALUE;
+    }
+    int dev = -1;
+    st = check_device(&dev);
+    if (st != GEMM_F16_SUCCESS)
+        return st;
+    hipStream_t s = (hipStream_t)stream;
+    if (plan.splits <= 1 || workspace)
+        return launch_plan(plan, M, N, K, A, ta, B, tb, C, epilogue, workspace, s);
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    void *w = nullptr;
+    st = owned_workspace(dev, s, plan.workspace_bytes, &w);
+    if (st == GEMM_F16_ERROR_WORKSPACE && fallback) {
+        st = make_plan(M, N, K, A, ta, B, tb, C, config, 1, &plan);
+        if (st != GEMM_F16_SUCCESS)
+            return st;
+    } else if (st != GEMM_F16_SUCCESS) {
+        return st;
+    }
+    return launch_plan(plan, M, N, K, A, ta, B, tb, C, epilogue, w, s);
 }
 
 } // namespace
@@ -291,13 +491,15 @@ extern "C" {
 gemm_f16_status_t gemm_f16(int64_t M, int64_t N, int64_t K, const void *A, const void *B, void *C,
                            int epilogue, void *stream)
 {
-    return run(M, N, K, A, false, B, false, C, epilogue, GEMM_F16_CONFIG_AUTO, stream);
+    return run(M, N, K, A, false, B, false, C, epilogue, GEMM_F16_CONFIG_AUTO, GEMM_F16_SPLITS_AUTO, nullptr, 0,
+               true, stream);
 }
 
 gemm_f16_status_t gemm_f16_ex(int64_t M, int64_t N, int64_t K, const void *A, const void *B, void *C,
                               int epilogue, int config, void *stream)
 {
-    return run(M, N, K, A, false, B, false, C, epilogue, config, stream);
+    const int splits = config == GEMM_F16_CONFIG_AUTO ? GEMM_F16_SPLITS_AUTO : 1;
+    return run(M, N, K, A, false, B, false, C, epilogue, config, splits, nullptr, 0, true, stream);
 }
 
 gemm_f16_status_t gemm_f16_trans(int64_t M, int64_t N, int64_t K, const void *A, int trans_a, const void *B,
@@ -305,7 +507,18 @@ gemm_f16_status_t gemm_f16_trans(int64_t M, int64_t N, int64_t K, const void *A,
 {
     if ((trans_a != 0 && trans_a != 1) || (trans_b != 0 && trans_b != 1))
         return GEMM_F16_ERROR_INVALID_VALUE;
-    return run(M, N, K, A, trans_a != 0, B, trans_b != 0, C, epilogue, config, stream);
+    const int splits = config == GEMM_F16_CONFIG_AUTO ? GEMM_F16_SPLITS_AUTO : 1;
+    return run(M, N, K, A, trans_a != 0, B, trans_b != 0, C, epilogue, config, splits, nullptr, 0, true, stream);
+}
+
+gemm_f16_status_t gemm_f16_split(int64_t M, int64_t N, int64_t K, const void *A, int trans_a, const void *B,
+                                 int trans_b, void *C, int epilogue, int config, int splits, void *workspace,
+                                 int64_t workspace_bytes, void *stream)
+{
+    if ((trans_a != 0 && trans_a != 1) || (trans_b != 0 && trans_b != 1))
+        return GEMM_F16_ERROR_INVALID_VALUE;
+    return run(M, N, K, A, trans_a != 0, B, trans_b != 0, C, epilogue, config, splits, workspace,
+               workspace_bytes, false, stream);
 }
 
 gemm_f16_status_t gemm_f16_plan(int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *C,
@@ -318,12 +531,40 @@ gemm_f16_status_t gemm_f16_plan_trans(int64_t M, int64_t N, int64_t K, const voi
                                       const void *B, int trans_b, const void *C, int config,
                                       gemm_f16_plan_t *plan)
 {
+    const int splits = config == GEMM_F16_CONFIG_AUTO ? GEMM_F16_SPLITS_AUTO : 1;
+    return gemm_f16_plan_split(M, N, K, A, trans_a, B, trans_b, C, config, splits, plan);
+}
+
+gemm_f16_status_t gemm_f16_plan_split(int64_t M, int64_t N, int64_t K, const void *A, int trans_a,
+                                      const void *B, int trans_b, const void *C, int config, int splits,
+                                      gemm_f16_plan_t *plan)
+{
     if (!plan || (trans_a != 0 && trans_a != 1) || (trans_b != 0 && trans_b != 1))
         return GEMM_F16_ERROR_INVALID_VALUE;
     gemm_f16_status_t st = validate(M, N, K, A, B, C, false);
     if (st != GEMM_F16_SUCCESS)
         return st;
-    return make_plan(M, N, K, A, trans_a != 0, B, trans_b != 0, C, config, plan);
+    return make_plan(M, N, K, A, trans_a != 0, B, trans_b != 0, C, config, splits, plan);
+}
+
+gemm_f16_status_t gemm_f16_release_workspaces(void)
+{
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    if (g_ws.empty())
+        return GEMM_F16_SUCCESS;
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess)
+        return GEMM_F16_ERROR_RUNTIME;
+    gemm_f16_status_t st = GEMM_F16_SUCCESS;
+    for (OwnedWorkspace &w : g_ws) {
+        // hipFree waits for the device's work, which may still read the buffer
+        if (w.ptr && (hipSetDevice(w.dev) != hipSuccess || hipFree(w.ptr) != hipSuccess))
+            st = GEMM_F16_ERROR_RUNTIME;
+    }
+    g_ws.clear();
+    if (hipSetDevice(cur) != hipSuccess)
+        st = GEMM_F16_ERROR_RUNTIME;
+    return st;
 }
 
 int gemm_f16_num_configs(void) { return kNumConfigs; }
@@ -347,11 +588,13 @@ const char *gemm_f16_status_string(gemm_f16_status_t status)
     switch (status) {
     case GEMM_F16_SUCCESS: return "success";
     case GEMM_F16_ERROR_INVALID_VALUE: return "invalid value";
-    case GEMM_F16_ERROR_MISALIGNED: return "pointer not 2-byte aligned";
+    case GEMM_F16_ERROR_MISALIGNED: return "pointer not aligned";
     case GEMM_F16_ERROR_NO_DEVICE: return "no HIP device";
     case GEMM_F16_ERROR_UNSUPPORTED_DEVICE: return "device is not gfx950";
     case GEMM_F16_ERROR_LAUNCH_FAILED: return "kernel launch failed";
     case GEMM_F16_ERROR_UNSUPPORTED_SIZE: return "size beyond the library's limits";
+    case GEMM_F16_ERROR_WORKSPACE: return "split-K workspace too small or not obtainable";
+    case GEMM_F16_ERROR_RUNTIME: return "HIP runtime call failed";
     }
     return "unknown status";
 }

@@ -20,6 +20,8 @@ struct KernelArgs {
     int relu;            // 1: max(acc, 0) before the fp16 conversion
     int vec_c;           // 8: 16-byte stores of C are aligned (LDS-staged write-back);
                          // 4: 8-byte stores; 1: 2-byte stores
+    int k_split;         // K elements per workgroup (a multiple of the tile depth); >= K unless split
+    float *W;            // split-K: splits x M x N fp32 partial sums (written instead of C); else null
 };
 
 // Static description of one compiled kernel configuration.
@@ -31,6 +33,7 @@ struct ConfigDesc {
     bool direct;          // operands move global -> LDS with buffer_load ... lds
     int min_vec;          // smallest vector width (elements) of A and B loads it accepts
     bool transposed;      // also compiled for A given K x M and/or B given N x K
+    int occupancy;        // workgroups resident per CU (LDS and register limits)
 };
 
 constexpr int kNumConfigs = 12;
@@ -43,6 +46,12 @@ extern const ConfigDesc kConfigs[kNumConfigs];
 // launch status.
 hipError_t launch(int config, const KernelArgs &a, int va, int vb, bool trans_a, bool trans_b, int64_t grid,
                   hipStream_t s);
+
+// Split-K reduction: C = rne16(epi(W[0] + ... + W[splits-1])) over M x N
+// elements (relu: 1 for the ReLU epilogue).  vec4: N % 4 == 0, C 8-byte and
+// W 16-byte aligned.
+hipError_t launch_reduce(const float *W, _Float16 *C, int64_t M, int64_t N, int splits, int relu, bool vec4,
+                         hipStream_t s);
 
 } // namespace gemm_f16_impl
 

@@ -39,6 +39,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "gemm_f16_internal.h"
 
 // Build-time switches kept for tuning sweeps (defaults are the measured best):
@@ -59,6 +61,7 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef short short4v __attribute__((ext_vector_type(4)));
 typedef float float16v __attribute__((ext_vector_type(16)));
+typedef float float4v __attribute__((ext_vector_type(4)));
 typedef int int4v __attribute__((ext_vector_type(4)));
 typedef int int2v __attribute__((ext_vector_type(2)));
 
@@ -70,7 +73,6 @@ constexpr int kBufferFlags = 0x00020000;
 // num_records (panels never exceed 2 GiB): reads give 0, writes are dropped.
 // It is OR-ed in arithmetically so that the compiler keeps one straight-line
 // instruction instead of branching around each access.
-constexpr uint32_t kOob = 0x80000000u;
 __device__ __forceinline__ uint32_t oob_unless(bool ok) { return (uint32_t)(!ok) << 31; }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
@@ -149,7 +151,7 @@ __device__ __forceinline__ int swz_b(int row)
 // walk tiles GROUP_M rows at a time (column-major inside the group) so that
 // concurrently running tiles share A row-panels and B column-panels.
 __device__ __forceinline__ void tile_coords(int wg, int grid, int tiles_m, int tiles_n, int group_m,
-                                            int &tm, int &tn)
+                                            int &tm, int &tn, int &split)
 {
 #if GEMM_F16_NO_XCD_REMAP
     int id = wg;
@@ -159,6 +161,9 @@ __device__ __forceinline__ void tile_coords(int wg, int grid, int tiles_m, int t
     int xcd = wg % kXcds, local = wg / kXcds;
     int id = (xcd < rem) ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
 #endif
+    // split-K: the K splits of the tile space follow one another
+    split = id / (tiles_m * tiles_n);
+    id -= split * (tiles_m * tiles_n);
     int width = group_m * tiles_n;
     int group = id / width;
     int first_m = group * group_m;
@@ -259,7 +264,8 @@ struct Operand {
     const half_t *X;       // the stored matrix
     int ld;                // its row pitch (elements)
     int mn0;               // first m (A) or n (B) of the workgroup's tile
-    int K;
+    int K;                 // end of the workgroup's k range
+    int kbase;             // start of the workgroup's k range (split-K), a multiple of BK
     __amdgpu_buffer_rsrc_t panel;   // ROWS_K: the workgroup's BMN rows
     uint32_t off0, step;   // direct: byte offset of the first chunk, distance between loads
     int kcol0;             // direct, ROWS_K: k column of the thread's chunks
@@ -268,13 +274,14 @@ struct Operand {
     int ldsv[VEC_DIV];
     typename VecT<V>::type reg[VEC_DIV];
 
-    __device__ __forceinline__ void init(const half_t *x, int ld_, int mn0_, int mn_total, int K_, int tid,
-                                         int wave, int lane)
+    __device__ __forceinline__ void init(const half_t *x, int ld_, int mn0_, int mn_total, int k_begin, int k_end,
+                                         int tid, int wave, int lane)
     {
         X = x;
         ld = ld_;
         mn0 = mn0_;
-        K = K_;
+        K = k_end;
+        kbase = k_begin;
         if constexpr (ROWS_K) {
             const int rows = min(BMN, mn_total - mn0);
             panel = make_rsrc(X + (int64_t)mn0 * ld, (uint32_t)rows * (uint32_t)ld * 2u);
@@ -299,11 +306,12 @@ struct Operand {
         }
     }
 
-    // Start the loads of k slice kt: into LDS at dst (direct) or into the
-    // registers (staged).  kt past the last slice is allowed and reads zeros.
+    // Start the loads of k slice kt of the workgroup's range: into LDS at dst
+    // (direct) or into the registers (staged).  kt past the last slice is
+    // allowed and reads zeros.
     __device__ __forceinline__ void issue(int kt, half_t *dst, int wave)
     {
-        const int k0 = kt * BK;
+        const int k0 = kbase + kt * BK;
         __amdgpu_buffer_rsrc_t rs;
         uint32_t shift = 0;
         if constexpr (ROWS_K) {
@@ -405,9 +413,12 @@ gemm_f16_kernel(KernelArgs args)
     half_t *const Bs = lds + STAGES * T::A_STAGE;            // STAGES B stages
 
     const int M = args.M, N = args.N, K = args.K;
-    int tm, tn;
-    tile_coords(blockIdx.x, gridDim.x, args.tiles_m, args.tiles_n, args.group_m, tm, tn);
+    int tm, tn, split;
+    tile_coords(blockIdx.x, gridDim.x, args.tiles_m, args.tiles_n, args.group_m, tm, tn, split);
     const int m0 = tm * BM, n0 = tn * BN;
+    // the workgroup's k range: all of K, or one split of k_split (a multiple of BK)
+    const int k_begin = split * args.k_split;
+    const int k_end = min(K, k_begin + args.k_split);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -415,14 +426,14 @@ gemm_f16_kernel(KernelArgs args)
     const int wm0 = (wave / WN) * T::WTM;                   // wave sub-tile origin in the tile
     const int wn0 = (wave % WN) * T::WTN;
 
-    const int nk = (K + BK - 1) / BK;
+    const int nk = (k_end - k_begin + BK - 1) / BK;
 
     // A is M x K (lda = K) or, given transposed, K x M (lda = M); B is K x N
     // (ldb = N) or, given transposed, N x K (ldb = K).
     typename T::OpA opa;
     typename T::OpB opb;
-    opa.init(args.A, A_ROWS_K ? K : M, m0, M, K, tid, wave, lane);
-    opb.init(args.B, B_ROWS_K ? K : N, n0, N, K, tid, wave, lane);
+    opa.init(args.A, A_ROWS_K ? K : M, m0, M, k_begin, k_end, tid, wave, lane);
+    opb.init(args.B, B_ROWS_K ? K : N, n0, N, k_begin, k_end, tid, wave, lane);
 
     auto issue_loads = [&](int kt, half_t *dst_a, half_t *dst_b) {
         opa.issue(kt, dst_a, wave);
@@ -588,8 +599,45 @@ gemm_f16_kernel(KernelArgs args)
         mma(f1);
     wait_vmcnt<0>();   // the tail's zero-filling loads must land before the workgroup retires
 
-    // ---- epilogue: optional ReLU, RNE to fp16, store ----
     const int c_rows = min(BM, M - m0);
+    if (args.W) {
+        // split-K: the fp32 partial sums of this split go to its slice of the
+        // workspace (row pitch N); the reduction applies the epilogue.  When
+        // N % 4 == 0 a lane's four consecutive columns leave as one 16-byte
+        // store, else as four 4-byte stores.
+        float *w_base = args.W + ((int64_t)split * M + m0) * N;
+        const __amdgpu_buffer_rsrc_t w_rsrc = make_rsrc(w_base, (uint32_t)c_rows * (uint32_t)N * 4u);
+        const bool w4 = (N & 3) == 0;
+#pragma unroll
+        for (int i = 0; i < T::TM; ++i) {
+            const int r = wm0 + 32 * i + (lane & 31);
+#pragma unroll
+            for (int j = 0; j < T::TN; ++j)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int n = n0 + wn0 + 32 * j + 8 * g + 4 * (lane >> 5);
+                    const uint32_t off = ((uint32_t)r * (uint32_t)N + (uint32_t)n) * 4u;
+                    // element values copied to scalars before any bit cast (see out4)
+                    const float v0 = acc[i][j][4 * g + 0], v1 = acc[i][j][4 * g + 1];
+                    const float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
+                    if (w4) {
+                        const float4v v = {v0, v1, v2, v3};
+                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(int4v, v), w_rsrc,
+                                                               off | oob_unless(n < N), 0, 0);
+                    } else {
+                        const int bits[4] = {__builtin_bit_cast(int, v0), __builtin_bit_cast(int, v1),
+                                             __builtin_bit_cast(int, v2), __builtin_bit_cast(int, v3)};
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            __builtin_amdgcn_raw_buffer_store_b32(bits[e], w_rsrc,
+                                                                  (off + 4u * e) | oob_unless(n + e < N), 0, 0);
+                    }
+                }
+        }
+        return;
+    }
+
+    // ---- epilogue: optional ReLU, RNE to fp16, store ----
     half_t *c_base = args.C + (int64_t)m0 * N;
     const __amdgpu_buffer_rsrc_t c_rsrc = make_rsrc(c_base, (uint32_t)c_rows * (uint32_t)N * 2u);
     const bool relu = args.relu != 0;
@@ -688,6 +736,67 @@ gemm_f16_kernel(KernelArgs args)
             }
         }
     }
+}
+
+// ---- split-K reduction ---------------------------------------------------------
+// C = rne16(epi(sum over s of W[s])) elementwise, the splits added in index
+// order in fp32 (so the result does not depend on scheduling).  W holds
+// `splits` slices of M x N fp32 one after another, C is M x N fp16, both
+// with row pitch N: the flattened index e addresses the same element in
+// both.  VEC4: four consecutive elements per step (M N % 4 == 0, C 8-byte
+// aligned, W 16-byte aligned).  An HBM-bound stream: 4 splits + 2 bytes
+// moved per output element.
+template <bool VEC4>
+__global__ void __launch_bounds__(256) splitk_reduce_kernel(const float *__restrict__ W, half_t *__restrict__ C,
+                                                            int64_t mn, int splits, int relu)
+{
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    if constexpr (VEC4) {
+        const int64_t n4 = mn / 4;
+        for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < n4; q += stride) {
+            float4v acc = __builtin_nontemporal_load(reinterpret_cast<const float4v *>(W) + q);
+            for (int s = 1; s < splits; ++s) {
+                const float4v v = __builtin_nontemporal_load(reinterpret_cast<const float4v *>(W + s * mn) + q);
+                acc[0] += v[0];
+                acc[1] += v[1];
+                acc[2] += v[2];
+                acc[3] += v[3];
+            }
+            if (relu) {
+                acc[0] = __builtin_fmaxf(acc[0], 0.0f);
+                acc[1] = __builtin_fmaxf(acc[1], 0.0f);
+                acc[2] = __builtin_fmaxf(acc[2], 0.0f);
+                acc[3] = __builtin_fmaxf(acc[3], 0.0f);
+            }
+            const half_t h0 = (half_t)acc[0], h1 = (half_t)acc[1], h2 = (half_t)acc[2], h3 = (half_t)acc[3];
+            reinterpret_cast<half4 *>(C)[q] = half4{h0, h1, h2, h3};
+        }
+    } else {
+        for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < mn; e += stride) {
+            float acc = W[e];
+            for (int s = 1; s < splits; ++s)
+                acc += W[s * mn + e];
+            if (relu)
+                acc = __builtin_fmaxf(acc, 0.0f);
+            C[e] = (half_t)acc;
+        }
+    }
+}
+
+hipError_t launch_reduce(const float *W, _Float16 *C, int64_t M, int64_t N, int splits, int relu, bool vec4,
+                         hipStream_t s)
+{
+    const int64_t mn = M * N;
+    const int64_t items = vec4 ? mn / 4 : mn;
+    // enough workgroups to keep every CU streaming, each thread a few items
+    const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((items + 255) / 256, 256 * 16));
+    if (vec4)
+        hipLaunchKernelGGL(splitk_reduce_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, s, W, C, mn, splits,
+                           relu);
+    else
+        hipLaunchKernelGGL(splitk_reduce_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, s, W, C, mn,
+                           splits, relu);
+    return hipGetLastError();
 }
 
 // ---- launchers ----------------------------------------------------------------

@@ -6,11 +6,13 @@ the search on new hardware ("TileLang：比 Triton 低一层的 tile 语言",
 section "工程上的几个注意点"; "5分钟上手TileLang：GPU内核开发指南", section
 "避坑与调参").  This script is that search for this library: on a GPU it
 times every configuration that accepts each shape of a grid (three sizes per
-dimension, four layouts, aligned and misaligned pitches) and writes
-``csrc/gemm_f16_tuned.inc``, a table the host planner consults before its
-analytic model.  Rebuild the library afterwards.
+dimension, four layouts, aligned and misaligned pitches), unsplit and with
+K split 2 to 16 ways, and writes ``csrc/gemm_f16_tuned.inc``, a table the
+host planner consults before its analytic model.  Rebuild the library
+afterwards.
 
-    python -m tiled_dense_gemm_fp16_amd.tune [--quick] [--out PATH]
+    python -m tiled_dense_gemm_fp16_amd.tune [--layouts nn,nt,tn,tt] [--out PATH] [--log LOG]
+    python -m tiled_dense_gemm_fp16_amd.tune --from-log LOG [LOG ...] [--out PATH]
 """
 from __future__ import annotations
 
@@ -27,6 +29,9 @@ OUT = os.path.join(HERE, "csrc", "gemm_f16_tuned.inc")
 SIZES_MN = [512, 2048, 8192]
 SIZES_K = [512, 2048, 8192]
 LAYOUTS = [(False, False), (False, True), (True, False), (True, True)]
+SPLITS = [1, 2, 4, 8, 16]
+WORKSPACE_MAX = 256 << 20     # the planner's limit for automatic splits
+_SIDE = None                  # one capture stream for the whole sweep (one library workspace)
 
 
 def _time(fn, flops, target_s=0.03):
@@ -37,7 +42,15 @@ def _time(fn, flops, target_s=0.03):
     rate Python can issue them."""
     import torch
 
+    global _SIDE
+    if _SIDE is None:
+        _SIDE = torch.cuda.Stream()
+    side = _SIDE
     fn()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()                  # sizes the library's split-K workspace for the capture stream
+    torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     s.record()
@@ -47,7 +60,6 @@ def _time(fn, flops, target_s=0.03):
     torch.cuda.synchronize()
     one = max(s.elapsed_time(e) / 4, 1e-3)   # ms, an upper bound for small shapes
     per_graph = max(1, min(64, int(2.0 / one)))
-    side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.stream(side):
@@ -92,20 +104,29 @@ def sweep(sizes_mn, sizes_k, layouts, log):
                         best = None
                         results = {}
                         for cfg in range(g.num_configs()):
-                            try:
-                                g.plan(m, n, k, a.data_ptr(), b.data_ptr(), c.data_ptr(), config=cfg,
-                                       trans_a=ta, trans_b=tb)
-                            except g.GemmError:
-                                continue
-                            tf = _time(lambda: g.gemm(a, b, out=c, config=cfg, trans_a=ta, trans_b=tb),
-                                       2.0 * m * n * k)
-                            results[cfg] = round(tf, 1)
-                            if best is None or tf > results[best]:
-                                best = cfg
+                            for sp in SPLITS:
+                                try:
+                                    p = g.plan(m, n, k, a.data_ptr(), b.data_ptr(), c.data_ptr(), config=cfg,
+                                               trans_a=ta, trans_b=tb, splits=sp)
+                                except g.GemmError:
+                                    break
+                                # a split must keep two k tiles and use a new count
+                                if sp > 1 and (p["splits"] != sp or p["k_tiles"] < 2
+                                               or p["workspace_bytes"] > WORKSPACE_MAX):
+                                    continue
+                                tf = _time(lambda: g.gemm(a, b, out=c, config=cfg, trans_a=ta, trans_b=tb,
+                                                          splits=sp), 2.0 * m * n * k)
+                                key = f"{cfg}:{sp}"
+                                results[key] = round(tf, 1)
+                                if best is None or tf > results[best]:
+                                    best = key
                         rec = {"M": m, "N": n, "K": k, "trans_a": int(ta), "trans_b": int(tb),
                                "aligned": int(aligned), "best": best, "tflops": results}
                         rows.append(rec)
                         print(json.dumps(rec), file=log, flush=True)
+                        if log is not sys.stdout:
+                            print(f"{m}x{n}x{k} ta={int(ta)} tb={int(tb)}: {best} "
+                                  f"{results.get(best, 0.0)} TF/s", flush=True)
                         del a, b, c
     return rows
 
@@ -116,13 +137,14 @@ def write_table(rows, path, note):
         "// tiled_dense_gemm_fp16_amd/tune.py; do not edit by hand.",
         f"// {note}",
         "// fields: log2 M, log2 N, log2 K (of the swept shape), trans_a, trans_b,",
-        "// pitches aligned to 16 bytes (1) or not (0), best configuration, its TFLOP/s",
+        "// pitches aligned to 16 bytes (1) or not (0), best configuration, K splits, its TFLOP/s",
     ]
     for r in rows:
         if r["best"] is None:
             continue
         lm, ln, lk = (round(math.log2(r[x])) for x in ("M", "N", "K"))
-        lines.append(f"{{{lm}, {ln}, {lk}, {r['trans_a']}, {r['trans_b']}, {r['aligned']}, {r['best']}, "
+        cfg, sp = r["best"].split(":")
+        lines.append(f"{{{lm}, {ln}, {lk}, {r['trans_a']}, {r['trans_b']}, {r['aligned']}, {cfg}, {sp}, "
                      f"{r['tflops'][r['best']]:.1f}}},")
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -130,17 +152,26 @@ def write_table(rows, path, note):
 
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("--quick", action="store_true", help="NN layout only")
+    ap.add_argument("--layouts", default="nn,nt,tn,tt",
+                    help="comma-separated layouts to sweep (n: as stored, t: given transposed)")
     ap.add_argument("--out", default=OUT)
     ap.add_argument("--log", default=None, help="also write every measurement (JSON lines) here")
+    ap.add_argument("--from-log", nargs="+", default=None, metavar="LOG",
+                    help="write the table from earlier sweeps' logs instead of measuring")
     args = ap.parse_args()
+    if args.from_log:
+        rows = [json.loads(line) for path in args.from_log for line in open(path) if line.strip()]
+        write_table(rows, args.out, f"combined from {len(args.from_log)} sweep log(s)")
+        print(f"wrote {args.out} ({len(rows)} shapes)", flush=True)
+        return 0
     import torch
 
     if not torch.cuda.is_available():
         print("tune.py needs a GPU", file=sys.stderr)
         return 2
+    codes = {"nn": (False, False), "nt": (False, True), "tn": (True, False), "tt": (True, True)}
+    layouts = [codes[x] for x in args.layouts.split(",")]
     log = open(args.log, "w") if args.log else sys.stdout
-    layouts = LAYOUTS[:1] if args.quick else LAYOUTS
     rows = sweep(SIZES_MN, SIZES_K, layouts, log)
     dev = torch.cuda.get_device_properties(0)
     note = (f"swept {datetime.date.today().isoformat()} on {dev.name} "
