@@ -308,8 +308,9 @@ struct Operand {
 
     // Start the loads of k slice kt of the workgroup's range: into LDS at dst
     // (direct) or into the registers (staged).  kt past the last slice is
-    // allowed and reads zeros.
-    __device__ __forceinline__ void issue(int kt, half_t *dst, int wave)
+    // allowed and reads zeros.  Direct loads may be issued in `nparts` parts
+    // (part `part` of them here), spread over a tile's k steps.
+    __device__ __forceinline__ void issue(int kt, half_t *dst, int wave, int part = 0, int nparts = 1)
     {
         const int k0 = kbase + kt * BK;
         __amdgpu_buffer_rsrc_t rs;
@@ -327,6 +328,8 @@ struct Operand {
             const uint32_t mask = ROWS_K ? oob_unless(k0 + kcol0 < K) : 0u;
 #pragma unroll
             for (int i = 0; i < DMA; ++i) {
+                if (i * nparts / DMA != part)
+                    continue;
                 const uint32_t off = (off0 + shift + (uint32_t)i * step) | mask;
                 LDS_AS void *d = (LDS_AS void *)(dst + (wave + WAVES * i) * 512);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d, 16, off, 0, 0, 0);
@@ -401,8 +404,12 @@ struct Tile {
     static constexpr int LOADS_PER_TILE = OpA::LOADS + OpB::LOADS;
 };
 
+// SPREAD (direct kernels): the loads of the tile requested during a step are
+// issued a part per k step instead of all at its start, so that four waves
+// do not queue a whole tile of loads ahead of their MFMAs at once (measured:
+// +3 % for 256x256 tiles with 4 waves, +6-8 % for 128x128; -2 % with 8 waves).
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool DIRECT, int VA, int VB, bool A_ROWS_K,
-          bool B_ROWS_K>
+          bool B_ROWS_K, bool SPREAD = false>
 __global__ void __launch_bounds__(64 * WM * WN)
 __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4)))
 gemm_f16_kernel(KernelArgs args)
@@ -435,9 +442,9 @@ gemm_f16_kernel(KernelArgs args)
     opa.init(args.A, A_ROWS_K ? K : M, m0, M, k_begin, k_end, tid, wave, lane);
     opb.init(args.B, B_ROWS_K ? K : N, n0, N, k_begin, k_end, tid, wave, lane);
 
-    auto issue_loads = [&](int kt, half_t *dst_a, half_t *dst_b) {
-        opa.issue(kt, dst_a, wave);
-        opb.issue(kt, dst_b, wave);
+    auto issue_loads = [&](int kt, half_t *dst_a, half_t *dst_b, int part = 0, int nparts = 1) {
+        opa.issue(kt, dst_a, wave, part, nparts);
+        opb.issue(kt, dst_b, wave, part, nparts);
     };
     auto store_staged = [&](half_t *dst_a, half_t *dst_b) {
         opa.store(dst_a);
@@ -517,10 +524,21 @@ gemm_f16_kernel(KernelArgs args)
     // `pending`.  The restrict qualifiers tell the compiler that the stage
     // being filled is not the stage being read, so it does not make the LDS
     // reads wait for those loads or writes.
+    constexpr bool SPREAD_LOADS = DIRECT && SPREAD;
+    constexpr int PARTS = SPREAD_LOADS ? NS : 1;
     auto step = [&](const half_t *__restrict__ rd_a, const half_t *__restrict__ rd_b,
                     half_t *__restrict__ wr_a, half_t *__restrict__ wr_b, int kt_next, bool pending) {
+        // direct, spread: part p of the requested tile goes out with k step p
+        auto issue_part = [&](int p) {
+            if constexpr (SPREAD_LOADS)
+                issue_loads(kt_next, wr_a, wr_b, p, PARTS);
+        };
         if constexpr (DIRECT) {
-            issue_loads(kt_next, wr_a, wr_b);   // past the last tile: zeros into a retired stage
+            // past the last tile: zeros into a retired stage
+            if constexpr (SPREAD_LOADS)
+                issue_part(0);
+            else
+                issue_loads(kt_next, wr_a, wr_b);
         } else {
             wait_vmcnt<0>();                    // tile kt+1 is in the registers
             store_staged(wr_a, wr_b);
@@ -529,18 +547,21 @@ gemm_f16_kernel(KernelArgs args)
         load_frags(f0, rd_a, rd_b, 0);
         if (pending)
             mma(f1);
-        interleave(DIRECT ? T::LOADS_PER_TILE : 0, DIRECT ? 0 : T::LOADS_PER_TILE);
+        constexpr int PART_LOADS = T::LOADS_PER_TILE / PARTS;
+        interleave(DIRECT ? PART_LOADS : 0, DIRECT ? 0 : T::LOADS_PER_TILE);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int ks = 0; ks + 1 < NS; ks += 2) {
+            issue_part(ks + 1);
             load_frags(f1, rd_a, rd_b, ks + 1);
             mma(f0);
-            interleave(0, 0);
+            interleave(SPREAD_LOADS ? PART_LOADS : 0, 0);
             __builtin_amdgcn_sched_barrier(0);
             if (ks + 2 < NS) {
+                issue_part(ks + 2);
                 load_frags(f0, rd_a, rd_b, ks + 2);
                 mma(f1);
-                interleave(0, 0);
+                interleave(SPREAD_LOADS ? PART_LOADS : 0, 0);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -801,10 +822,11 @@ hipError_t launch_reduce(const float *W, _Float16 *C, int64_t M, int64_t N, int 
 
 // ---- launchers ----------------------------------------------------------------
 
-template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool DIRECT, int VA, int VB, bool AR, bool BR>
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool DIRECT, int VA, int VB, bool AR, bool BR,
+          bool SPREAD = false>
 static hipError_t launch_one(const KernelArgs &a, int64_t grid, hipStream_t stream)
 {
-    hipLaunchKernelGGL((gemm_f16_kernel<BM, BN, BK, WM, WN, STAGES, DIRECT, VA, VB, AR, BR>),
+    hipLaunchKernelGGL((gemm_f16_kernel<BM, BN, BK, WM, WN, STAGES, DIRECT, VA, VB, AR, BR, SPREAD>),
                        dim3((unsigned)grid), dim3(64 * WM * WN), 0, stream, a);
     return hipGetLastError();
 }
@@ -859,7 +881,7 @@ static hipError_t launch_transposed(int config, const KernelArgs &a, int va, int
                                     hipStream_t s)
 {
     switch (config) {
-    case 2: return launch_one<128, 128, 64, 2, 2, 3, true, 8, 8, AR, BR>(a, grid, s);
+    case 2: return launch_one<128, 128, 64, 2, 2, 3, true, 8, 8, AR, BR, true>(a, grid, s);
     case 3: return launch_staged_8or1<128, 128, 32, 2, 2, 2, AR, BR>(a, va, vb, grid, s);
     case 4: return launch_staged_8or1<64, 64, 64, 2, 2, 2, AR, BR>(a, va, vb, grid, s);
     case 7: return launch_one<256, 256, 64, 2, 4, 2, true, 8, 8, AR, BR>(a, grid, s);
@@ -881,9 +903,9 @@ hipError_t launch(int config, const KernelArgs &a, int va, int vb, bool trans_a,
     // A as M x K, B as K x N: every configuration
     constexpr bool AR = true, BR = false;
     switch (config) {
-    case 0: return launch_one<256, 256, 64, 2, 2, 2, true, 8, 8, AR, BR>(a, grid, s);
-    case 1: return launch_one<256, 128, 64, 2, 2, 3, true, 8, 8, AR, BR>(a, grid, s);
-    case 2: return launch_one<128, 128, 64, 2, 2, 3, true, 8, 8, AR, BR>(a, grid, s);
+    case 0: return launch_one<256, 256, 64, 2, 2, 2, true, 8, 8, AR, BR, true>(a, grid, s);
+    case 1: return launch_one<256, 128, 64, 2, 2, 3, true, 8, 8, AR, BR, true>(a, grid, s);
+    case 2: return launch_one<128, 128, 64, 2, 2, 3, true, 8, 8, AR, BR, true>(a, grid, s);
     case 3: return launch_staged<128, 128, 32, 2, 2, 2, AR, BR>(a, va, vb, grid, s);
     case 4: return launch_staged<64, 64, 64, 2, 2, 2, AR, BR>(a, va, vb, grid, s);
     case 5: return launch_one<256, 256, 32, 2, 2, 4, true, 8, 8, AR, BR>(a, grid, s);
