@@ -17,10 +17,14 @@ round-to-nearest-even to binary16.  The arithmetic lives in plain C
 patterns (``uint16``) to it.  The tolerance rule used to compare a GPU
 result with the oracle's is here too.
 
+The 2:4 structured-sparse product of the same pages' overview (section
+"高级特性超越基础矩阵乘法", ``T.gemm_sp``) is ``oracle_sparse.c``: magnitude
+compression to (values, positions) and the product on the compressed operand.
+
 Every function is pinned by the ``-m "not gpu"`` tests against facts that do
 not come from the oracle itself: numpy's own binary16 conversion, exact
-rational brute force, identity / permutation / integer cases and algebraic
-invariants.
+rational brute force, identity / permutation / integer cases, algebraic
+invariants, and (sparse) an independent numpy selection of the kept entries.
 """
 import ctypes
 import os
@@ -55,6 +59,15 @@ def _lib():
         lib.oracle_gemm_f16_sampled.argtypes = [i64, i64, i64, u16p, u16p, i64p, i64, i64p, i64,
                                                 ctypes.c_int, u16p, ctypes.c_int]
         lib.oracle_gemm_f16_sampled.restype = ctypes.c_int
+        lib.oracle_sp_compress.argtypes = [i64, i64, u16p, u16p, u16p]
+        lib.oracle_sp_compress.restype = ctypes.c_int
+        lib.oracle_sp_decompress.argtypes = [i64, i64, u16p, u16p, u16p]
+        lib.oracle_sp_decompress.restype = ctypes.c_int
+        lib.oracle_gemm_f16_sp.argtypes = [i64, i64, i64, u16p, u16p, u16p, ctypes.c_int, u16p, ctypes.c_int]
+        lib.oracle_gemm_f16_sp.restype = ctypes.c_int
+        lib.oracle_gemm_f16_sp_sampled.argtypes = [i64, i64, i64, u16p, u16p, u16p, i64p, i64, i64p, i64,
+                                                   ctypes.c_int, u16p, ctypes.c_int]
+        lib.oracle_gemm_f16_sp_sampled.restype = ctypes.c_int
         _LIB = lib
     return _LIB
 
@@ -134,6 +147,84 @@ def gemm_sampled(A, B, rows, cols, relu: bool = False, threads: int = 0) -> np.n
                                         int(bool(relu)), _ptr(C, ctypes.c_uint16), int(threads))
     if rc != 0:
         raise RuntimeError("oracle_gemm_f16_sampled failed (bad index or allocation failure)")
+    return C
+
+
+# ---- 2:4 structured sparsity (oracle_sparse.c) ------------------------------
+# A (M x K, K % 16 == 0) is kept as vals (M x K/2 binary16, the 2 kept values
+# of every group of 4 k in increasing position order) and meta (M x K/16
+# uint16: bits 2s+1..2s of word w give the position in its group of kept
+# value s of dense k 16w .. 16w+15).  See the C file's header for the reading
+# of the pages this follows.
+
+def _u16(x, name):
+    x = np.asarray(x)
+    if x.dtype != np.uint16:
+        raise TypeError(f"{name}: expected uint16, got {x.dtype}")
+    return np.ascontiguousarray(x)
+
+
+def sp_compress(A):
+    """(vals, meta) of the 2:4 compression of A: per group of 4 k, the 2
+    entries of largest magnitude (ties: lower position)."""
+    A = _as_bits(A, "A")
+    M, K = A.shape
+    vals = np.zeros((M, K // 2), dtype=np.uint16)
+    meta = np.zeros((M, K // 16), dtype=np.uint16)
+    if _lib().oracle_sp_compress(M, K, _ptr(A, ctypes.c_uint16), _ptr(vals, ctypes.c_uint16),
+                                 _ptr(meta, ctypes.c_uint16)) != 0:
+        raise ValueError(f"K = {K} is not a multiple of 16")
+    return vals, meta
+
+
+def sp_decompress(vals, meta):
+    """The dense matrix (binary16 bits) a compressed operand stands for."""
+    vals = _as_bits(vals, "vals")
+    meta = _u16(meta, "meta")
+    M, K = vals.shape[0], 2 * vals.shape[1]
+    if meta.shape != (M, K // 16):
+        raise ValueError(f"meta shape {meta.shape}, expected {(M, K // 16)}")
+    A = np.zeros((M, K), dtype=np.uint16)
+    if _lib().oracle_sp_decompress(M, K, _ptr(vals, ctypes.c_uint16), _ptr(meta, ctypes.c_uint16),
+                                   _ptr(A, ctypes.c_uint16)) != 0:
+        raise ValueError("bad K or a group naming one position twice")
+    return A
+
+
+def gemm_sp(vals, meta, B, relu: bool = False, threads: int = 0) -> np.ndarray:
+    """C = rne16(epi(A . B)) for a compressed 2:4-sparse A; returns uint16 (M x N)."""
+    vals = _as_bits(vals, "vals")
+    meta = _u16(meta, "meta")
+    B = _as_bits(B, "B")
+    M, K = vals.shape[0], 2 * vals.shape[1]
+    if meta.shape != (M, K // 16) or B.shape[0] != K:
+        raise ValueError(f"shape mismatch: vals {vals.shape}, meta {meta.shape}, B {B.shape}")
+    N = B.shape[1]
+    C = np.zeros((M, N), dtype=np.uint16)
+    if _lib().oracle_gemm_f16_sp(M, N, K, _ptr(vals, ctypes.c_uint16), _ptr(meta, ctypes.c_uint16),
+                                 _ptr(B, ctypes.c_uint16), int(bool(relu)), _ptr(C, ctypes.c_uint16),
+                                 int(threads)) != 0:
+        raise RuntimeError("oracle_gemm_f16_sp failed")
+    return C
+
+
+def gemm_sp_sampled(vals, meta, B, rows, cols, relu: bool = False, threads: int = 0) -> np.ndarray:
+    """The block C[rows x cols] of the sparse product; returns uint16."""
+    vals = _as_bits(vals, "vals")
+    meta = _u16(meta, "meta")
+    B = _as_bits(B, "B")
+    M, K = vals.shape[0], 2 * vals.shape[1]
+    if meta.shape != (M, K // 16) or B.shape[0] != K:
+        raise ValueError(f"shape mismatch: vals {vals.shape}, meta {meta.shape}, B {B.shape}")
+    N = B.shape[1]
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    cols = np.ascontiguousarray(np.asarray(cols, dtype=np.int64))
+    C = np.zeros((rows.size, cols.size), dtype=np.uint16)
+    if _lib().oracle_gemm_f16_sp_sampled(M, N, K, _ptr(vals, ctypes.c_uint16), _ptr(meta, ctypes.c_uint16),
+                                         _ptr(B, ctypes.c_uint16), _ptr(rows, ctypes.c_int64), rows.size,
+                                         _ptr(cols, ctypes.c_int64), cols.size, int(bool(relu)),
+                                         _ptr(C, ctypes.c_uint16), int(threads)) != 0:
+        raise RuntimeError("oracle_gemm_f16_sp_sampled failed (bad index or allocation failure)")
     return C
 
 

@@ -8,11 +8,12 @@ import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "oracle_gemm.c")
+SRCS = [SRC, os.path.join(HERE, "oracle_sparse.c")]
 LIB = os.path.join(HERE, "liboracle_gemm.so")
 
 
 def build(verbose: bool = False) -> str:
-    """Compile oracle_gemm.c into liboracle_gemm.so and return its path.
+    """Compile oracle_gemm.c and oracle_sparse.c into liboracle_gemm.so and return its path.
 
     -O2 without -ffast-math keeps IEEE semantics: every element's sum stays
     sequential in k.  -ffp-contract=off is stated for clarity only (products
@@ -21,7 +22,7 @@ def build(verbose: bool = False) -> str:
     """
     tmp = LIB + ".tmp"
     cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
-           "-fno-fast-math", "-Wall", "-Wextra", "-o", tmp, SRC, "-lm", "-lpthread"]
+           "-fno-fast-math", "-Wall", "-Wextra", "-o", tmp, *SRCS, "-lm", "-lpthread"]
     if verbose:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)
