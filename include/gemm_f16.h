@@ -187,6 +187,48 @@ gemm_f16_status_t gemm_f16_split(int64_t M, int64_t N, int64_t K,
  */
 gemm_f16_status_t gemm_f16_release_workspaces(void);
 
+/*
+ * 2:4 structured-sparse A.  The pages name 2:4 sparse GEMM (`T.gemm_sp`)
+ * among TileLang's features ("TileLang：让GPU编程像Python一样简单的高性能计算
+ * 新范式", section "高级特性超越基础矩阵乘法") without a storage format; this
+ * library's format, matched to gfx950's v_smfmac_f32_32x32x32_f16:
+ *   vals : M x K/2 binary16, row-major: in every aligned group of 4
+ *          consecutive k of a row, the 2 kept values in position order.
+ *   meta : M x K/16 uint16, row-major: word w of a row covers k = 16w ..
+ *          16w+15; bits 2s+1..2s give the position (0..3) inside group
+ *          4w + s/2 of kept value s (s = 0..7), i.e. vals[i][8w + s] sits at
+ *          k = 16w + 4 (s/2) + position.
+ * K must be a multiple of 16.
+ */
+
+/*
+ * Compress A (M x K binary16, row-major, on the device) into vals and meta
+ * (device buffers of M*K/2 halves and M*K/16 words, caller-owned, not
+ * overlapping A or each other): in each group of 4 the 2 entries of largest
+ * magnitude are kept (magnitudes compared exactly; ties: lower position).
+ * An already 2:4-sparse A is kept exactly.  Asynchronous on `stream`.
+ * K % 16 != 0 or a negative dimension: GEMM_F16_ERROR_INVALID_VALUE;
+ * odd pointers: GEMM_F16_ERROR_MISALIGNED.
+ */
+gemm_f16_status_t gemm_f16_sp_compress(int64_t M, int64_t K, const void *A, void *vals, void *meta,
+                                       void *stream);
+
+/*
+ * C = epi(A . B) with A given as (vals, meta) above, B K x N and C M x N
+ * binary16 row-major.  Products of kept values accumulate in fp32; one RNE
+ * rounding to binary16 at the end, as gemm_f16.
+ *   config : GEMM_F16_CONFIG_AUTO or an index < gemm_f16_sp_num_configs().
+ * Requirements: K % 16 == 0 (else INVALID_VALUE); vals and B 16-byte
+ * aligned and N % 8 == 0, meta and C 2-byte aligned (else MISALIGNED);
+ * C must not overlap vals, meta or B.  Other rules as gemm_f16.
+ */
+gemm_f16_status_t gemm_f16_sp(int64_t M, int64_t N, int64_t K, const void *vals, const void *meta,
+                              const void *B, void *C, int epilogue, int config, void *stream);
+
+/* Number and names of the sparse kernel configurations. */
+int gemm_f16_sp_num_configs(void);
+const char *gemm_f16_sp_config_name(int config);
+
 /* How a call would run; filled by gemm_f16_plan without any HIP call. */
 typedef struct gemm_f16_plan {
     int32_t config;        /* configuration index actually chosen */
@@ -227,6 +269,12 @@ gemm_f16_status_t gemm_f16_plan(int64_t M, int64_t N, int64_t K,
 gemm_f16_status_t gemm_f16_plan_trans(int64_t M, int64_t N, int64_t K,
                                       const void *A, int trans_a, const void *B, int trans_b,
                                       const void *C, int config, gemm_f16_plan_t *plan);
+
+/* As gemm_f16_plan, for gemm_f16_sp (config indexes the sparse list; flops
+ * counts the products of kept values, M N K; lds_bytes the compressed A and
+ * the B stages). */
+gemm_f16_status_t gemm_f16_plan_sp(int64_t M, int64_t N, int64_t K, const void *vals, const void *meta,
+                                   const void *B, const void *C, int config, gemm_f16_plan_t *plan);
 
 /* As gemm_f16_plan_trans, for gemm_f16_split with the given split request. */
 gemm_f16_status_t gemm_f16_plan_split(int64_t M, int64_t N, int64_t K,

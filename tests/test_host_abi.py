@@ -294,3 +294,27 @@ def test_split_workspace_validation_before_any_launch():
     assert _split_call(WS, need, splits=65) == 1              # split count beyond the maximum
     # (valid arguments are not tried here: on a GPU host they would launch
     # on these stand-in addresses)
+
+
+def test_sparse_argument_checks_before_any_launch():
+    sp = g.lib().gemm_f16_sp
+    V, Mt, B, C = FAKE, FAKE * 4, FAKE * 8, FAKE * 12
+    assert sp(64, 64, 40, V, Mt, B, C, 0, -1, None) == 1            # K % 16 != 0
+    assert sp(64, 64, 48, V + 8, Mt, B, C, 0, -1, None) == 2        # vals not 16-byte aligned
+    assert sp(64, 60, 48, V, Mt, B, C, 0, -1, None) == 2            # N % 8 != 0
+    assert sp(64, 64, 48, V, Mt + 1, B, C, 0, -1, None) == 2        # odd meta pointer
+    assert sp(64, 64, 48, V, 0, B, C, 0, -1, None) == 1             # no meta
+    assert sp(64, 64, 48, V, Mt, B, V, 0, -1, None) == 1            # C overlaps vals
+    assert sp(64, 64, 48, V, Mt, B, C, 2, -1, None) == 1            # unknown epilogue
+    assert sp(64, 64, 48, V, Mt, B, C, 0, g.sp_num_configs(), None) == 1
+    assert sp(0, 64, 48, V, Mt, B, C, 0, -1, None) == 0             # empty: no launch
+    assert g.lib().gemm_f16_sp_compress(4, 24, FAKE, V, Mt, None) == 1
+    assert g.lib().gemm_f16_sp_compress(4, 32, FAKE + 1, V, Mt, None) == 2
+    assert g.lib().gemm_f16_sp_compress(0, 32, 0, 0, 0, None) == 0
+    names = [g.sp_config_name(c) for c in range(g.sp_num_configs())]
+    assert all(names) and len(set(names)) == len(names) and g.sp_config_name(-1) is None
+    p = g.plan_sp(4096, 4096, 4096, FAKE, FAKE, FAKE, FAKE)
+    assert p["flops"] == 4096.0 ** 3 and p["lds_bytes"] <= 163840
+    for c in range(g.sp_num_configs()):
+        q = g.plan_sp(300, 264, 1008, FAKE, FAKE, FAKE, FAKE, config=c)
+        assert q["config"] == c and q["grid"] == q["tiles_m"] * q["tiles_n"]

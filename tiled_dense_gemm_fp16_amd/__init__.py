@@ -57,6 +57,11 @@ SIGNATURES = {
     "gemm_f16_plan_trans": ([_i64, _i64, _i64, _vp, _int, _vp, _int, _vp, _int, ctypes.POINTER(Plan)], _int),
     "gemm_f16_plan_split": ([_i64, _i64, _i64, _vp, _int, _vp, _int, _vp, _int, _int, ctypes.POINTER(Plan)],
                             _int),
+    "gemm_f16_sp_compress": ([_i64, _i64, _vp, _vp, _vp, _vp], _int),
+    "gemm_f16_sp": ([_i64, _i64, _i64, _vp, _vp, _vp, _vp, _int, _int, _vp], _int),
+    "gemm_f16_plan_sp": ([_i64, _i64, _i64, _vp, _vp, _vp, _vp, _int, ctypes.POINTER(Plan)], _int),
+    "gemm_f16_sp_num_configs": ([], _int),
+    "gemm_f16_sp_config_name": ([_int], ctypes.c_char_p),
     "gemm_f16_num_configs": ([], _int),
     "gemm_f16_config_name": ([_int], ctypes.c_char_p),
     "gemm_f16_stage_bytes": ([_i64, _i64, _i64, _i64], _i64),
@@ -199,6 +204,83 @@ def gemm(a, b, epilogue: str = "none", out=None, config: int = CONFIG_AUTO, stre
                                       ws_bytes, stream.cuda_stream or None)
     if st != SUCCESS:
         raise GemmError(st, "gemm_f16")
+    return out
+
+
+# ---- 2:4 structured-sparse A (gemm_f16_sp*, see include/gemm_f16.h) --------
+
+def sp_num_configs() -> int:
+    return int(lib().gemm_f16_sp_num_configs())
+
+
+def sp_config_name(config: int) -> str | None:
+    s = lib().gemm_f16_sp_config_name(int(config))
+    return s.decode() if s is not None else None
+
+
+def plan_sp(M: int, N: int, K: int, vals_ptr: int = 0, meta_ptr: int = 0, B_ptr: int = 0, C_ptr: int = 0,
+            config: int = CONFIG_AUTO) -> dict:
+    """How gemm_f16_sp would run this shape (host logic only)."""
+    p = Plan()
+    st = lib().gemm_f16_plan_sp(M, N, K, vals_ptr or None, meta_ptr or None, B_ptr or None, C_ptr or None,
+                                config, ctypes.byref(p))
+    if st != SUCCESS:
+        raise GemmError(st, "gemm_f16_plan_sp")
+    return p.as_dict()
+
+
+def _check_gpu_2d(t, name, dtype):
+    import torch
+
+    if not isinstance(t, torch.Tensor) or t.dtype != dtype or t.dim() != 2:
+        raise ValueError(f"{name} must be a 2-D {dtype} tensor")
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous GPU tensor")
+
+
+def sp_compress(a, stream=None):
+    """(vals, meta) for a (M x K float16 GPU tensor, K % 16 == 0): vals is
+    M x K/2 float16, meta M x K/16 int16 (the uint16 words' bits)."""
+    import torch
+
+    _check_gpu_2d(a, "a", torch.float16)
+    M, K = a.shape
+    vals = torch.empty((M, K // 2), dtype=torch.float16, device=a.device)
+    meta = torch.empty((M, K // 16), dtype=torch.int16, device=a.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(a.device)
+    with torch.cuda.device(a.device):
+        st = lib().gemm_f16_sp_compress(M, K, a.data_ptr() or None, vals.data_ptr() or None,
+                                        meta.data_ptr() or None, stream.cuda_stream or None)
+    if st != SUCCESS:
+        raise GemmError(st, "gemm_f16_sp_compress")
+    return vals, meta
+
+
+def gemm_sp(vals, meta, b, epilogue: str = "none", out=None, config: int = CONFIG_AUTO, stream=None):
+    """C = epi(A @ b) for a 2:4-sparse A given as (vals, meta) from sp_compress."""
+    import torch
+
+    if epilogue not in _EPILOGUES:
+        raise ValueError(f"epilogue must be one of {sorted(_EPILOGUES)}, got {epilogue!r}")
+    _check_gpu_2d(vals, "vals", torch.float16)
+    _check_gpu_2d(meta, "meta", torch.int16)
+    _check_gpu_2d(b, "b", torch.float16)
+    M, K = vals.shape[0], 2 * vals.shape[1]
+    if tuple(meta.shape) != (M, K // 16) or b.shape[0] != K:
+        raise ValueError(f"shape mismatch: vals {tuple(vals.shape)}, meta {tuple(meta.shape)}, b {tuple(b.shape)}")
+    N = b.shape[1]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=b.device)
+    elif out.dtype != torch.float16 or tuple(out.shape) != (M, N) or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous float16 tensor of shape {(M, N)}")
+    if stream is None:
+        stream = torch.cuda.current_stream(b.device)
+    with torch.cuda.device(b.device):
+        st = lib().gemm_f16_sp(M, N, K, vals.data_ptr() or None, meta.data_ptr() or None, b.data_ptr() or None,
+                               out.data_ptr() or None, _EPILOGUES[epilogue], config, stream.cuda_stream or None)
+    if st != SUCCESS:
+        raise GemmError(st, "gemm_f16_sp")
     return out
 
 

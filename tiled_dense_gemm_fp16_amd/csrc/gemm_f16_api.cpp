@@ -33,6 +33,13 @@ const ConfigDesc kConfigs[kNumConfigs] = {
     {"256x128x64_s2_staged", 256, 128, 64, 2, 4, false, 4, false, 1},
 };
 
+// Sparse configurations (2:4 A): fields as above; every one takes A as
+// compressed values + positions and B as K x N.
+const ConfigDesc kSpConfigs[kNumSpConfigs] = {
+    {"sp_256x256x64_s3_w8", 256, 256, 64, 3, 8, true, 8, false, 1},
+    {"sp_128x128x64_s3", 128, 128, 64, 3, 4, true, 8, false, 1},
+};
+
 namespace {
 
 constexpr int kComputeUnits = 256;   // MI355X
@@ -425,6 +432,7 @@ gemm_f16_status_t launch_plan(const gemm_f16_plan_t &plan, int64_t M, int64_t N,
     a.vec_c = plan.vec_c;
     a.k_split = (int)plan.k_split;
     a.W = plan.splits > 1 ? (float *)W : nullptr;
+    a.meta = nullptr;
     hipError_t e = launch(plan.config, a, plan.vec_a, plan.vec_b, ta, tb, plan.grid, s);
     if (e == hipSuccess && plan.splits > 1)
         e = launch_reduce((const float *)W, (_Float16 *)C, M, N, plan.splits, a.relu, plan.vec_c >= 4, s);
@@ -479,6 +487,79 @@ gemm_f16_status_t run(int64_t M, int64_t N, int64_t K, const void *A, bool ta, c
         return st;
     }
     return launch_plan(plan, M, N, K, A, ta, B, tb, C, epilogue, w, s);
+}
+
+// ---- 2:4 structured-sparse A -------------------------------------------------
+
+gemm_f16_status_t validate_sp(int64_t M, int64_t N, int64_t K, const void *vals, const void *meta, const void *B,
+                              const void *C, bool check_c_overlap)
+{
+    if (M < 0 || N < 0 || K < 0 || K % 16 != 0)
+        return GEMM_F16_ERROR_INVALID_VALUE;
+    if (M > GEMM_F16_MAX_DIM || N > GEMM_F16_MAX_N || K > GEMM_F16_MAX_K)
+        return GEMM_F16_ERROR_UNSUPPORTED_SIZE;
+    const bool a_nonempty = M > 0 && K > 0, b_nonempty = K > 0 && N > 0, c_nonempty = M > 0 && N > 0;
+    if ((a_nonempty && (!vals || !meta)) || (b_nonempty && !B) || (c_nonempty && !C))
+        return GEMM_F16_ERROR_INVALID_VALUE;
+    // 16-byte loads of the compressed values and of B: rows of K/2 (K % 16 == 0)
+    // and N halves; the position words and C need 2 bytes
+    if ((a_nonempty && (uintptr_t)vals % 16) || (b_nonempty && ((uintptr_t)B % 16 || N % 8)) ||
+        ((uintptr_t)meta | (uintptr_t)C) & 1u)
+        return GEMM_F16_ERROR_MISALIGNED;
+    if (check_c_overlap && c_nonempty &&
+        (overlaps(C, 2 * M * N, vals, a_nonempty ? M * K : 0) ||
+         overlaps(C, 2 * M * N, meta, a_nonempty ? M * K / 8 : 0) ||
+         overlaps(C, 2 * M * N, B, b_nonempty ? 2 * K * N : 0)))
+        return GEMM_F16_ERROR_INVALID_VALUE;
+    return GEMM_F16_SUCCESS;
+}
+
+// Relative per-workgroup throughput of the sparse tiles (ranking only).
+double sp_config_efficiency(int c) { return c == 0 ? 1.0 : 0.76; }
+
+gemm_f16_status_t make_plan_sp(int64_t M, int64_t N, int64_t K, int config, gemm_f16_plan_t *p)
+{
+    if (config != GEMM_F16_CONFIG_AUTO && (config < 0 || config >= kNumSpConfigs))
+        return GEMM_F16_ERROR_INVALID_VALUE;
+    int c = config;
+    if (c == GEMM_F16_CONFIG_AUTO) {
+        double best_t = 0.0;
+        for (int i = 0; i < kNumSpConfigs; ++i) {
+            const ConfigDesc &d = kSpConfigs[i];
+            const double rounds = (double)ceil_div(ceil_div(M, d.block_m) * ceil_div(N, d.block_n), kComputeUnits);
+            const double t = rounds * (double)d.block_m * (double)d.block_n / sp_config_efficiency(i);
+            if (c < 0 || t < best_t * 0.999) {
+                c = i;
+                best_t = t;
+            }
+        }
+    }
+    const ConfigDesc &d = kSpConfigs[c];
+    memset(p, 0, sizeof(*p));
+    p->config = c;
+    p->block_m = d.block_m;
+    p->block_n = d.block_n;
+    p->block_k = d.block_k;
+    p->stages = d.stages;
+    p->threads = 64 * d.waves;
+    p->direct_lds = 1;
+    p->vec_a = 8;
+    p->vec_b = 8;
+    p->vec_c = 1;
+    p->tiles_m = ceil_div(M, d.block_m);
+    p->tiles_n = ceil_div(N, d.block_n);
+    p->grid = p->tiles_m * p->tiles_n;
+    p->k_tiles = ceil_div(K, d.block_k);
+    // LDS: the compressed A tile (bK/2 columns) and the B tile per stage
+    p->lds_bytes = gemm_f16_stage_bytes(d.block_m, 0, d.block_k / 2, d.stages) +
+                   gemm_f16_stage_bytes(0, d.block_n, d.block_k, d.stages);
+    p->flops = (double)M * (double)N * (double)K;   // 2 M N (K/2): products of kept values
+    p->min_bytes = (double)M * K + (double)M * K / 8 + 2.0 * ((double)K * N + (double)M * N);
+    p->splits = 1;
+    p->k_split = K;
+    if (p->grid > 0x7fffffff)
+        return GEMM_F16_ERROR_UNSUPPORTED_SIZE;
+    return GEMM_F16_SUCCESS;
 }
 
 } // namespace
@@ -545,6 +626,88 @@ gemm_f16_status_t gemm_f16_plan_split(int64_t M, int64_t N, int64_t K, const voi
     if (st != GEMM_F16_SUCCESS)
         return st;
     return make_plan(M, N, K, A, trans_a != 0, B, trans_b != 0, C, config, splits, plan);
+}
+
+gemm_f16_status_t gemm_f16_sp_compress(int64_t M, int64_t K, const void *A, void *vals, void *meta, void *stream)
+{
+    if (M < 0 || K < 0 || K % 16 != 0)
+        return GEMM_F16_ERROR_INVALID_VALUE;
+    if (M > GEMM_F16_MAX_DIM || K > GEMM_F16_MAX_K)
+        return GEMM_F16_ERROR_UNSUPPORTED_SIZE;
+    if (M == 0 || K == 0)
+        return GEMM_F16_SUCCESS;
+    if (!A || !vals || !meta)
+        return GEMM_F16_ERROR_INVALID_VALUE;
+    if (((uintptr_t)A | (uintptr_t)vals | (uintptr_t)meta) & 1u)
+        return GEMM_F16_ERROR_MISALIGNED;
+    if (overlaps(vals, M * K, A, 2 * M * K) || overlaps(meta, M * K / 8, A, 2 * M * K) ||
+        overlaps(meta, M * K / 8, vals, M * K))
+        return GEMM_F16_ERROR_INVALID_VALUE;
+    int dev = -1;
+    gemm_f16_status_t st = check_device(&dev);
+    if (st != GEMM_F16_SUCCESS)
+        return st;
+    const bool vec = (uintptr_t)A % 16 == 0 && (uintptr_t)vals % 16 == 0;
+    hipError_t e = launch_sp_compress((const _Float16 *)A, (_Float16 *)vals, (uint16_t *)meta, M, K, vec,
+                                      (hipStream_t)stream);
+    return e == hipSuccess ? GEMM_F16_SUCCESS : GEMM_F16_ERROR_LAUNCH_FAILED;
+}
+
+gemm_f16_status_t gemm_f16_plan_sp(int64_t M, int64_t N, int64_t K, const void *vals, const void *meta,
+                                   const void *B, const void *C, int config, gemm_f16_plan_t *plan)
+{
+    if (!plan)
+        return GEMM_F16_ERROR_INVALID_VALUE;
+    gemm_f16_status_t st = validate_sp(M, N, K, vals, meta, B, C, false);
+    if (st != GEMM_F16_SUCCESS)
+        return st;
+    return make_plan_sp(M, N, K, config, plan);
+}
+
+gemm_f16_status_t gemm_f16_sp(int64_t M, int64_t N, int64_t K, const void *vals, const void *meta, const void *B,
+                              void *C, int epilogue, int config, void *stream)
+{
+    gemm_f16_status_t st = validate_sp(M, N, K, vals, meta, B, C, true);
+    if (st != GEMM_F16_SUCCESS)
+        return st;
+    if (epilogue != GEMM_F16_EPILOGUE_NONE && epilogue != GEMM_F16_EPILOGUE_RELU)
+        return GEMM_F16_ERROR_INVALID_VALUE;
+    gemm_f16_plan_t plan;
+    st = make_plan_sp(M, N, K, config, &plan);
+    if (st != GEMM_F16_SUCCESS)
+        return st;
+    if (M == 0 || N == 0)
+        return GEMM_F16_SUCCESS;
+    int dev = -1;
+    st = check_device(&dev);
+    if (st != GEMM_F16_SUCCESS)
+        return st;
+    KernelArgs a;
+    a.A = (const _Float16 *)vals;
+    a.B = (const _Float16 *)B;
+    a.C = (_Float16 *)C;
+    a.M = (int)M;
+    a.N = (int)N;
+    a.K = (int)K;
+    a.tiles_m = (int)plan.tiles_m;
+    a.tiles_n = (int)plan.tiles_n;
+    a.group_m = GEMM_F16_GROUP_M;
+    a.relu = epilogue == GEMM_F16_EPILOGUE_RELU ? 1 : 0;
+    a.vec_c = 1;
+    a.k_split = (int)K;
+    a.W = nullptr;
+    a.meta = (const uint16_t *)meta;
+    hipError_t e = launch_sparse(plan.config, a, plan.grid, (hipStream_t)stream);
+    return e == hipSuccess ? GEMM_F16_SUCCESS : GEMM_F16_ERROR_LAUNCH_FAILED;
+}
+
+int gemm_f16_sp_num_configs(void) { return kNumSpConfigs; }
+
+const char *gemm_f16_sp_config_name(int config)
+{
+    if (config < 0 || config >= kNumSpConfigs)
+        return nullptr;
+    return kSpConfigs[config].name;
 }
 
 gemm_f16_status_t gemm_f16_release_workspaces(void)

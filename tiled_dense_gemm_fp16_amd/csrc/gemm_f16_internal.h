@@ -22,6 +22,7 @@ struct KernelArgs {
                          // 4: 8-byte stores; 1: 2-byte stores
     int k_split;         // K elements per workgroup (a multiple of the tile depth); >= K unless split
     float *W;            // split-K: splits x M x N fp32 partial sums (written instead of C); else null
+    const uint16_t *meta;  // sparse A: M x K/16 position words (A then holds the M x K/2 kept values)
 };
 
 // Static description of one compiled kernel configuration.
@@ -46,6 +47,16 @@ extern const ConfigDesc kConfigs[kNumConfigs];
 // launch status.
 hipError_t launch(int config, const KernelArgs &a, int va, int vb, bool trans_a, bool trans_b, int64_t grid,
                   hipStream_t s);
+
+// 2:4 sparse A: compress M x K (K % 16 == 0) to vals (M x K/2) and meta
+// (M x K/16 words); vec: A and vals 16-byte aligned.
+hipError_t launch_sp_compress(const _Float16 *A, _Float16 *vals, uint16_t *meta, int64_t M, int64_t K, bool vec,
+                              hipStream_t s);
+
+// Sparse GEMM, configuration `config` of kSpConfigs (A = vals, a.meta set).
+constexpr int kNumSpConfigs = 2;
+extern const ConfigDesc kSpConfigs[kNumSpConfigs];
+hipError_t launch_sparse(int config, const KernelArgs &a, int64_t grid, hipStream_t s);
 
 // Split-K reduction: C = rne16(epi(W[0] + ... + W[splits-1])) over M x N
 // elements (relu: 1 for the ReLU epilogue).  vec4: N % 4 == 0, C 8-byte and

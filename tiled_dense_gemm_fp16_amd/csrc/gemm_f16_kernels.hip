@@ -58,6 +58,7 @@ namespace gemm_f16_impl {
 
 typedef _Float16 half_t;
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half16 __attribute__((ext_vector_type(16)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef short short4v __attribute__((ext_vector_type(4)));
 typedef float float16v __attribute__((ext_vector_type(16)));
@@ -383,8 +384,12 @@ struct Operand {
 };
 
 // ---- the kernel -------------------------------------------------------------
+// SPARSE: A is 2:4 structured-sparse, given as compressed values (M x K/2,
+// staged like a k-rows operand of BK/2 columns per tile) and positions
+// (M x K/16 uint16 words, loaded straight into registers); the product uses
+// v_smfmac_f32_32x32x32_f16, 32 k per step.
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool DIRECT, int VA, int VB, bool A_ROWS_K,
-          bool B_ROWS_K>
+          bool B_ROWS_K, bool SPARSE = false>
 struct Tile {
     static constexpr int kWaves = WM * WN;           // 4 (one per SIMD) or 8 (two per SIMD)
     static constexpr int kThreads = 64 * kWaves;
@@ -394,14 +399,17 @@ struct Tile {
     static constexpr int TM = WTM / 32;              // 32x32 MFMA blocks per wave along m
     static constexpr int TN = WTN / 32;              // ... along n
     static_assert(TM >= 1 && TN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
-    static_assert(BK % 16 == 0, "BK multiple of the MFMA depth");
-    using OpA = Operand<A_ROWS_K, BM, BK, kThreads, DIRECT, VA>;
+    static constexpr int KSTEP = SPARSE ? 32 : 16;    // k per MFMA step
+    static_assert(BK % (2 * KSTEP) == 0, "an even number of MFMA steps per tile");
+    static_assert(!SPARSE || (A_ROWS_K && DIRECT), "sparse A: compressed rows, direct loads");
+    using OpA = Operand<A_ROWS_K, BM, SPARSE ? BK / 2 : BK, kThreads, DIRECT, VA>;
     using OpB = Operand<B_ROWS_K, BN, BK, kThreads, DIRECT, VB>;
     static constexpr int A_STAGE = OpA::STAGE;
     static constexpr int B_STAGE = OpB::STAGE;
     static constexpr int LDS_BYTES = STAGES * (A_STAGE + B_STAGE) * 2;
     static_assert(LDS_BYTES <= 163840, "LDS budget");
-    static constexpr int LOADS_PER_TILE = OpA::LOADS + OpB::LOADS;
+    static constexpr int META_LOADS = SPARSE ? TM * (BK / 32) : 0;   // position words per lane per tile
+    static constexpr int LOADS_PER_TILE = OpA::LOADS + OpB::LOADS + META_LOADS;
 };
 
 // SPREAD (direct kernels): the loads of the tile requested during a step are
@@ -409,12 +417,12 @@ struct Tile {
 // do not queue a whole tile of loads ahead of their MFMAs at once (measured:
 // +3 % for 256x256 tiles with 4 waves, +6-8 % for 128x128; -2 % with 8 waves).
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool DIRECT, int VA, int VB, bool A_ROWS_K,
-          bool B_ROWS_K, bool SPREAD = false>
+          bool B_ROWS_K, bool SPREAD = false, bool SPARSE = false>
 __global__ void __launch_bounds__(64 * WM * WN)
 __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4)))
 gemm_f16_kernel(KernelArgs args)
 {
-    using T = Tile<BM, BN, BK, WM, WN, STAGES, DIRECT, VA, VB, A_ROWS_K, B_ROWS_K>;
+    using T = Tile<BM, BN, BK, WM, WN, STAGES, DIRECT, VA, VB, A_ROWS_K, B_ROWS_K, SPARSE>;
     __shared__ __attribute__((aligned(1024))) half_t lds[T::LDS_BYTES / 2];
     half_t *const As = lds;                                  // STAGES A stages
     half_t *const Bs = lds + STAGES * T::A_STAGE;            // STAGES B stages
@@ -436,13 +444,54 @@ gemm_f16_kernel(KernelArgs args)
     const int nk = (k_end - k_begin + BK - 1) / BK;
 
     // A is M x K (lda = K) or, given transposed, K x M (lda = M); B is K x N
-    // (ldb = N) or, given transposed, N x K (ldb = K).
+    // (ldb = N) or, given transposed, N x K (ldb = K).  Sparse A: the
+    // compressed values, M x K/2, addressed in compressed columns.
     typename T::OpA opa;
     typename T::OpB opb;
-    opa.init(args.A, A_ROWS_K ? K : M, m0, M, k_begin, k_end, tid, wave, lane);
+    if constexpr (SPARSE)
+        opa.init(args.A, K / 2, m0, M, k_begin / 2, k_end / 2, tid, wave, lane);
+    else
+        opa.init(args.A, A_ROWS_K ? K : M, m0, M, k_begin, k_end, tid, wave, lane);
     opb.init(args.B, B_ROWS_K ? K : N, n0, N, k_begin, k_end, tid, wave, lane);
 
-    auto issue_loads = [&](int kt, half_t *dst_a, half_t *dst_b, int part = 0, int nparts = 1) {
+    // Sparse A's positions: lane l of fragment i (row wm0 + 32 i + l % 32)
+    // uses, in MFMA step ks of tile kt, the word of its half l / 32 of those
+    // 32 k: word (k_begin + kt BK) / 16 + 2 ks + l / 32 of its row.  They are
+    // loaded with each tile's operands (before them, so that the waits for a
+    // tile cover its words too) into slot kt % STAGES.
+    constexpr int NSTEP = BK / T::KSTEP;
+    constexpr int MSLOTS = SPARSE ? STAGES : 1;
+    uint32_t meta[MSLOTS][T::TM][SPARSE ? NSTEP : 1];
+    const int kwords = K / 16;
+    const __amdgpu_buffer_rsrc_t meta_rsrc =
+        make_rsrc(SPARSE ? args.meta + (int64_t)m0 * kwords : args.meta,
+                  SPARSE ? (uint32_t)min(BM, M - m0) * (uint32_t)kwords * 2u : 0u);
+    uint32_t meta_off[T::TM];
+    if constexpr (SPARSE) {
+#pragma unroll
+        for (int i = 0; i < T::TM; ++i)
+            meta_off[i] = ((uint32_t)(wm0 + 32 * i + (lane & 31)) * (uint32_t)kwords + (uint32_t)(lane >> 5)) * 2u;
+    }
+    auto issue_meta = [&](int kt, int slot) {
+        if constexpr (SPARSE) {
+#pragma unroll
+            for (int ks = 0; ks < NSTEP; ++ks) {
+                const int w = (k_begin + kt * BK) / 16 + 2 * ks;
+                const uint32_t mask = oob_unless(w + (lane >> 5) < kwords);
+#pragma unroll
+                for (int i = 0; i < T::TM; ++i)
+                    meta[slot][i][ks] = (uint32_t)(unsigned short)__builtin_amdgcn_raw_buffer_load_b16(
+                        meta_rsrc, (meta_off[i] + (uint32_t)w * 2u) | mask, 0, 0);
+            }
+        } else {
+            (void)kt;
+            (void)slot;
+        }
+    };
+
+    auto issue_loads = [&](int kt, half_t *dst_a, half_t *dst_b, int part = 0, int nparts = 1, int mslot = 0) {
+        if (part == 0)
+            issue_meta(kt, mslot);
         opa.issue(kt, dst_a, wave, part, nparts);
         opb.issue(kt, dst_b, wave, part, nparts);
     };
@@ -460,17 +509,38 @@ gemm_f16_kernel(KernelArgs args)
 
     // Fragments of one 16-deep k step: x = B^T slices (one per 32-column
     // block), y = A^T slices (one per 32-row block).
+    // Sparse: x holds 32 k of B per lane (two 16-deep fragments: k 8 h .. +7
+    // and 16 + 8 h .. +7 of the step, h = lane / 32, the order
+    // v_smfmac_f32_32x32x32_f16 pairs with A's compressed values, measured
+    // with a one-wave probe), y the 8 compressed values of A (its 16 k), and
+    // idx the positions word of each A fragment.
+    using BFrag = typename std::conditional<SPARSE, half16, half8>::type;
     struct Frags {
-        half8 x[T::TN];
+        BFrag x[T::TN];
         half8 y[T::TM];
+        uint32_t idx[SPARSE ? T::TM : 1];
     };
-    auto load_frags = [&](Frags &f, const half_t *as, const half_t *bs, int ks) {
+    auto load_frags = [&](Frags &f, const half_t *as, const half_t *bs, int ks, int mslot = 0) {
 #pragma unroll
         for (int i = 0; i < T::TM; ++i)
             f.y[i] = opa.frag(as, wm0 + 32 * i, ks, lane);
 #pragma unroll
-        for (int j = 0; j < T::TN; ++j)
-            f.x[j] = opb.frag(bs, wn0 + 32 * j, ks, lane);
+        for (int j = 0; j < T::TN; ++j) {
+            if constexpr (SPARSE) {
+                const half8 lo = opb.frag(bs, wn0 + 32 * j, 2 * ks, lane);
+                const half8 hi = opb.frag(bs, wn0 + 32 * j, 2 * ks + 1, lane);
+                f.x[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+            } else {
+                f.x[j] = opb.frag(bs, wn0 + 32 * j, ks, lane);
+            }
+        }
+        if constexpr (SPARSE) {
+#pragma unroll
+            for (int i = 0; i < T::TM; ++i)
+                f.idx[i] = meta[mslot][i][ks];
+        } else {
+            (void)mslot;
+        }
     };
     auto mma = [&](const Frags &f) {
 #pragma unroll
@@ -482,14 +552,19 @@ gemm_f16_kernel(KernelArgs args)
 #else
                 const int j = jj;
 #endif
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.x[j], f.y[i], acc[i][j], 0, 0, 0);
+                if constexpr (SPARSE)
+                    // C = A . B directly: the sparse operand must come first
+                    acc[i][j] = __builtin_amdgcn_smfmac_f32_32x32x32_f16(f.y[i], f.x[j], acc[i][j],
+                                                                          (int)f.idx[i], 0, 0);
+                else
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.x[j], f.y[i], acc[i][j], 0, 0, 0);
             }
     };
     // Ask the scheduler to alternate the MFMAs of one step with the LDS reads
     // of the next step (and, after a barrier, with the next tile's loads and
     // LDS writes), so the matrix core keeps busy while those are in flight.
     constexpr int kMfmaPerStep = T::TM * T::TN;
-    constexpr int kReadsPerStep = T::TM + 2 * T::TN;
+    constexpr int kReadsPerStep = T::TM + (SPARSE ? 4 : 2) * T::TN;
     // Reads go two per MFMA (measured: +4 % for 128x128 tiles over one per
     // MFMA, and no loss elsewhere), so that the next step's fragments are
     // requested early in the current one.
@@ -519,7 +594,7 @@ gemm_f16_kernel(KernelArgs args)
     //  staged:  registers hold tile kt+1 at the start of step kt; the step
     //           writes them to the free stage, requests tile kt+2 into the
     //           registers, then multiplies tile kt (two LDS stages suffice).
-    constexpr int NS = BK / 16;
+    constexpr int NS = BK / T::KSTEP;
     static_assert(NS % 2 == 0, "an even number of k steps per tile");
     static_assert(DIRECT || STAGES == 2, "register-staged kernels use two LDS stages");
     constexpr int LOOKAHEAD = DIRECT ? STAGES - 1 : 2;
@@ -532,25 +607,28 @@ gemm_f16_kernel(KernelArgs args)
     // reads wait for those loads or writes.
     constexpr bool SPREAD_LOADS = DIRECT && SPREAD;
     constexpr int PARTS = SPREAD_LOADS ? NS : 1;
+    // rd_slot / wr_slot: the stage indices of (rd_a, rd_b) and (wr_a, wr_b),
+    // which are also the register slots of sparse A's position words
     auto step = [&](const half_t *__restrict__ rd_a, const half_t *__restrict__ rd_b,
-                    half_t *__restrict__ wr_a, half_t *__restrict__ wr_b, int kt_next, bool pending) {
+                    half_t *__restrict__ wr_a, half_t *__restrict__ wr_b, int kt_next, bool pending,
+                    int rd_slot, int wr_slot) {
         // direct, spread: part p of the requested tile goes out with k step p
         auto issue_part = [&](int p) {
             if constexpr (SPREAD_LOADS)
-                issue_loads(kt_next, wr_a, wr_b, p, PARTS);
+                issue_loads(kt_next, wr_a, wr_b, p, PARTS, wr_slot);
         };
         if constexpr (DIRECT) {
             // past the last tile: zeros into a retired stage
             if constexpr (SPREAD_LOADS)
                 issue_part(0);
             else
-                issue_loads(kt_next, wr_a, wr_b);
+                issue_loads(kt_next, wr_a, wr_b, 0, 1, wr_slot);
         } else {
             wait_vmcnt<0>();                    // tile kt+1 is in the registers
             store_staged(wr_a, wr_b);
             issue_loads(kt_next, nullptr, nullptr);
         }
-        load_frags(f0, rd_a, rd_b, 0);
+        load_frags(f0, rd_a, rd_b, 0, rd_slot);
         if (pending)
             mma(f1);
         constexpr int PART_LOADS = T::LOADS_PER_TILE / PARTS;
@@ -559,13 +637,13 @@ gemm_f16_kernel(KernelArgs args)
 #pragma unroll
         for (int ks = 0; ks + 1 < NS; ks += 2) {
             issue_part(ks + 1);
-            load_frags(f1, rd_a, rd_b, ks + 1);
+            load_frags(f1, rd_a, rd_b, ks + 1, rd_slot);
             mma(f0);
             interleave(SPREAD_LOADS ? PART_LOADS : 0, 0);
             __builtin_amdgcn_sched_barrier(0);
             if (ks + 2 < NS) {
                 issue_part(ks + 2);
-                load_frags(f0, rd_a, rd_b, ks + 2);
+                load_frags(f0, rd_a, rd_b, ks + 2, rd_slot);
                 mma(f1);
                 interleave(SPREAD_LOADS ? PART_LOADS : 0, 0);
                 __builtin_amdgcn_sched_barrier(0);
@@ -593,7 +671,7 @@ gemm_f16_kernel(KernelArgs args)
 #pragma unroll
         for (int s = 0; s < STAGES - 1; ++s)
             if (s < nk)
-                issue_loads(s, As + s * T::A_STAGE, Bs + s * T::B_STAGE);
+                issue_loads(s, As + s * T::A_STAGE, Bs + s * T::B_STAGE, 0, 1, s);
     } else {
         if (nk > 0) {
             issue_loads(0, nullptr, nullptr);
@@ -606,7 +684,8 @@ gemm_f16_kernel(KernelArgs args)
     constexpr int W_OFF = DIRECT ? LOOKAHEAD : 1;
     if (nk > 0) {
         tile_ready(0);
-        step(As, Bs, As + (W_OFF % STAGES) * T::A_STAGE, Bs + (W_OFF % STAGES) * T::B_STAGE, LOOKAHEAD, false);
+        step(As, Bs, As + (W_OFF % STAGES) * T::A_STAGE, Bs + (W_OFF % STAGES) * T::B_STAGE, LOOKAHEAD, false,
+             0, W_OFF % STAGES);
     }
     // tiles 1 .. nk-1, unrolled so that every stage index is a constant
     for (int kt0 = 1; kt0 < nk; kt0 += STAGES) {
@@ -618,7 +697,7 @@ gemm_f16_kernel(KernelArgs args)
             if (kt < nk) {
                 tile_ready(kt);
                 step(As + s * T::A_STAGE, Bs + s * T::B_STAGE, As + w * T::A_STAGE, Bs + w * T::B_STAGE,
-                     kt + LOOKAHEAD, true);
+                     kt + LOOKAHEAD, true, s, w);
             }
         }
     }
@@ -627,6 +706,33 @@ gemm_f16_kernel(KernelArgs args)
     wait_vmcnt<0>();   // the tail's zero-filling loads must land before the workgroup retires
 
     const int c_rows = min(BM, M - m0);
+    if constexpr (SPARSE) {
+        // C = A . B was computed untransposed: lane l of block (i, j) holds
+        // column wn0 + 32 j + l % 32, rows wm0 + 32 i + 8 g + 4 (l / 32) + r
+        // in accumulator 4 g + r.  Each store writes one element; the 32
+        // lanes of a half-wave cover 64 consecutive bytes of one row.
+        half_t *c_base = args.C + (int64_t)m0 * N;
+        const __amdgpu_buffer_rsrc_t c_rsrc = make_rsrc(c_base, (uint32_t)c_rows * (uint32_t)N * 2u);
+        const bool relu = args.relu != 0;
+#pragma unroll
+        for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+            for (int j = 0; j < T::TN; ++j) {
+                const int n = n0 + wn0 + 32 * j + (lane & 31);
+                const uint32_t col_mask = oob_unless(n < N);
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int r = wm0 + 32 * i + 8 * (v / 4) + 4 * (lane >> 5) + (v % 4);
+                    float x = acc[i][j][v];
+                    if (relu)
+                        x = __builtin_fmaxf(x, 0.0f);
+                    const half_t h = (half_t)x;
+                    const uint32_t off = ((uint32_t)r * (uint32_t)N + (uint32_t)n) * 2u;
+                    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(short, h), c_rsrc, off | col_mask, 0, 0);
+                }
+            }
+        return;
+    }
     if (args.W) {
         // split-K: the fp32 partial sums of this split go to its slice of the
         // workspace (row pitch N); the reduction applies the epilogue.  When
@@ -826,13 +932,94 @@ hipError_t launch_reduce(const float *W, _Float16 *C, int64_t M, int64_t N, int 
     return hipGetLastError();
 }
 
+// ---- 2:4 compression -------------------------------------------------------------
+// One thread per 16 consecutive k of a row of A (M x K, K % 16 == 0): in
+// each group of 4 it keeps the 2 entries of largest magnitude (compared as
+// binary16 bit patterns without the sign; ties: lower position), writes
+// them in position order to vals (M x K/2) and their positions, 2 bits per
+// kept value, to one word of meta (M x K/16).  VEC: A and vals 16-byte
+// aligned (16-byte loads and stores).
+template <bool VEC>
+__global__ void __launch_bounds__(256) sp_compress_kernel(const half_t *__restrict__ A, half_t *__restrict__ vals,
+                                                          unsigned short *__restrict__ meta, int64_t words)
+{
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t w = (int64_t)blockIdx.x * 256 + threadIdx.x; w < words; w += stride) {
+        unsigned short x[16];
+        if constexpr (VEC) {
+            const int4v lo = reinterpret_cast<const int4v *>(A)[2 * w];
+            const int4v hi = reinterpret_cast<const int4v *>(A)[2 * w + 1];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                x[2 * e] = (unsigned short)((unsigned)lo[e] & 0xffffu);
+                x[2 * e + 1] = (unsigned short)((unsigned)lo[e] >> 16);
+                x[8 + 2 * e] = (unsigned short)((unsigned)hi[e] & 0xffffu);
+                x[8 + 2 * e + 1] = (unsigned short)((unsigned)hi[e] >> 16);
+            }
+        } else {
+            const unsigned short *a = reinterpret_cast<const unsigned short *>(A) + 16 * w;
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                x[e] = a[e];
+        }
+        unsigned short kept[8];
+        unsigned word = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const unsigned short *g = x + 4 * q;
+            int best = 0;
+#pragma unroll
+            for (int p = 1; p < 4; ++p)
+                if ((g[p] & 0x7fffu) > (g[best] & 0x7fffu))
+                    best = p;
+            int next = best == 0 ? 1 : 0;
+#pragma unroll
+            for (int p = 0; p < 4; ++p)
+                if (p != best && (g[p] & 0x7fffu) > (g[next] & 0x7fffu))
+                    next = p;
+            const int lo = best < next ? best : next, hi = best < next ? next : best;
+            kept[2 * q] = g[lo];
+            kept[2 * q + 1] = g[hi];
+            word |= (unsigned)lo << (4 * q);
+            word |= (unsigned)hi << (4 * q + 2);
+        }
+        if constexpr (VEC) {
+            int4v out;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                out[e] = (int)((unsigned)kept[2 * e] | ((unsigned)kept[2 * e + 1] << 16));
+            reinterpret_cast<int4v *>(vals)[w] = out;
+        } else {
+            unsigned short *v = reinterpret_cast<unsigned short *>(vals) + 8 * w;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                v[e] = kept[e];
+        }
+        meta[w] = (unsigned short)word;
+    }
+}
+
+hipError_t launch_sp_compress(const _Float16 *A, _Float16 *vals, uint16_t *meta, int64_t M, int64_t K, bool vec,
+                              hipStream_t s)
+{
+    const int64_t words = M * (K / 16);
+    const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((words + 255) / 256, 256 * 16));
+    if (vec)
+        hipLaunchKernelGGL(sp_compress_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, s, A, vals,
+                           (unsigned short *)meta, words);
+    else
+        hipLaunchKernelGGL(sp_compress_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, s, A, vals,
+                           (unsigned short *)meta, words);
+    return hipGetLastError();
+}
+
 // ---- launchers ----------------------------------------------------------------
 
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool DIRECT, int VA, int VB, bool AR, bool BR,
-          bool SPREAD = false>
+          bool SPREAD = false, bool SPARSE = false>
 static hipError_t launch_one(const KernelArgs &a, int64_t grid, hipStream_t stream)
 {
-    hipLaunchKernelGGL((gemm_f16_kernel<BM, BN, BK, WM, WN, STAGES, DIRECT, VA, VB, AR, BR, SPREAD>),
+    hipLaunchKernelGGL((gemm_f16_kernel<BM, BN, BK, WM, WN, STAGES, DIRECT, VA, VB, AR, BR, SPREAD, SPARSE>),
                        dim3((unsigned)grid), dim3(64 * WM * WN), 0, stream, a);
     return hipGetLastError();
 }
@@ -921,6 +1108,16 @@ hipError_t launch(int config, const KernelArgs &a, int va, int vb, bool trans_a,
     case 9: return launch_one<256, 256, 64, 4, 2, 2, true, 8, 8, AR, BR>(a, grid, s);
     case 10: return launch_staged_wide<256, 256, 64, 2, 4, 2, AR, BR>(a, va, vb, grid, s);
     case 11: return launch_staged_wide<256, 128, 64, 2, 2, 2, AR, BR>(a, va, vb, grid, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+// Sparse configurations (A compressed 2:4, B as K x N, 16-byte loads).
+hipError_t launch_sparse(int config, const KernelArgs &a, int64_t grid, hipStream_t s)
+{
+    switch (config) {
+    case 0: return launch_one<256, 256, 64, 2, 4, 3, true, 8, 8, true, false, false, true>(a, grid, s);
+    case 1: return launch_one<128, 128, 64, 2, 2, 3, true, 8, 8, true, false, false, true>(a, grid, s);
     default: return hipErrorInvalidValue;
     }
 }
