@@ -26,6 +26,8 @@ sys.path.insert(0, ROOT)
 
 PEAK_TFLOPS = 256 * 2.4e9 * 4096 / 1e12          # 256 CUs x 2.4 GHz x 4096 flop/clk/CU (dense FP16 MFMA)
 METRIC = "fp16 GEMM TFLOP/s at 1 MI355X and % of dense FP16 MFMA peak"
+SPARSE_METRIC = ("2:4-sparse fp16 GEMM TFLOP/s at 1 MI355X (2 flop per product of a kept value: "
+                 "M N K per call) and % of dense FP16 MFMA peak")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_8192.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "tiled_dense_gemm_fp16_amd", "csrc", f)
                   for f in ("gemm_f16_kernels.hip", "gemm_f16_internal.h", "gemm_f16_api.cpp")]
@@ -53,7 +55,7 @@ def measured_traffic(workload: str, config_name: str):
     return float(t["fetch_bytes_per_launch"]) + float(t["write_bytes_per_launch"])
 
 
-def cpu_baseline(a, b, w, budget_s: float):
+def cpu_baseline(a, b, w, budget_s: float, sparse=None):
     """Time the oracle on a seeded block of the same product (rows x columns
     of C, full K), sized to take roughly ``budget_s`` seconds."""
     import numpy as np
@@ -66,18 +68,25 @@ def cpu_baseline(a, b, w, budget_s: float):
     B = b.view(torch.int16).numpy().view(np.uint16)
     rows_all, cols_all = workloads.sample_indices(w)
     cols = cols_all.numpy()
+    if sparse is None:
+        run = lambda rows: oracle.gemm_sampled(A, B, rows, cols)          # noqa: E731
+        per_element = 2.0 * w.K
+    else:
+        vals, meta = sparse
+        run = lambda rows: oracle.gemm_sp_sampled(vals, meta, B, rows, cols)   # noqa: E731
+        per_element = 1.0 * w.K                                           # products of kept values
     # calibrate on a small block, then size the timed block
     n_cal = 128
-    oracle.gemm_sampled(A, B, rows_all[:16].numpy(), cols)            # warm the pages
+    run(rows_all[:16].numpy())                                            # warm the pages
     t0 = time.perf_counter()
-    oracle.gemm_sampled(A, B, rows_all[:n_cal].numpy(), cols)
+    run(rows_all[:n_cal].numpy())
     t_cal = max(time.perf_counter() - t0, 1e-3)
     n_rows = int(min(len(rows_all), max(n_cal, n_cal * budget_s / t_cal)))
     rows = rows_all[:n_rows].numpy()
     t0 = time.perf_counter()
-    oracle.gemm_sampled(A, B, rows, cols)
+    run(rows)
     dt = time.perf_counter() - t0
-    flops = 2.0 * len(rows) * len(cols) * w.K
+    flops = per_element * len(rows) * len(cols)
     return {
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
@@ -157,6 +166,9 @@ def main() -> int:
                     help="untimed calls first (about 0.3 s at 8192^3, so the clocks settle)")
     ap.add_argument("--workload", default="gemm_8192")
     ap.add_argument("--config", type=int, default=-1, help="kernel configuration (-1: automatic)")
+    ap.add_argument("--sparse", action="store_true",
+                    help="time the 2:4-sparse product instead: A pruned to 2:4 and compressed once "
+                         "on the GPU before timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the MFMA-only ceiling probe")
@@ -195,11 +207,24 @@ def main() -> int:
     ad, bd = a.to(dev), b.to(dev)
     cd = torch.empty((w.M, w.N), dtype=torch.float16, device=dev)
     epi = "relu" if w.relu else "none"
-    plan = g.plan(w.M, w.N, w.K, ad.data_ptr(), bd.data_ptr(), cd.data_ptr(), config=args.config)
     stream = torch.cuda.current_stream(dev)
+    if args.sparse:
+        vals, meta = g.sp_compress(ad, stream=stream)
+        torch.cuda.synchronize()
+        del ad
+        plan = g.plan_sp(w.M, w.N, w.K, vals.data_ptr(), meta.data_ptr(), bd.data_ptr(), cd.data_ptr(),
+                         config=args.config)
+
+        def call():
+            g.gemm_sp(vals, meta, bd, epilogue=epi, out=cd, config=args.config, stream=stream)
+    else:
+        plan = g.plan(w.M, w.N, w.K, ad.data_ptr(), bd.data_ptr(), cd.data_ptr(), config=args.config)
+
+        def call():
+            g.gemm(ad, bd, epilogue=epi, out=cd, config=args.config, stream=stream)
 
     for _ in range(args.warmup):
-        g.gemm(ad, bd, epilogue=epi, out=cd, config=args.config, stream=stream)
+        call()
     torch.cuda.synchronize()
 
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
@@ -208,14 +233,14 @@ def main() -> int:
     t0 = time.perf_counter()
     for i in range(args.steps):
         starts[i].record(stream)
-        g.gemm(ad, bd, epilogue=epi, out=cd, config=args.config, stream=stream)
+        call()
         ends[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
     launch_ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
     ms_per_step = wall * 1e3 / args.steps
-    flops = float(w.flops)
+    flops = float(plan["flops"])          # 2 M N K; sparse: M N K (products of kept values)
     value = flops * args.steps / wall / 1e12
     achieved = flops / (launch_ms.mean() * 1e-3) / 1e12
 
@@ -223,14 +248,18 @@ def main() -> int:
     import oracle
     rows, cols = workloads.sample_indices(w, 64)
     got = cd[rows.to(dev)][:, cols.to(dev)].cpu().view(torch.int16).numpy().view(np.uint16)
-    ref = oracle.gemm_sampled(a.view(torch.int16).numpy().view(np.uint16),
-                              b.view(torch.int16).numpy().view(np.uint16), rows.numpy(), cols.numpy(),
-                              relu=w.relu)
+    A_host = a.view(torch.int16).numpy().view(np.uint16)
+    B_host = b.view(torch.int16).numpy().view(np.uint16)
+    host_sparse = oracle.sp_compress(A_host) if args.sparse else None
+    if args.sparse:
+        ref = oracle.gemm_sp_sampled(*host_sparse, B_host, rows.numpy(), cols.numpy(), relu=w.relu)
+    else:
+        ref = oracle.gemm_sampled(A_host, B_host, rows.numpy(), cols.numpy(), relu=w.relu)
     spot = oracle.compare(got, ref)
 
-    config_name = g.config_name(plan["config"])
+    config_name = g.sp_config_name(plan["config"]) if args.sparse else g.config_name(plan["config"])
     out = {
-        "metric": METRIC,
+        "metric": SPARSE_METRIC if args.sparse else METRIC,
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -242,8 +271,9 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic",
-        "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "epilogue": epi,
-                   "inputs": f"{w.dist} seed {w.seed}", "kernel": config_name},
+        "config": {"workload": w.name + ("_sparse_2of4" if args.sparse else ""), "M": w.M, "N": w.N, "K": w.K,
+                   "epilogue": epi, "inputs": f"{w.dist} seed {w.seed}" + (", A pruned to 2:4" if args.sparse else ""),
+                   "kernel": config_name},
         "pct_of_peak": round(100.0 * value / PEAK_TFLOPS, 2),
         "roofline": {
             "bound": "mfma",
@@ -251,12 +281,12 @@ def main() -> int:
             "peak": round(PEAK_TFLOPS, 1),
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_TFLOPS, 4),
-            "traffic": measured_traffic(w.name, config_name),
+            "traffic": None if args.sparse else measured_traffic(w.name, config_name),
             "kernel_ms_mean": round(float(launch_ms.mean()), 5),
             "kernel_ms_median": round(float(np.median(launch_ms)), 5),
             "kernel_ms_min": round(float(launch_ms.min()), 5),
             "algorithmic_flops": flops,
-            "algorithmic_bytes": float(w.min_bytes),
+            "algorithmic_bytes": float(plan["min_bytes"]),
         },
         "spot_check": {"n": spot["n"], "pass": spot["pass"], "max_ulp_err": spot["max_ulp_err"]},
     }
@@ -269,7 +299,7 @@ def main() -> int:
             "random_operands": round(rnd, 1), "constant_operands": round(const, 1), "unit": "TFLOP/s",
             "achieved_over_random_ceiling": round(achieved / rnd, 3)}
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(a, b, w, args.cpu_budget)
+        out["cpu_baseline"] = cpu_baseline(a, b, w, args.cpu_budget, sparse=host_sparse)
     print(json.dumps(out), flush=True)
     return 0 if spot["pass"] else 1
 

@@ -38,6 +38,8 @@ const ConfigDesc kConfigs[kNumConfigs] = {
 const ConfigDesc kSpConfigs[kNumSpConfigs] = {
     {"sp_256x256x64_s3_w8", 256, 256, 64, 3, 8, true, 8, false, 1},
     {"sp_128x128x64_s3", 128, 128, 64, 3, 4, true, 8, false, 1},
+    {"sp_256x256x64_s3", 256, 256, 64, 3, 4, true, 8, false, 1},
+    {"sp_256x256x64_s3_spread", 256, 256, 64, 3, 4, true, 8, false, 1},
 };
 
 namespace {
@@ -514,8 +516,19 @@ gemm_f16_status_t validate_sp(int64_t M, int64_t N, int64_t K, const void *vals,
     return GEMM_F16_SUCCESS;
 }
 
-// Relative per-workgroup throughput of the sparse tiles (ranking only).
-double sp_config_efficiency(int c) { return c == 0 ? 1.0 : 0.76; }
+// Relative per-workgroup throughput of the sparse tiles (ranking only; 8192^3
+// and 4096^3 on MI355X): the 4-wave 256x256 tile shares each B fragment
+// between 4 A fragments, and the sparse MFMA leaves the kernel bound by
+// B's movement through LDS.  0: kept for tests and sweeps only.
+double sp_config_efficiency(int c)
+{
+    switch (c) {
+    case 2: return 1.00;   // 256x256x64, 4 waves
+    case 0: return 0.68;   // 256x256x64, 8 waves
+    case 1: return 0.60;   // 128x128x64, 4 waves
+    default: return 0.0;
+    }
+}
 
 gemm_f16_status_t make_plan_sp(int64_t M, int64_t N, int64_t K, int config, gemm_f16_plan_t *p)
 {
@@ -525,6 +538,8 @@ gemm_f16_status_t make_plan_sp(int64_t M, int64_t N, int64_t K, int config, gemm
     if (c == GEMM_F16_CONFIG_AUTO) {
         double best_t = 0.0;
         for (int i = 0; i < kNumSpConfigs; ++i) {
+            if (sp_config_efficiency(i) <= 0.0)
+                continue;
             const ConfigDesc &d = kSpConfigs[i];
             const double rounds = (double)ceil_div(ceil_div(M, d.block_m) * ceil_div(N, d.block_n), kComputeUnits);
             const double t = rounds * (double)d.block_m * (double)d.block_n / sp_config_efficiency(i);

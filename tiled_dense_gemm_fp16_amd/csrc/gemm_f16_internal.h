@@ -54,7 +54,7 @@ hipError_t launch_sp_compress(const _Float16 *A, _Float16 *vals, uint16_t *meta,
                               hipStream_t s);
 
 // Sparse GEMM, configuration `config` of kSpConfigs (A = vals, a.meta set).
-constexpr int kNumSpConfigs = 2;
+constexpr int kNumSpConfigs = 4;
 extern const ConfigDesc kSpConfigs[kNumSpConfigs];
 hipError_t launch_sparse(int config, const KernelArgs &a, int64_t grid, hipStream_t s);
 

@@ -1118,6 +1118,8 @@ hipError_t launch_sparse(int config, const KernelArgs &a, int64_t grid, hipStrea
     switch (config) {
     case 0: return launch_one<256, 256, 64, 2, 4, 3, true, 8, 8, true, false, false, true>(a, grid, s);
     case 1: return launch_one<128, 128, 64, 2, 2, 3, true, 8, 8, true, false, false, true>(a, grid, s);
+    case 2: return launch_one<256, 256, 64, 2, 2, 3, true, 8, 8, true, false, false, true>(a, grid, s);
+    case 3: return launch_one<256, 256, 64, 2, 2, 3, true, 8, 8, true, false, true, true>(a, grid, s);
     default: return hipErrorInvalidValue;
     }
 }
