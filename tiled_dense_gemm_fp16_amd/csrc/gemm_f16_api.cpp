@@ -19,8 +19,8 @@ namespace gemm_f16_impl {
 // occupancy: workgroups per CU as limited by LDS (160 KiB) and by registers
 // (512 per lane per SIMD, VGPRs + AGPRs as the compiler reports them).
 const ConfigDesc kConfigs[kNumConfigs] = {
-    {"256x256x64_s2_direct", 256, 256, 64, 2, 4, true, 8, false, 1},
-    {"256x128x64_s3_direct", 256, 128, 64, 3, 4, true, 8, false, 1},
+    {"256x256x64_s2_direct", 256, 256, 64, 2, 4, true, 8, true, 1},
+    {"256x128x64_s3_direct", 256, 128, 64, 3, 4, true, 8, true, 1},
     {"128x128x64_s3_direct", 128, 128, 64, 3, 4, true, 8, true, 1},
     {"128x128x32_s2_staged", 128, 128, 32, 2, 4, false, 1, true, 2},
     {"64x64x64_s2_staged", 64, 64, 64, 2, 4, false, 1, true, 5},
