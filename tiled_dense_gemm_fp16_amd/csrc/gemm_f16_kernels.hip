@@ -413,11 +413,13 @@ struct Tile {
 };
 
 // SPREAD (direct kernels): the loads of the tile requested during a step are
-// issued a part per k step instead of all at its start, so that four waves
-// do not queue a whole tile of loads ahead of their MFMAs at once (measured:
-// +3 % for 256x256 tiles with 4 waves, +6-8 % for 128x128; -2 % with 8 waves).
+// issued in SPREAD parts, one with each of the first SPREAD k steps, instead
+// of all at its start, so that the waves do not queue a whole tile of loads
+// ahead of their MFMAs at once (measured: 4 parts +3 % for 256x256 tiles
+// with 4 waves and +6-8 % for 128x128; 2 parts +0-3 % with 8 waves, where 4
+// parts leave the last loads too little time).  1: all at the start.
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool DIRECT, int VA, int VB, bool A_ROWS_K,
-          bool B_ROWS_K, bool SPREAD = false, bool SPARSE = false>
+          bool B_ROWS_K, int SPREAD = 1, bool SPARSE = false>
 __global__ void __launch_bounds__(64 * WM * WN)
 __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4)))
 gemm_f16_kernel(KernelArgs args)
@@ -605,8 +607,9 @@ gemm_f16_kernel(KernelArgs args)
     // `pending`.  The restrict qualifiers tell the compiler that the stage
     // being filled is not the stage being read, so it does not make the LDS
     // reads wait for those loads or writes.
-    constexpr bool SPREAD_LOADS = DIRECT && SPREAD;
-    constexpr int PARTS = SPREAD_LOADS ? NS : 1;
+    constexpr bool SPREAD_LOADS = DIRECT && SPREAD > 1;
+    constexpr int PARTS = SPREAD_LOADS ? SPREAD : 1;
+    static_assert(PARTS <= NS && T::LOADS_PER_TILE % PARTS == 0, "whole parts, one per k step at most");
     // rd_slot / wr_slot: the stage indices of (rd_a, rd_b) and (wr_a, wr_b),
     // which are also the register slots of sparse A's position words
     auto step = [&](const half_t *__restrict__ rd_a, const half_t *__restrict__ rd_b,
@@ -615,7 +618,8 @@ gemm_f16_kernel(KernelArgs args)
         // direct, spread: part p of the requested tile goes out with k step p
         auto issue_part = [&](int p) {
             if constexpr (SPREAD_LOADS)
-                issue_loads(kt_next, wr_a, wr_b, p, PARTS, wr_slot);
+                if (p < PARTS)
+                    issue_loads(kt_next, wr_a, wr_b, p, PARTS, wr_slot);
         };
         if constexpr (DIRECT) {
             // past the last tile: zeros into a retired stage
@@ -639,13 +643,13 @@ gemm_f16_kernel(KernelArgs args)
             issue_part(ks + 1);
             load_frags(f1, rd_a, rd_b, ks + 1, rd_slot);
             mma(f0);
-            interleave(SPREAD_LOADS ? PART_LOADS : 0, 0);
+            interleave(SPREAD_LOADS && ks + 1 < PARTS ? PART_LOADS : 0, 0);
             __builtin_amdgcn_sched_barrier(0);
             if (ks + 2 < NS) {
                 issue_part(ks + 2);
                 load_frags(f0, rd_a, rd_b, ks + 2, rd_slot);
                 mma(f1);
-                interleave(SPREAD_LOADS ? PART_LOADS : 0, 0);
+                interleave(SPREAD_LOADS && ks + 2 < PARTS ? PART_LOADS : 0, 0);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -1016,7 +1020,7 @@ hipError_t launch_sp_compress(const _Float16 *A, _Float16 *vals, uint16_t *meta,
 // ---- launchers ----------------------------------------------------------------
 
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool DIRECT, int VA, int VB, bool AR, bool BR,
-          bool SPREAD = false, bool SPARSE = false>
+          int SPREAD = 1, bool SPARSE = false>
 static hipError_t launch_one(const KernelArgs &a, int64_t grid, hipStream_t stream)
 {
     hipLaunchKernelGGL((gemm_f16_kernel<BM, BN, BK, WM, WN, STAGES, DIRECT, VA, VB, AR, BR, SPREAD, SPARSE>),
@@ -1074,12 +1078,12 @@ static hipError_t launch_transposed(int config, const KernelArgs &a, int va, int
                                     hipStream_t s)
 {
     switch (config) {
-    case 0: return launch_one<256, 256, 64, 2, 2, 2, true, 8, 8, AR, BR, true>(a, grid, s);
-    case 1: return launch_one<256, 128, 64, 2, 2, 3, true, 8, 8, AR, BR, true>(a, grid, s);
-    case 2: return launch_one<128, 128, 64, 2, 2, 3, true, 8, 8, AR, BR, true>(a, grid, s);
+    case 0: return launch_one<256, 256, 64, 2, 2, 2, true, 8, 8, AR, BR, 4>(a, grid, s);
+    case 1: return launch_one<256, 128, 64, 2, 2, 3, true, 8, 8, AR, BR, 4>(a, grid, s);
+    case 2: return launch_one<128, 128, 64, 2, 2, 3, true, 8, 8, AR, BR, 4>(a, grid, s);
     case 3: return launch_staged_8or1<128, 128, 32, 2, 2, 2, AR, BR>(a, va, vb, grid, s);
     case 4: return launch_staged_8or1<64, 64, 64, 2, 2, 2, AR, BR>(a, va, vb, grid, s);
-    case 7: return launch_one<256, 256, 64, 2, 4, 2, true, 8, 8, AR, BR>(a, grid, s);
+    case 7: return launch_one<256, 256, 64, 2, 4, 2, true, 8, 8, AR, BR, 2>(a, grid, s);
     case 10: return launch_staged_wide<256, 256, 64, 2, 4, 2, AR, BR>(a, va, vb, grid, s);
     default: return hipErrorInvalidValue;
     }
@@ -1098,14 +1102,14 @@ hipError_t launch(int config, const KernelArgs &a, int va, int vb, bool trans_a,
     // A as M x K, B as K x N: every configuration
     constexpr bool AR = true, BR = false;
     switch (config) {
-    case 0: return launch_one<256, 256, 64, 2, 2, 2, true, 8, 8, AR, BR, true>(a, grid, s);
-    case 1: return launch_one<256, 128, 64, 2, 2, 3, true, 8, 8, AR, BR, true>(a, grid, s);
-    case 2: return launch_one<128, 128, 64, 2, 2, 3, true, 8, 8, AR, BR, true>(a, grid, s);
+    case 0: return launch_one<256, 256, 64, 2, 2, 2, true, 8, 8, AR, BR, 4>(a, grid, s);
+    case 1: return launch_one<256, 128, 64, 2, 2, 3, true, 8, 8, AR, BR, 4>(a, grid, s);
+    case 2: return launch_one<128, 128, 64, 2, 2, 3, true, 8, 8, AR, BR, 4>(a, grid, s);
     case 3: return launch_staged<128, 128, 32, 2, 2, 2, AR, BR>(a, va, vb, grid, s);
     case 4: return launch_staged<64, 64, 64, 2, 2, 2, AR, BR>(a, va, vb, grid, s);
     case 5: return launch_one<256, 256, 32, 2, 2, 4, true, 8, 8, AR, BR>(a, grid, s);
     case 6: return launch_one<256, 256, 32, 2, 2, 5, true, 8, 8, AR, BR>(a, grid, s);
-    case 7: return launch_one<256, 256, 64, 2, 4, 2, true, 8, 8, AR, BR>(a, grid, s);
+    case 7: return launch_one<256, 256, 64, 2, 4, 2, true, 8, 8, AR, BR, 2>(a, grid, s);
     case 8: return launch_one<256, 256, 32, 2, 4, 5, true, 8, 8, AR, BR>(a, grid, s);
     case 9: return launch_one<256, 256, 64, 4, 2, 2, true, 8, 8, AR, BR>(a, grid, s);
     case 10: return launch_staged_wide<256, 256, 64, 2, 4, 2, AR, BR>(a, va, vb, grid, s);
@@ -1118,10 +1122,10 @@ hipError_t launch(int config, const KernelArgs &a, int va, int vb, bool trans_a,
 hipError_t launch_sparse(int config, const KernelArgs &a, int64_t grid, hipStream_t s)
 {
     switch (config) {
-    case 0: return launch_one<256, 256, 64, 2, 4, 3, true, 8, 8, true, false, false, true>(a, grid, s);
-    case 1: return launch_one<128, 128, 64, 2, 2, 3, true, 8, 8, true, false, false, true>(a, grid, s);
-    case 2: return launch_one<256, 256, 64, 2, 2, 3, true, 8, 8, true, false, false, true>(a, grid, s);
-    case 3: return launch_one<256, 256, 64, 2, 2, 3, true, 8, 8, true, false, true, true>(a, grid, s);
+    case 0: return launch_one<256, 256, 64, 2, 4, 3, true, 8, 8, true, false, 1, true>(a, grid, s);
+    case 1: return launch_one<128, 128, 64, 2, 2, 3, true, 8, 8, true, false, 1, true>(a, grid, s);
+    case 2: return launch_one<256, 256, 64, 2, 2, 3, true, 8, 8, true, false, 1, true>(a, grid, s);
+    case 3: return launch_one<256, 256, 64, 2, 2, 3, true, 8, 8, true, false, 2, true>(a, grid, s);
     default: return hipErrorInvalidValue;
     }
 }
