@@ -214,16 +214,17 @@ gemm_f16_status_t gemm_f16_sp_compress(int64_t M, int64_t K, const void *A, void
                                        void *stream);
 
 /*
- * C = epi(A . B) with A given as (vals, meta) above, B K x N and C M x N
- * binary16 row-major.  Products of kept values accumulate in fp32; one RNE
+ * C = epi(A . op(B)) with A given as (vals, meta) above and C M x N binary16
+ * row-major; op(B) = B (K x N, trans_b = 0) or B^T (B stored N x K,
+ * trans_b = 1).  Products of kept values accumulate in fp32; one RNE
  * rounding to binary16 at the end, as gemm_f16.
  *   config : GEMM_F16_CONFIG_AUTO or an index < gemm_f16_sp_num_configs().
  * Requirements: K % 16 == 0 (else INVALID_VALUE); vals and B 16-byte
- * aligned and N % 8 == 0, meta and C 2-byte aligned (else MISALIGNED);
- * C must not overlap vals, meta or B.  Other rules as gemm_f16.
+ * aligned and (trans_b = 0) N % 8 == 0, meta and C 2-byte aligned (else
+ * MISALIGNED); C must not overlap vals, meta or B.  Other rules as gemm_f16.
  */
 gemm_f16_status_t gemm_f16_sp(int64_t M, int64_t N, int64_t K, const void *vals, const void *meta,
-                              const void *B, void *C, int epilogue, int config, void *stream);
+                              const void *B, int trans_b, void *C, int epilogue, int config, void *stream);
 
 /* Number and names of the sparse kernel configurations. */
 int gemm_f16_sp_num_configs(void);
@@ -274,7 +275,8 @@ gemm_f16_status_t gemm_f16_plan_trans(int64_t M, int64_t N, int64_t K,
  * counts the products of kept values, M N K; lds_bytes the compressed A and
  * the B stages). */
 gemm_f16_status_t gemm_f16_plan_sp(int64_t M, int64_t N, int64_t K, const void *vals, const void *meta,
-                                   const void *B, const void *C, int config, gemm_f16_plan_t *plan);
+                                   const void *B, int trans_b, const void *C, int config,
+                                   gemm_f16_plan_t *plan);
 
 /* As gemm_f16_plan_trans, for gemm_f16_split with the given split request. */
 gemm_f16_status_t gemm_f16_plan_split(int64_t M, int64_t N, int64_t K,

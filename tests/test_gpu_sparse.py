@@ -59,13 +59,15 @@ def test_compress_unaligned_source():
     assert np.array_equal(u16(vals), v_ref) and np.array_equal(u16(meta), m_ref)
 
 
-def check_sp(M, N, K, seed, config=g.CONFIG_AUTO, epilogue="none"):
+def check_sp(M, N, K, seed, config=g.CONFIG_AUTO, epilogue="none", trans_b=False):
     a, b = draw(M, N, K, seed)
     vals, meta = g.sp_compress(a.to(DEV))
-    c = g.gemm_sp(vals, meta, b.to(DEV), epilogue=epilogue, config=config)
+    b_st = b.t().contiguous() if trans_b else b
+    c = g.gemm_sp(vals, meta, b_st.to(DEV), epilogue=epilogue, config=config, trans_b=trans_b)
     torch.cuda.synchronize()
-    p = g.plan_sp(M, N, K, vals.data_ptr(), meta.data_ptr(), 1 << 20, 1 << 20, config=config)
-    print(f"[sparse] gemm {M}x{N}x{K} config={g.sp_config_name(p['config'])} epi={epilogue}", flush=True)
+    p = g.plan_sp(M, N, K, vals.data_ptr(), meta.data_ptr(), 1 << 20, 1 << 20, config=config, trans_b=trans_b)
+    print(f"[sparse] gemm {M}x{N}x{K} trans_b={trans_b} config={g.sp_config_name(p['config'])} epi={epilogue}",
+          flush=True)
     v_ref, m_ref = oracle.sp_compress(u16(a))
     ref = oracle.gemm_sp(v_ref, m_ref, u16(b), relu=(epilogue == "relu"))
     res = oracle.compare(u16(c), ref)
@@ -81,6 +83,13 @@ SHAPES = [(256, 256, 256), (300, 264, 1008), (1, 8, 16), (257, 520, 80), (130, 7
 def test_every_sparse_config(shape):
     for c in range(g.sp_num_configs()):
         check_sp(*shape, seed=sum(shape), config=c)
+
+
+@pytest.mark.parametrize("shape", [(256, 256, 256), (300, 268, 1008), (1, 4, 16), (130, 72, 4096)])
+def test_every_sparse_config_b_transposed(shape):
+    # B given N x K (N need not be a multiple of 8 then)
+    for c in range(g.sp_num_configs()):
+        check_sp(*shape, seed=3 * sum(shape), config=c, trans_b=True)
 
 
 @pytest.mark.parametrize("epilogue", ["none", "relu"])

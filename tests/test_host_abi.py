@@ -299,15 +299,18 @@ def test_split_workspace_validation_before_any_launch():
 def test_sparse_argument_checks_before_any_launch():
     sp = g.lib().gemm_f16_sp
     V, Mt, B, C = FAKE, FAKE * 4, FAKE * 8, FAKE * 12
-    assert sp(64, 64, 40, V, Mt, B, C, 0, -1, None) == 1            # K % 16 != 0
-    assert sp(64, 64, 48, V + 8, Mt, B, C, 0, -1, None) == 2        # vals not 16-byte aligned
-    assert sp(64, 60, 48, V, Mt, B, C, 0, -1, None) == 2            # N % 8 != 0
-    assert sp(64, 64, 48, V, Mt + 1, B, C, 0, -1, None) == 2        # odd meta pointer
-    assert sp(64, 64, 48, V, 0, B, C, 0, -1, None) == 1             # no meta
-    assert sp(64, 64, 48, V, Mt, B, V, 0, -1, None) == 1            # C overlaps vals
-    assert sp(64, 64, 48, V, Mt, B, C, 2, -1, None) == 1            # unknown epilogue
-    assert sp(64, 64, 48, V, Mt, B, C, 0, g.sp_num_configs(), None) == 1
-    assert sp(0, 64, 48, V, Mt, B, C, 0, -1, None) == 0             # empty: no launch
+    assert sp(64, 64, 40, V, Mt, B, 0, C, 0, -1, None) == 1            # K % 16 != 0
+    assert sp(64, 64, 48, V + 8, Mt, B, 0, C, 0, -1, None) == 2        # vals not 16-byte aligned
+    assert sp(64, 60, 48, V, Mt, B, 0, C, 0, -1, None) == 2            # N % 8 != 0
+    assert sp(64, 64, 48, V, Mt + 1, B, 0, C, 0, -1, None) == 2        # odd meta pointer
+    assert sp(64, 64, 48, V, 0, B, 0, C, 0, -1, None) == 1             # no meta
+    assert sp(64, 64, 48, V, Mt, B, 0, V, 0, -1, None) == 1            # C overlaps vals
+    assert sp(64, 64, 48, V, Mt, B, 0, C, 2, -1, None) == 1            # unknown epilogue
+    assert sp(64, 64, 48, V, Mt, B, 0, C, 0, g.sp_num_configs(), None) == 1
+    assert sp(0, 64, 48, V, Mt, B, 0, C, 0, -1, None) == 0             # empty: no launch
+    assert sp(64, 64, 48, V, Mt, B, 2, C, 0, -1, None) == 1            # trans_b not 0 / 1
+    assert sp(0, 60, 48, V, Mt, B, 1, C, 0, -1, None) == 0             # B as N x K: N % 8 not needed
+    assert sp(64, 60, 48, V, Mt, B + 8, 1, C, 0, -1, None) == 2        # ... but 16-byte B
     assert g.lib().gemm_f16_sp_compress(4, 24, FAKE, V, Mt, None) == 1
     assert g.lib().gemm_f16_sp_compress(4, 32, FAKE + 1, V, Mt, None) == 2
     assert g.lib().gemm_f16_sp_compress(0, 32, 0, 0, 0, None) == 0

@@ -58,8 +58,8 @@ SIGNATURES = {
     "gemm_f16_plan_split": ([_i64, _i64, _i64, _vp, _int, _vp, _int, _vp, _int, _int, ctypes.POINTER(Plan)],
                             _int),
     "gemm_f16_sp_compress": ([_i64, _i64, _vp, _vp, _vp, _vp], _int),
-    "gemm_f16_sp": ([_i64, _i64, _i64, _vp, _vp, _vp, _vp, _int, _int, _vp], _int),
-    "gemm_f16_plan_sp": ([_i64, _i64, _i64, _vp, _vp, _vp, _vp, _int, ctypes.POINTER(Plan)], _int),
+    "gemm_f16_sp": ([_i64, _i64, _i64, _vp, _vp, _vp, _int, _vp, _int, _int, _vp], _int),
+    "gemm_f16_plan_sp": ([_i64, _i64, _i64, _vp, _vp, _vp, _int, _vp, _int, ctypes.POINTER(Plan)], _int),
     "gemm_f16_sp_num_configs": ([], _int),
     "gemm_f16_sp_config_name": ([_int], ctypes.c_char_p),
     "gemm_f16_num_configs": ([], _int),
@@ -219,11 +219,11 @@ def sp_config_name(config: int) -> str | None:
 
 
 def plan_sp(M: int, N: int, K: int, vals_ptr: int = 0, meta_ptr: int = 0, B_ptr: int = 0, C_ptr: int = 0,
-            config: int = CONFIG_AUTO) -> dict:
+            config: int = CONFIG_AUTO, trans_b: bool = False) -> dict:
     """How gemm_f16_sp would run this shape (host logic only)."""
     p = Plan()
-    st = lib().gemm_f16_plan_sp(M, N, K, vals_ptr or None, meta_ptr or None, B_ptr or None, C_ptr or None,
-                                config, ctypes.byref(p))
+    st = lib().gemm_f16_plan_sp(M, N, K, vals_ptr or None, meta_ptr or None, B_ptr or None, int(trans_b),
+                                C_ptr or None, config, ctypes.byref(p))
     if st != SUCCESS:
         raise GemmError(st, "gemm_f16_plan_sp")
     return p.as_dict()
@@ -257,8 +257,10 @@ def sp_compress(a, stream=None):
     return vals, meta
 
 
-def gemm_sp(vals, meta, b, epilogue: str = "none", out=None, config: int = CONFIG_AUTO, stream=None):
-    """C = epi(A @ b) for a 2:4-sparse A given as (vals, meta) from sp_compress."""
+def gemm_sp(vals, meta, b, epilogue: str = "none", out=None, config: int = CONFIG_AUTO, stream=None,
+            trans_b: bool = False):
+    """C = epi(A @ op(b)) for a 2:4-sparse A given as (vals, meta) from
+    sp_compress; b is K x N, or N x K with ``trans_b``."""
     import torch
 
     if epilogue not in _EPILOGUES:
@@ -267,9 +269,9 @@ def gemm_sp(vals, meta, b, epilogue: str = "none", out=None, config: int = CONFI
     _check_gpu_2d(meta, "meta", torch.int16)
     _check_gpu_2d(b, "b", torch.float16)
     M, K = vals.shape[0], 2 * vals.shape[1]
-    if tuple(meta.shape) != (M, K // 16) or b.shape[0] != K:
+    kb, N = (b.shape[1], b.shape[0]) if trans_b else (b.shape[0], b.shape[1])
+    if tuple(meta.shape) != (M, K // 16) or kb != K:
         raise ValueError(f"shape mismatch: vals {tuple(vals.shape)}, meta {tuple(meta.shape)}, b {tuple(b.shape)}")
-    N = b.shape[1]
     if out is None:
         out = torch.empty((M, N), dtype=torch.float16, device=b.device)
     elif out.dtype != torch.float16 or tuple(out.shape) != (M, N) or not out.is_contiguous():
@@ -278,7 +280,8 @@ def gemm_sp(vals, meta, b, epilogue: str = "none", out=None, config: int = CONFI
         stream = torch.cuda.current_stream(b.device)
     with torch.cuda.device(b.device):
         st = lib().gemm_f16_sp(M, N, K, vals.data_ptr() or None, meta.data_ptr() or None, b.data_ptr() or None,
-                               out.data_ptr() or None, _EPILOGUES[epilogue], config, stream.cuda_stream or None)
+                               int(trans_b), out.data_ptr() or None, _EPILOGUES[epilogue], config,
+                               stream.cuda_stream or None)
     if st != SUCCESS:
         raise GemmError(st, "gemm_f16_sp")
     return out

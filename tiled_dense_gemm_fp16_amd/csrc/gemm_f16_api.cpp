@@ -494,7 +494,7 @@ gemm_f16_status_t run(int64_t M, int64_t N, int64_t K, const void *A, bool ta, c
 // ---- 2:4 structured-sparse A -------------------------------------------------
 
 gemm_f16_status_t validate_sp(int64_t M, int64_t N, int64_t K, const void *vals, const void *meta, const void *B,
-                              const void *C, bool check_c_overlap)
+                              bool trans_b, const void *C, bool check_c_overlap)
 {
     if (M < 0 || N < 0 || K < 0 || K % 16 != 0)
         return GEMM_F16_ERROR_INVALID_VALUE;
@@ -504,8 +504,8 @@ gemm_f16_status_t validate_sp(int64_t M, int64_t N, int64_t K, const void *vals,
     if ((a_nonempty && (!vals || !meta)) || (b_nonempty && !B) || (c_nonempty && !C))
         return GEMM_F16_ERROR_INVALID_VALUE;
     // 16-byte loads of the compressed values and of B: rows of K/2 (K % 16 == 0)
-    // and N halves; the position words and C need 2 bytes
-    if ((a_nonempty && (uintptr_t)vals % 16) || (b_nonempty && ((uintptr_t)B % 16 || N % 8)) ||
+    // and of N (or, B given N x K, K) halves; the position words and C need 2 bytes
+    if ((a_nonempty && (uintptr_t)vals % 16) || (b_nonempty && ((uintptr_t)B % 16 || (!trans_b && N % 8))) ||
         ((uintptr_t)meta | (uintptr_t)C) & 1u)
         return GEMM_F16_ERROR_MISALIGNED;
     if (check_c_overlap && c_nonempty &&
@@ -669,20 +669,24 @@ gemm_f16_status_t gemm_f16_sp_compress(int64_t M, int64_t K, const void *A, void
 }
 
 gemm_f16_status_t gemm_f16_plan_sp(int64_t M, int64_t N, int64_t K, const void *vals, const void *meta,
-                                   const void *B, const void *C, int config, gemm_f16_plan_t *plan)
+                                   const void *B, int trans_b, const void *C, int config, gemm_f16_plan_t *plan)
 {
-    if (!plan)
+    if (!plan || (trans_b != 0 && trans_b != 1))
         return GEMM_F16_ERROR_INVALID_VALUE;
-    gemm_f16_status_t st = validate_sp(M, N, K, vals, meta, B, C, false);
+    gemm_f16_status_t st = validate_sp(M, N, K, vals, meta, B, trans_b != 0, C, false);
     if (st != GEMM_F16_SUCCESS)
         return st;
-    return make_plan_sp(M, N, K, config, plan);
+    st = make_plan_sp(M, N, K, config, plan);
+    plan->trans_b = trans_b;
+    return st;
 }
 
 gemm_f16_status_t gemm_f16_sp(int64_t M, int64_t N, int64_t K, const void *vals, const void *meta, const void *B,
-                              void *C, int epilogue, int config, void *stream)
+                              int trans_b, void *C, int epilogue, int config, void *stream)
 {
-    gemm_f16_status_t st = validate_sp(M, N, K, vals, meta, B, C, true);
+    if (trans_b != 0 && trans_b != 1)
+        return GEMM_F16_ERROR_INVALID_VALUE;
+    gemm_f16_status_t st = validate_sp(M, N, K, vals, meta, B, trans_b != 0, C, true);
     if (st != GEMM_F16_SUCCESS)
         return st;
     if (epilogue != GEMM_F16_EPILOGUE_NONE && epilogue != GEMM_F16_EPILOGUE_RELU)
@@ -712,7 +716,7 @@ gemm_f16_status_t gemm_f16_sp(int64_t M, int64_t N, int64_t K, const void *vals,
     a.k_split = (int)K;
     a.W = nullptr;
     a.meta = (const uint16_t *)meta;
-    hipError_t e = launch_sparse(plan.config, a, plan.grid, (hipStream_t)stream);
+    hipError_t e = launch_sparse(plan.config, a, trans_b != 0, plan.grid, (hipStream_t)stream);
     return e == hipSuccess ? GEMM_F16_SUCCESS : GEMM_F16_ERROR_LAUNCH_FAILED;
 }
 

@@ -53,10 +53,11 @@ hipError_t launch(int config, const KernelArgs &a, int va, int vb, bool trans_a,
 hipError_t launch_sp_compress(const _Float16 *A, _Float16 *vals, uint16_t *meta, int64_t M, int64_t K, bool vec,
                               hipStream_t s);
 
-// Sparse GEMM, configuration `config` of kSpConfigs (A = vals, a.meta set).
+// Sparse GEMM, configuration `config` of kSpConfigs (A = vals, a.meta set;
+// trans_b: B stored N x K).
 constexpr int kNumSpConfigs = 4;
 extern const ConfigDesc kSpConfigs[kNumSpConfigs];
-hipError_t launch_sparse(int config, const KernelArgs &a, int64_t grid, hipStream_t s);
+hipError_t launch_sparse(int config, const KernelArgs &a, bool trans_b, int64_t grid, hipStream_t s);
 
 // Split-K reduction: C = rne16(epi(W[0] + ... + W[splits-1])) over M x N
 // elements (relu: 1 for the ReLU epilogue).  vec4: N % 4 == 0, C 8-byte and

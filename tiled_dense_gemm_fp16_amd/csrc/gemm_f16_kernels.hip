@@ -1118,16 +1118,23 @@ hipError_t launch(int config, const KernelArgs &a, int va, int vb, bool trans_a,
     }
 }
 
-// Sparse configurations (A compressed 2:4, B as K x N, 16-byte loads).
-hipError_t launch_sparse(int config, const KernelArgs &a, int64_t grid, hipStream_t s)
+// Sparse configurations (A compressed 2:4; B as K x N, or given as N x K
+// when BR; 16-byte loads).
+template <bool BR>
+static hipError_t launch_sparse_layout(int config, const KernelArgs &a, int64_t grid, hipStream_t s)
 {
     switch (config) {
-    case 0: return launch_one<256, 256, 64, 2, 4, 3, true, 8, 8, true, false, 1, true>(a, grid, s);
-    case 1: return launch_one<128, 128, 64, 2, 2, 3, true, 8, 8, true, false, 1, true>(a, grid, s);
-    case 2: return launch_one<256, 256, 64, 2, 2, 3, true, 8, 8, true, false, 1, true>(a, grid, s);
-    case 3: return launch_one<256, 256, 64, 2, 2, 3, true, 8, 8, true, false, 2, true>(a, grid, s);
+    case 0: return launch_one<256, 256, 64, 2, 4, 3, true, 8, 8, true, BR, 1, true>(a, grid, s);
+    case 1: return launch_one<128, 128, 64, 2, 2, 3, true, 8, 8, true, BR, 1, true>(a, grid, s);
+    case 2: return launch_one<256, 256, 64, 2, 2, 3, true, 8, 8, true, BR, 1, true>(a, grid, s);
+    case 3: return launch_one<256, 256, 64, 2, 2, 3, true, 8, 8, true, BR, 2, true>(a, grid, s);
     default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_sparse(int config, const KernelArgs &a, bool trans_b, int64_t grid, hipStream_t s)
+{
+    return trans_b ? launch_sparse_layout<true>(config, a, grid, s) : launch_sparse_layout<false>(config, a, grid, s);
 }
 
 } // namespace gemm_f16_impl
