@@ -18,28 +18,30 @@ namespace gemm_f16_impl {
 
 // occupancy: workgroups per CU as limited by LDS (160 KiB) and by registers
 // (512 per lane per SIMD, VGPRs + AGPRs as the compiler reports them).
+constexpr int kNN = 1, kNT = 2, kAllLayouts = 15;   // masks over bit 2 trans_a + trans_b
 const ConfigDesc kConfigs[kNumConfigs] = {
-    {"256x256x64_s2_direct", 256, 256, 64, 2, 4, true, 8, true, 1},
-    {"256x128x64_s3_direct", 256, 128, 64, 3, 4, true, 8, true, 1},
-    {"128x128x64_s3_direct", 128, 128, 64, 3, 4, true, 8, true, 1},
-    {"128x128x32_s2_staged", 128, 128, 32, 2, 4, false, 1, true, 2},
-    {"64x64x64_s2_staged", 64, 64, 64, 2, 4, false, 1, true, 5},
-    {"256x256x32_s4_direct", 256, 256, 32, 4, 4, true, 8, false, 1},
-    {"256x256x32_s5_direct", 256, 256, 32, 5, 4, true, 8, false, 1},
-    {"256x256x64_s2_direct_w8n", 256, 256, 64, 2, 8, true, 8, true, 1},
-    {"256x256x32_s5_direct_w8n", 256, 256, 32, 5, 8, true, 8, false, 1},
-    {"256x256x64_s2_direct_w8m", 256, 256, 64, 2, 8, true, 8, false, 1},
-    {"256x256x64_s2_staged_w8", 256, 256, 64, 2, 8, false, 4, true, 1},
-    {"256x128x64_s2_staged", 256, 128, 64, 2, 4, false, 4, false, 1},
+    {"256x256x64_s2_direct", 256, 256, 64, 2, 4, true, 8, kAllLayouts, 1},
+    {"256x128x64_s3_direct", 256, 128, 64, 3, 4, true, 8, kAllLayouts, 1},
+    {"128x128x64_s3_direct", 128, 128, 64, 3, 4, true, 8, kAllLayouts, 1},
+    {"128x128x32_s2_staged", 128, 128, 32, 2, 4, false, 1, kAllLayouts, 2},
+    {"64x64x64_s2_staged", 64, 64, 64, 2, 4, false, 1, kAllLayouts, 5},
+    {"256x256x32_s4_direct", 256, 256, 32, 4, 4, true, 8, kNN, 1},
+    {"256x256x32_s5_direct", 256, 256, 32, 5, 4, true, 8, kNN, 1},
+    {"256x256x64_s2_direct_w8n", 256, 256, 64, 2, 8, true, 8, kAllLayouts, 1},
+    {"256x256x32_s5_direct_w8n", 256, 256, 32, 5, 8, true, 8, kNN, 1},
+    {"256x256x64_s2_direct_w8m", 256, 256, 64, 2, 8, true, 8, kNN, 1},
+    {"256x256x64_s2_staged_w8", 256, 256, 64, 2, 8, false, 4, kAllLayouts, 1},
+    {"256x128x64_s2_staged", 256, 128, 64, 2, 4, false, 4, kNN, 1},
+    {"256x256x64_s2_direct_m16", 256, 256, 64, 2, 4, true, 8, kAllLayouts, 1},
 };
 
 // Sparse configurations (2:4 A): fields as above; every one takes A as
 // compressed values + positions and B as K x N.
 const ConfigDesc kSpConfigs[kNumSpConfigs] = {
-    {"sp_256x256x64_s3_w8", 256, 256, 64, 3, 8, true, 8, false, 1},
-    {"sp_128x128x64_s3", 128, 128, 64, 3, 4, true, 8, false, 1},
-    {"sp_256x256x64_s3", 256, 256, 64, 3, 4, true, 8, false, 1},
-    {"sp_256x256x64_s3_spread", 256, 256, 64, 3, 4, true, 8, false, 1},
+    {"sp_256x256x64_s3_w8", 256, 256, 64, 3, 8, true, 8, kNN | kNT, 1},
+    {"sp_128x128x64_s3", 128, 128, 64, 3, 4, true, 8, kNN | kNT, 1},
+    {"sp_256x256x64_s3", 256, 256, 64, 3, 4, true, 8, kNN | kNT, 1},
+    {"sp_256x256x64_s3_spread", 256, 256, 64, 3, 4, true, 8, kNN | kNT, 1},
 };
 
 namespace {
@@ -99,6 +101,7 @@ gemm_f16_status_t validate(int64_t M, int64_t N, int64_t K, const void *A, const
 double config_efficiency(int c)
 {
     switch (c) {
+    case 12: return 1.06;   // 256x256x64 direct, 4 waves, 16x16x32 MFMAs
     case 7: return 1.00;    // 256x256x64 direct, 8 waves
     case 0: return 0.97;    // 256x256x64 direct, 4 waves
     case 1: return 0.90;    // 256x128x64 direct
@@ -111,9 +114,9 @@ double config_efficiency(int c)
     }
 }
 
-bool config_fits(int c, int va, int vb, bool transposed)
+bool config_fits(int c, int va, int vb, bool ta, bool tb)
 {
-    if (transposed && !kConfigs[c].transposed)
+    if (!(kConfigs[c].layouts & (1 << (2 * (int)ta + (int)tb))))
         return false;
     return va >= kConfigs[c].min_vec && vb >= kConfigs[c].min_vec;
 }
@@ -217,7 +220,7 @@ const TunedEntry *tuned_entry(int64_t M, int64_t N, int64_t K, bool ta, bool tb,
         if (e.trans_a != (int)ta || e.trans_b != (int)tb || e.aligned != (int)aligned)
             continue;
         const double d = sqrt((lm - e.lm) * (lm - e.lm) + (ln - e.ln) * (ln - e.ln) + (lk - e.lk) * (lk - e.lk));
-        if (d < best_d && e.config < kNumConfigs && config_fits(e.config, va, vb, ta || tb)) {
+        if (d < best_d && e.config < kNumConfigs && config_fits(e.config, va, vb, ta, tb)) {
             best = &e;
             best_d = d;
         }
@@ -285,12 +288,12 @@ Split model_split(int c, int64_t M, int64_t N, int64_t K, int requested, double 
 }
 
 // Configuration (and split) with the lowest modelled time.
-int choose_config(int64_t M, int64_t N, int64_t K, int va, int vb, bool transposed, int requested, Split *split)
+int choose_config(int64_t M, int64_t N, int64_t K, int va, int vb, bool ta, bool tb, int requested, Split *split)
 {
     int best = -1;
     double best_t = 0.0;
     for (int c = 0; c < kNumConfigs; ++c) {
-        if (!config_fits(c, va, vb, transposed) || config_efficiency(c) <= 0.0)
+        if (!config_fits(c, va, vb, ta, tb) || config_efficiency(c) <= 0.0)
             continue;
         double t;
         const Split sp = model_split(c, M, N, K, requested, &t);
@@ -314,7 +317,6 @@ gemm_f16_status_t make_plan(int64_t M, int64_t N, int64_t K, const void *A, bool
     const int64_t lda = ta ? M : K, ldb = tb ? K : N;
     const int va = vec_width(A, lda), vb = vec_width(B, ldb);
     const int vc = (N % 8 == 0 && (uintptr_t)C % 16 == 0) ? 8 : (N % 4 == 0 && (uintptr_t)C % 8 == 0) ? 4 : 1;
-    const bool tr = ta || tb;
     int c = config;
     Split sp = {1, K};
     if (c == GEMM_F16_CONFIG_AUTO) {
@@ -326,12 +328,12 @@ gemm_f16_status_t make_plan(int64_t M, int64_t N, int64_t K, const void *A, bool
                                   !split_addressable(kConfigs[c], N)))
                 sp = {1, K};
         } else {
-            c = choose_config(M, N, K, va, vb, tr, splits, &sp);
+            c = choose_config(M, N, K, va, vb, ta, tb, splits, &sp);
         }
-    } else if (config_fits(c, va, vb, tr)) {
+    } else if (config_fits(c, va, vb, ta, tb)) {
         sp = model_split(c, M, N, K, splits, nullptr);
     }
-    if (c < 0 || !config_fits(c, va, vb, tr))
+    if (c < 0 || !config_fits(c, va, vb, ta, tb))
         return GEMM_F16_ERROR_INVALID_VALUE;
     if (sp.splits > 1 && !split_addressable(kConfigs[c], N))
         return GEMM_F16_ERROR_UNSUPPORTED_SIZE;

@@ -33,11 +33,11 @@ struct ConfigDesc {
     int waves;            // wave64s per workgroup (4: one per SIMD, 8: two)
     bool direct;          // operands move global -> LDS with buffer_load ... lds
     int min_vec;          // smallest vector width (elements) of A and B loads it accepts
-    bool transposed;      // also compiled for A given K x M and/or B given N x K
+    int layouts;          // layouts compiled, bit 2 trans_a + trans_b: 1 = A . B only, 15 = all four
     int occupancy;        // workgroups resident per CU (LDS and register limits)
 };
 
-constexpr int kNumConfigs = 12;
+constexpr int kNumConfigs = 13;
 extern const ConfigDesc kConfigs[kNumConfigs];
 
 // Launch configuration `config` with `grid` workgroups on `s`.

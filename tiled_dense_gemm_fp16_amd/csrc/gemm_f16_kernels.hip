@@ -146,6 +146,16 @@ __device__ __forceinline__ int swz_b(int row)
         return 0;                          // four rows per window already disjoint
 }
 
+// B-type tile read as 16x16x32 fragments: a pass reads rows k..k+3 and
+// k+8..k+11, 32 bytes each; 4 (row & 3) chunks apart (64 bytes) as swz_b,
+// and rows 8 apart a further 2 chunks (32 bytes) apart.
+template <int CHUNKS>
+__device__ __forceinline__ int swz_b16(int row)
+{
+    static_assert(CHUNKS >= 16, "rows of at least 256 bytes");
+    return 4 * (row & 3) ^ 2 * ((row >> 3) & 1);
+}
+
 // ---- tile index remap -----------------------------------------------------
 // Workgroups are handed to the 8 XCDs round-robin (id % 8).  Give XCD x a
 // contiguous block of logical tile ids so its L2 sees neighbouring tiles, then
@@ -231,7 +241,9 @@ __device__ __forceinline__ void lds_store(half_t *p, typename VecT<V>::type v)
 // Each k slice is one buffer descriptor (rows past K read as 0); columns past
 // the matrix edge are not masked: they only reach output rows or columns
 // that are never stored.
-template <bool ROWS_K, int BMN, int BK, int THREADS, bool DIRECT, int V>
+// M16: the tile is read as 16x16x32 fragments (frag16); an mn-rows tile then
+// uses swz_b16, which also separates rows 8 apart.
+template <bool ROWS_K, int BMN, int BK, int THREADS, bool DIRECT, int V, bool M16 = false>
 struct Operand {
     static constexpr int STAGE = BMN * BK;                   // halves per LDS stage
     static constexpr int ROW = ROWS_K ? BK : BMN;            // halves per LDS tile row
@@ -247,7 +259,10 @@ struct Operand {
     // consecutive direct loads of a thread are ROW_STEP rows apart, a multiple
     // of the swizzle period, so they share one column and one base offset
     static constexpr int ROW_STEP = WAVES * ROWS_PER_KB;
-    static_assert(!DIRECT || ROW_STEP % (ROWS_K ? 16 : 4) == 0, "row step keeps the swizzle phase");
+    // swz_b16 repeats every 16 rows, but its bit from row bit 3 flips every 8:
+    // loads whose row step is an odd multiple of 8 alternate between two columns
+    static constexpr bool ALT_COLUMN = DIRECT && !ROWS_K && M16 && (ROW_STEP / 8) % 2 == 1;
+    static_assert(!DIRECT || ROW_STEP % (ROWS_K ? 16 : (M16 ? 8 : 4)) == 0, "row step keeps the swizzle phase");
     // staged: vectors of V halves through registers
     static constexpr int VECS = STAGE / V / THREADS;
     static_assert(DIRECT || STAGE % (V * THREADS) == 0, "staged tiles split evenly over the threads");
@@ -258,6 +273,8 @@ struct Operand {
     {
         if constexpr (ROWS_K)
             return swz_a<CHUNKS>(row);
+        else if constexpr (M16)
+            return swz_b16<CHUNKS>(row);
         else
             return swz_b<CHUNKS>(row);
     }
@@ -269,6 +286,7 @@ struct Operand {
     int kbase;             // start of the workgroup's k range (split-K), a multiple of BK
     __amdgpu_buffer_rsrc_t panel;   // ROWS_K: the workgroup's BMN rows
     uint32_t off0, step;   // direct: byte offset of the first chunk, distance between loads
+    uint32_t alt;          // direct, ALT_COLUMN: offset change (mod 2^32) on odd loads
     int kcol0;             // direct, ROWS_K: k column of the thread's chunks
     uint32_t offv[VEC_DIV];
     int kcolv[VEC_DIV];
@@ -294,6 +312,14 @@ struct Operand {
             kcol0 = c;
             off0 = ((uint32_t)r * (uint32_t)ld + (uint32_t)(ROWS_K ? c : mn0 + c)) * 2u;
             step = (uint32_t)ROW_STEP * (uint32_t)ld * 2u;
+            if constexpr (ALT_COLUMN) {
+                // row r + ROW_STEP flips swz_b16's 2-chunk term: the chunk moves by +-2
+                const int pos = (byte % (ROW * 2)) / 16;
+                const int c_odd = (pos ^ swz(r + ROW_STEP)) * 8;
+                alt = (uint32_t)((c_odd - c) * 2);
+            } else {
+                alt = 0;
+            }
         } else {
 #pragma unroll
             for (int i = 0; i < VECS; ++i) {
@@ -331,7 +357,7 @@ struct Operand {
             for (int i = 0; i < DMA; ++i) {
                 if (i * nparts / DMA != part)
                     continue;
-                const uint32_t off = (off0 + shift + (uint32_t)i * step) | mask;
+                const uint32_t off = (off0 + shift + (uint32_t)i * step + ((ALT_COLUMN && (i & 1)) ? alt : 0u)) | mask;
                 LDS_AS void *d = (LDS_AS void *)(dst + (wave + WAVES * i) * 512);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d, 16, off, 0, 0, 0);
             }
@@ -356,6 +382,36 @@ struct Operand {
                 lds_store<V>(dst + ldsv[i], reg[i]);
         } else {
             (void)dst;
+        }
+    }
+
+    // v_mfma_f32_16x16x32_f16 fragment: the 16 m (or n) starting at mnb of
+    // the 32-deep k step ks; lane l gets 8 k values 32 ks + 8 (l / 16) .. +7
+    // of m (or n) mnb + l % 16.  k-rows tile: one 16-byte read (16 rows per
+    // pass, conflict-free under swz_a).  mn-rows tile: two transposing reads;
+    // in 16-lane group g, lane j gives the address of row 32 ks + 8 g + j / 4
+    // (+4), columns mnb + 4 (j % 4) .. +3, and lane i receives column mnb + i.
+    // A pass of 32 lanes covers rows k..k+3 and k+8..k+11, 32 bytes each:
+    // swz_b16 puts them in 8 different 32-byte slots of the bank window.
+    __device__ __forceinline__ half8 frag16(const half_t *stage, int mnb, int ks, int lane) const
+    {
+        static_assert(M16, "a tile read as 16x16x32 fragments uses the M16 swizzle");
+        if constexpr (ROWS_K) {
+            const int r = mnb + (lane & 15);
+            const int c = 4 * ks + (lane >> 4);
+            return *reinterpret_cast<const half8 *>(stage + r * ROW + ((c ^ swz(r)) * 8));
+        } else {
+            const int g = lane >> 4, j = lane & 15;
+            const int r0 = 32 * ks + 8 * g + (j >> 2);
+            const int r1 = r0 + 4;
+            const int col = mnb + 4 * (j & 3);
+            const half_t *p0 = stage + r0 * ROW + (((col >> 3) ^ swz(r0)) * 8) + (col & 7);
+            const half_t *p1 = stage + r1 * ROW + (((col >> 3) ^ swz(r1)) * 8) + (col & 7);
+            short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS short4v *)p0);
+            short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS short4v *)p1);
+            half4 lo_h = __builtin_bit_cast(half4, lo);
+            half4 hi_h = __builtin_bit_cast(half4, hi);
+            return half8{lo_h[0], lo_h[1], lo_h[2], lo_h[3], hi_h[0], hi_h[1], hi_h[2], hi_h[3]};
         }
     }
 
@@ -388,22 +444,26 @@ struct Operand {
 // staged like a k-rows operand of BK/2 columns per tile) and positions
 // (M x K/16 uint16 words, loaded straight into registers); the product uses
 // v_smfmac_f32_32x32x32_f16, 32 k per step.
+// M16: v_mfma_f32_16x16x32_f16 on 16x16 blocks (32 k per step) instead of
+// 32x32x16.
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool DIRECT, int VA, int VB, bool A_ROWS_K,
-          bool B_ROWS_K, bool SPARSE = false>
+          bool B_ROWS_K, bool SPARSE = false, bool M16 = false>
 struct Tile {
     static constexpr int kWaves = WM * WN;           // 4 (one per SIMD) or 8 (two per SIMD)
     static constexpr int kThreads = 64 * kWaves;
     static_assert(kWaves == 4 || kWaves == 8, "4 or 8 waves");
     static constexpr int WTM = BM / WM;              // wave sub-tile rows (m)
     static constexpr int WTN = BN / WN;              // wave sub-tile cols (n)
-    static constexpr int TM = WTM / 32;              // 32x32 MFMA blocks per wave along m
-    static constexpr int TN = WTN / 32;              // ... along n
-    static_assert(TM >= 1 && TN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
-    static constexpr int KSTEP = SPARSE ? 32 : 16;    // k per MFMA step
+    static constexpr int BLK = M16 ? 16 : 32;        // MFMA block edge
+    static constexpr int TM = WTM / BLK;             // MFMA blocks per wave along m
+    static constexpr int TN = WTN / BLK;             // ... along n
+    static_assert(TM >= 1 && TN >= 1 && WTM % BLK == 0 && WTN % BLK == 0, "wave tile");
+    static_assert(!M16 || !SPARSE, "16x16x32 blocks: dense only");
+    static constexpr int KSTEP = SPARSE || M16 ? 32 : 16;   // k per MFMA step
     static_assert(BK % (2 * KSTEP) == 0, "an even number of MFMA steps per tile");
     static_assert(!SPARSE || (A_ROWS_K && DIRECT), "sparse A: compressed rows, direct loads");
-    using OpA = Operand<A_ROWS_K, BM, SPARSE ? BK / 2 : BK, kThreads, DIRECT, VA>;
-    using OpB = Operand<B_ROWS_K, BN, BK, kThreads, DIRECT, VB>;
+    using OpA = Operand<A_ROWS_K, BM, SPARSE ? BK / 2 : BK, kThreads, DIRECT, VA, M16>;
+    using OpB = Operand<B_ROWS_K, BN, BK, kThreads, DIRECT, VB, M16>;
     static constexpr int A_STAGE = OpA::STAGE;
     static constexpr int B_STAGE = OpB::STAGE;
     static constexpr int LDS_BYTES = STAGES * (A_STAGE + B_STAGE) * 2;
@@ -419,12 +479,12 @@ struct Tile {
 // with 4 waves and +6-8 % for 128x128; 2 parts +0-3 % with 8 waves, where 4
 // parts leave the last loads too little time).  1: all at the start.
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool DIRECT, int VA, int VB, bool A_ROWS_K,
-          bool B_ROWS_K, int SPREAD = 1, bool SPARSE = false>
+          bool B_ROWS_K, int SPREAD = 1, bool SPARSE = false, bool M16 = false>
 __global__ void __launch_bounds__(64 * WM * WN)
 __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4)))
 gemm_f16_kernel(KernelArgs args)
 {
-    using T = Tile<BM, BN, BK, WM, WN, STAGES, DIRECT, VA, VB, A_ROWS_K, B_ROWS_K, SPARSE>;
+    using T = Tile<BM, BN, BK, WM, WN, STAGES, DIRECT, VA, VB, A_ROWS_K, B_ROWS_K, SPARSE, M16>;
     __shared__ __attribute__((aligned(1024))) half_t lds[T::LDS_BYTES / 2];
     half_t *const As = lds;                                  // STAGES A stages
     half_t *const Bs = lds + STAGES * T::A_STAGE;            // STAGES B stages
@@ -502,12 +562,13 @@ gemm_f16_kernel(KernelArgs args)
         opb.store(dst_b);
     };
 
-    float16v acc[T::TM][T::TN];
+    using Acc = typename std::conditional<M16, float4v, float16v>::type;
+    Acc acc[T::TM][T::TN];
 #pragma unroll
     for (int i = 0; i < T::TM; ++i)
 #pragma unroll
         for (int j = 0; j < T::TN; ++j)
-            acc[i][j] = float16v{};
+            acc[i][j] = Acc{};
 
     // Fragments of one 16-deep k step: x = B^T slices (one per 32-column
     // block), y = A^T slices (one per 32-row block).
@@ -524,11 +585,17 @@ gemm_f16_kernel(KernelArgs args)
     };
     auto load_frags = [&](Frags &f, const half_t *as, const half_t *bs, int ks, int mslot = 0) {
 #pragma unroll
-        for (int i = 0; i < T::TM; ++i)
-            f.y[i] = opa.frag(as, wm0 + 32 * i, ks, lane);
+        for (int i = 0; i < T::TM; ++i) {
+            if constexpr (M16)
+                f.y[i] = opa.frag16(as, wm0 + 16 * i, ks, lane);
+            else
+                f.y[i] = opa.frag(as, wm0 + 32 * i, ks, lane);
+        }
 #pragma unroll
         for (int j = 0; j < T::TN; ++j) {
-            if constexpr (SPARSE) {
+            if constexpr (M16) {
+                f.x[j] = opb.frag16(bs, wn0 + 16 * j, ks, lane);
+            } else if constexpr (SPARSE) {
                 const half8 lo = opb.frag(bs, wn0 + 32 * j, 2 * ks, lane);
                 const half8 hi = opb.frag(bs, wn0 + 32 * j, 2 * ks + 1, lane);
                 f.x[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
@@ -558,6 +625,8 @@ gemm_f16_kernel(KernelArgs args)
                     // C = A . B directly: the sparse operand must come first
                     acc[i][j] = __builtin_amdgcn_smfmac_f32_32x32x32_f16(f.y[i], f.x[j], acc[i][j],
                                                                           (int)f.idx[i], 0, 0);
+                else if constexpr (M16)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(f.x[j], f.y[i], acc[i][j], 0, 0, 0);
                 else
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.x[j], f.y[i], acc[i][j], 0, 0, 0);
             }
@@ -566,7 +635,8 @@ gemm_f16_kernel(KernelArgs args)
     // of the next step (and, after a barrier, with the next tile's loads and
     // LDS writes), so the matrix core keeps busy while those are in flight.
     constexpr int kMfmaPerStep = T::TM * T::TN;
-    constexpr int kReadsPerStep = T::TM + (SPARSE ? 4 : 2) * T::TN;
+    constexpr int kReadsPerStep = M16 ? (A_ROWS_K ? 1 : 2) * T::TM + (B_ROWS_K ? 1 : 2) * T::TN
+                                      : T::TM + (SPARSE ? 4 : 2) * T::TN;
     // Reads go two per MFMA (measured: +4 % for 128x128 tiles over one per
     // MFMA, and no loss elsewhere), so that the next step's fragments are
     // requested early in the current one.
@@ -710,6 +780,15 @@ gemm_f16_kernel(KernelArgs args)
     wait_vmcnt<0>();   // the tail's zero-filling loads must land before the workgroup retires
 
     const int c_rows = min(BM, M - m0);
+    // The accumulator of MFMA block (i, j) holds, in register group g (32x32
+    // blocks: g = 0..3; 16x16 blocks: g = 0), four consecutive columns
+    // col_of(j, g) .. +3 of the tile in row row_of(i) of the panel (the
+    // dense product is computed transposed, C^T = B^T . A^T).
+    constexpr int GROUPS = M16 ? 1 : 4;
+    auto row_of = [&](int i) { return M16 ? wm0 + 16 * i + (lane & 15) : wm0 + 32 * i + (lane & 31); };
+    auto col_of = [&](int j, int g) {
+        return M16 ? wn0 + 16 * j + 4 * (lane >> 4) : wn0 + 32 * j + 8 * g + 4 * (lane >> 5);
+    };
     if constexpr (SPARSE) {
         // C = A . B was computed untransposed: lane l of block (i, j) holds
         // column wn0 + 32 j + l % 32, rows wm0 + 32 i + 8 g + 4 (l / 32) + r
@@ -747,12 +826,12 @@ gemm_f16_kernel(KernelArgs args)
         const bool w4 = (N & 3) == 0;
 #pragma unroll
         for (int i = 0; i < T::TM; ++i) {
-            const int r = wm0 + 32 * i + (lane & 31);
+            const int r = row_of(i);
 #pragma unroll
             for (int j = 0; j < T::TN; ++j)
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int n = n0 + wn0 + 32 * j + 8 * g + 4 * (lane >> 5);
+                for (int g = 0; g < GROUPS; ++g) {
+                    const int n = n0 + col_of(j, g);
                     const uint32_t off = ((uint32_t)r * (uint32_t)N + (uint32_t)n) * 4u;
                     // element values copied to scalars before any bit cast (see out4)
                     const float v0 = acc[i][j][4 * g + 0], v1 = acc[i][j][4 * g + 1];
@@ -779,8 +858,7 @@ gemm_f16_kernel(KernelArgs args)
     const __amdgpu_buffer_rsrc_t c_rsrc = make_rsrc(c_base, (uint32_t)c_rows * (uint32_t)N * 2u);
     const bool relu = args.relu != 0;
     const int vec_c = args.vec_c;
-    // The four values a lane holds for MFMA block (i, j), register group g:
-    // row wm0 + 32 i + lane % 32, columns wn0 + 32 j + 8 g + 4 (lane / 32) .. +3.
+    // The four values of block (i, j), group g, as fp16 after the epilogue.
     auto out4 = [&](int i, int j, int g, half_t &h0, half_t &h1, half_t &h2, half_t &h3) {
         float v0 = acc[i][j][4 * g + 0], v1 = acc[i][j][4 * g + 1];
         float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
@@ -813,14 +891,14 @@ gemm_f16_kernel(KernelArgs args)
         __builtin_amdgcn_s_barrier();                       // every wave is done with the stages
 #pragma unroll
         for (int i = 0; i < T::TM; ++i) {
-            const int r = wm0 + 32 * i + (lane & 31);
+            const int r = row_of(i);
 #pragma unroll
             for (int j = 0; j < T::TN; ++j)
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
+                for (int g = 0; g < GROUPS; ++g) {
                     half_t h0, h1, h2, h3;
                     out4(i, j, g, h0, h1, h2, h3);
-                    const int u = (wn0 + 32 * j + 8 * g) / 4 + (lane >> 5);
+                    const int u = col_of(j, g) / 4;
                     half4 h = {h0, h1, h2, h3};
                     *reinterpret_cast<half4 *>(ct + r * BN + 4 * (u ^ (r & UMASK))) = h;
                 }
@@ -848,12 +926,12 @@ gemm_f16_kernel(KernelArgs args)
     }
 #pragma unroll
     for (int i = 0; i < T::TM; ++i) {
-        const int r = wm0 + 32 * i + (lane & 31);            // row inside the panel
+        const int r = row_of(i);                             // row inside the panel
 #pragma unroll
         for (int j = 0; j < T::TN; ++j) {
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int n = n0 + wn0 + 32 * j + 8 * g + 4 * (lane >> 5);
+            for (int g = 0; g < GROUPS; ++g) {
+                const int n = n0 + col_of(j, g);
                 half_t h0, h1, h2, h3;
                 out4(i, j, g, h0, h1, h2, h3);
                 const uint32_t off = ((uint32_t)r * (uint32_t)N + (uint32_t)n) * 2u;
@@ -1020,10 +1098,10 @@ hipError_t launch_sp_compress(const _Float16 *A, _Float16 *vals, uint16_t *meta,
 // ---- launchers ----------------------------------------------------------------
 
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool DIRECT, int VA, int VB, bool AR, bool BR,
-          int SPREAD = 1, bool SPARSE = false>
+          int SPREAD = 1, bool SPARSE = false, bool M16 = false>
 static hipError_t launch_one(const KernelArgs &a, int64_t grid, hipStream_t stream)
 {
-    hipLaunchKernelGGL((gemm_f16_kernel<BM, BN, BK, WM, WN, STAGES, DIRECT, VA, VB, AR, BR, SPREAD, SPARSE>),
+    hipLaunchKernelGGL((gemm_f16_kernel<BM, BN, BK, WM, WN, STAGES, DIRECT, VA, VB, AR, BR, SPREAD, SPARSE, M16>),
                        dim3((unsigned)grid), dim3(64 * WM * WN), 0, stream, a);
     return hipGetLastError();
 }
@@ -1085,6 +1163,7 @@ static hipError_t launch_transposed(int config, const KernelArgs &a, int va, int
     case 4: return launch_staged_8or1<64, 64, 64, 2, 2, 2, AR, BR>(a, va, vb, grid, s);
     case 7: return launch_one<256, 256, 64, 2, 4, 2, true, 8, 8, AR, BR, 2>(a, grid, s);
     case 10: return launch_staged_wide<256, 256, 64, 2, 4, 2, AR, BR>(a, va, vb, grid, s);
+    case 12: return launch_one<256, 256, 64, 2, 2, 2, true, 8, 8, AR, BR, 2, false, true>(a, grid, s);
     default: return hipErrorInvalidValue;
     }
 }
@@ -1114,6 +1193,7 @@ hipError_t launch(int config, const KernelArgs &a, int va, int vb, bool trans_a,
     case 9: return launch_one<256, 256, 64, 4, 2, 2, true, 8, 8, AR, BR>(a, grid, s);
     case 10: return launch_staged_wide<256, 256, 64, 2, 4, 2, AR, BR>(a, va, vb, grid, s);
     case 11: return launch_staged_wide<256, 128, 64, 2, 2, 2, AR, BR>(a, va, vb, grid, s);
+    case 12: return launch_one<256, 256, 64, 2, 2, 2, true, 8, 8, AR, BR, 2, false, true>(a, grid, s);
     default: return hipErrorInvalidValue;
     }
 }
