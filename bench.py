@@ -292,10 +292,13 @@ def main() -> int:
     }
     if not args.no_ceiling:
         # the matrix cores' sustained rate on register operands alone, for the
-        # same instruction mix, with constant and with changing random bits
-        rnd = g.probe_mfma_tflops(g.PROBE_RANDOM_CHANGING)
-        const = g.probe_mfma_tflops(g.PROBE_CONSTANT)
+        # kernel's MFMA instruction, with constant and with changing random bits
+        m16 = (not args.sparse) and config_name.endswith("_m16")
+        extra = g.PROBE_MFMA16 if m16 else 0
+        rnd = g.probe_mfma_tflops(g.PROBE_RANDOM_CHANGING + extra)
+        const = g.probe_mfma_tflops(g.PROBE_CONSTANT + extra)
         out["roofline"]["mfma_only_ceiling"] = {
+            "instruction": "v_mfma_f32_16x16x32_f16" if m16 else "v_mfma_f32_32x32x16_f16",
             "random_operands": round(rnd, 1), "constant_operands": round(const, 1), "unit": "TFLOP/s",
             "achieved_over_random_ceiling": round(achieved / rnd, 3)}
     if not args.no_cpu_baseline:
