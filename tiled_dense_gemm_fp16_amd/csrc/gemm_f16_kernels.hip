@@ -478,8 +478,13 @@ struct Tile {
 // ahead of their MFMAs at once (measured: 4 parts +3 % for 256x256 tiles
 // with 4 waves and +6-8 % for 128x128; 2 parts +0-3 % with 8 waves, where 4
 // parts leave the last loads too little time).  1: all at the start.
+// STAGED_ONLY: compiled with the LDS-staged fp16 epilogue alone (no split-K
+// partials, N % 8 == 0 and C 16-byte aligned), for tiles whose accumulator
+// fills the matrix-core registers: with one epilogue path the accumulator
+// does not have to be held in vector registers across a branch, where it
+// overflows them and spills to scratch.
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool DIRECT, int VA, int VB, bool A_ROWS_K,
-          bool B_ROWS_K, int SPREAD = 1, bool SPARSE = false, bool M16 = false>
+          bool B_ROWS_K, int SPREAD = 1, bool SPARSE = false, bool M16 = false, bool STAGED_ONLY = false>
 __global__ void __launch_bounds__(64 * WM * WN)
 __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4)))
 gemm_f16_kernel(KernelArgs args)
@@ -670,7 +675,7 @@ gemm_f16_kernel(KernelArgs args)
     static_assert(NS % 2 == 0, "an even number of k steps per tile");
     static_assert(DIRECT || STAGES == 2, "register-staged kernels use two LDS stages");
     constexpr int LOOKAHEAD = DIRECT ? STAGES - 1 : 2;
-    Frags f0, f1;
+    Frags f0, f1 = {};   // f1 zero: an empty K loop multiplies zeros below
     // One tile: bring tile kt_next toward LDS -- (wr_a, wr_b) is the stage it
     // (direct) or the register-held tile (staged) goes to -- then the math on
     // stage (rd_a, rd_b); f1 holds the previous tile's last step when
@@ -775,7 +780,7 @@ gemm_f16_kernel(KernelArgs args)
             }
         }
     }
-    if (nk > 0)
+    if (STAGED_ONLY || nk > 0)
         mma(f1);
     wait_vmcnt<0>();   // the tail's zero-filling loads must land before the workgroup retires
 
@@ -816,7 +821,7 @@ gemm_f16_kernel(KernelArgs args)
             }
         return;
     }
-    if (args.W) {
+    if (!STAGED_ONLY && args.W) {
         // split-K: the fp32 partial sums of this split go to its slice of the
         // workspace (row pitch N); the reduction applies the epilogue.  When
         // N % 4 == 0 a lane's four consecutive columns leave as one 16-byte
@@ -876,15 +881,19 @@ gemm_f16_kernel(KernelArgs args)
         h3 = (half_t)v3;
     };
     static_assert(BM * BN * 2 <= T::LDS_BYTES, "the output tile fits in the LDS stages");
-    if (vec_c == 8) {
+    if (STAGED_ONLY || vec_c == 8) {
         // N % 8 == 0 and C 16-byte aligned: stage the fp16 tile through the
         // (now idle) LDS and write it as 16-byte pieces of consecutive
         // columns, so that every row of the tile leaves as whole cache lines.
         // LDS layout [BM][BN] with the 8-byte unit index XOR-ed with the row's
         // low bits: the 32 lanes of a pass write 32 different rows of one
-        // column unit, and these land in 32 different bank pairs.
+        // column unit (32x32 blocks) or 16 rows of two units (16x16 blocks),
+        // and SQ_LDS_BANK_CONFLICT reads 0 for both.  (Twice the row's low
+        // 4 bits for 16x16 blocks, although distinct per pass in a 64-bank
+        // model, measured 1.5 % conflict cycles.)
         constexpr int UNITS = BN / 4;                       // 8-byte units per row
         constexpr int UMASK = (UNITS < 32 ? UNITS : 32) - 1;
+        auto swz = [](int row) { return row & UMASK; };
         half_t *ct = lds;
         wait_vmcnt<0>();
         wait_lgkm0();
@@ -900,7 +909,7 @@ gemm_f16_kernel(KernelArgs args)
                     out4(i, j, g, h0, h1, h2, h3);
                     const int u = col_of(j, g) / 4;
                     half4 h = {h0, h1, h2, h3};
-                    *reinterpret_cast<half4 *>(ct + r * BN + 4 * (u ^ (r & UMASK))) = h;
+                    *reinterpret_cast<half4 *>(ct + r * BN + 4 * (u ^ swz(r))) = h;
                 }
         }
         wait_lgkm0();
@@ -913,7 +922,7 @@ gemm_f16_kernel(KernelArgs args)
             const int id = tid + q * T::kThreads;
             const int r = id / CHUNKS_PER_ROW;
             const int c = id % CHUNKS_PER_ROW;
-            const int sw = r & UMASK;
+            const int sw = swz(r);
             // units 2c and 2c+1 sit side by side at unit (2c ^ sw) & ~1, swapped when sw is odd
             int4v v = *reinterpret_cast<const int4v *>(ct + r * BN + 4 * ((2 * c ^ sw) & ~1));
             if (sw & 1)
@@ -1101,6 +1110,17 @@ template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool DIRECT, int V
           int SPREAD = 1, bool SPARSE = false, bool M16 = false>
 static hipError_t launch_one(const KernelArgs &a, int64_t grid, hipStream_t stream)
 {
+    // one wave per SIMD holding a 128x128 accumulator (256 registers): the
+    // common unsplit, 16-byte-aligned case runs the staged-epilogue build
+    constexpr bool FULL_ACC = !SPARSE && WM * WN == 4 && BM * BN == 256 * 256;
+    if constexpr (FULL_ACC) {
+        if (a.W == nullptr && a.vec_c == 8) {
+            hipLaunchKernelGGL(
+                (gemm_f16_kernel<BM, BN, BK, WM, WN, STAGES, DIRECT, VA, VB, AR, BR, SPREAD, SPARSE, M16, true>),
+                dim3((unsigned)grid), dim3(64 * WM * WN), 0, stream, a);
+            return hipGetLastError();
+        }
+    }
     hipLaunchKernelGGL((gemm_f16_kernel<BM, BN, BK, WM, WN, STAGES, DIRECT, VA, VB, AR, BR, SPREAD, SPARSE, M16>),
                        dim3((unsigned)grid), dim3(64 * WM * WN), 0, stream, a);
     return hipGetLastError();
