@@ -120,6 +120,49 @@ def test_degenerate_dimensions():
     check(a, b, label="dot product")
 
 
+def test_empty_k_every_config():
+    # K == 0 with N % 8 == 0: every configuration, including the 256x256
+    # four-wave tiles' staged-epilogue build, whose last MFMA then multiplies
+    # zeroed fragments; C must hold +0 (also under ReLU)
+    M, N = 300, 264
+    a = torch.empty(M, 0, dtype=torch.float16, device=DEV)
+    b = torch.empty(0, N, dtype=torch.float16, device=DEV)
+    cfgs = configs_for(M, N, 0)
+    assert len(cfgs) == g.num_configs()
+    for cfg in cfgs:
+        for epi in ("none", "relu"):
+            print(f"[parity] empty K config={cfg} epi={epi}", flush=True)
+            c = torch.full((M, N), -5.0, dtype=torch.float16, device=DEV)
+            g.gemm(a, b, epilogue=epi, out=c, config=cfg)
+            torch.cuda.synchronize()
+            assert np.all(u16(c) == 0), (cfg, epi)
+
+
+@pytest.mark.parametrize("offset", [1, 4])
+def test_unaligned_output_every_config(offset):
+    # C starting 1 or 4 elements into its buffer (2- or 8-byte aligned): the
+    # general epilogue with 2- or 8-byte stores in every configuration, next
+    # to the 16-byte operands the direct kernels need
+    M, N, K = 300, 264, 136
+    a, b = workloads.draw(M, N, K, "uniform", 40 + offset)
+    ad, bd = a.to(DEV), b.to(DEV)
+    ref = oracle.gemm(u16(a), u16(b))
+    guard = 64
+    for cfg in configs_for(M, N, K):
+        buf = torch.full((M * N + offset + guard,), -1234.0, dtype=torch.float16, device=DEV)
+        c = buf[offset:offset + M * N].view(M, N)
+        p = g.plan(M, N, K, ad.data_ptr(), bd.data_ptr(), c.data_ptr(), config=cfg)
+        assert p["vec_c"] == (1 if offset == 1 else 4)
+        print(f"[parity] unaligned C offset={offset} config={cfg}", flush=True)
+        g.gemm(ad, bd, out=c, config=cfg)
+        torch.cuda.synchronize()
+        res = oracle.compare(u16(c), ref)
+        assert res["pass"], (cfg, res)
+        host = u16(buf)
+        sentinel = np.float16(-1234.0).view(np.uint16)
+        assert np.all(host[:offset] == sentinel) and np.all(host[offset + M * N:] == sentinel)
+
+
 def test_no_writes_outside_c():
     M, N, K = 300, 264, 72
     a, b = workloads.draw(M, N, K, "uniform", 21)
