@@ -28,7 +28,7 @@ PEAK_TFLOPS = 256 * 2.4e9 * 4096 / 1e12          # 256 CUs x 2.4 GHz x 4096 flop
 METRIC = "fp16 GEMM TFLOP/s at 1 MI355X and % of dense FP16 MFMA peak"
 SPARSE_METRIC = ("2:4-sparse fp16 GEMM TFLOP/s at 1 MI355X (2 flop per product of a kept value: "
                  "M N K per call) and % of dense FP16 MFMA peak")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_8192.json")
+PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = [os.path.join(ROOT, "tiled_dense_gemm_fp16_amd", "csrc", f)
                   for f in ("gemm_f16_kernels.hip", "gemm_f16_internal.h", "gemm_f16_api.cpp")]
 
@@ -41,11 +41,15 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
+def traffic_file(workload: str) -> str:
+    return os.path.join(PROFILES, f"traffic_{workload}.json")
+
+
 def measured_traffic(workload: str, config_name: str):
     """HBM bytes per launch from the committed counter summary, if it was taken
     on the current kernel source, this workload and this configuration."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(traffic_file(workload)) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
@@ -129,7 +133,8 @@ def _counter_per_dispatch(csv_path: str, counter: str, kernel_substr: str):
 
 def traffic_from(directory: str, workload: str, config_name: str) -> int:
     """Turn rocprofv3 --pmc CSVs into HBM bytes per GEMM launch, calibrated by
-    the copy kernel, and record them with the kernel source hash."""
+    the copy kernel, and record them with the kernel source hash (the sparse
+    product runs the same kernel template, so the same kernel name matches)."""
     import glob
     import statistics
 
@@ -152,7 +157,7 @@ def traffic_from(directory: str, workload: str, config_name: str) -> int:
            "fetch_bytes_per_launch": fetch, "write_bytes_per_launch": write,
            "fetch_calibration": f_fetch, "write_calibration": f_write,
            "copy_fetch_kib": copy_fetch, "copy_write_kib": copy_write}
-    with open(TRAFFIC_FILE, "w") as f:
+    with open(traffic_file(workload), "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec), flush=True)
     return 0
@@ -198,9 +203,15 @@ def main() -> int:
         __graft_entry__.build()
 
     w = workloads.WORKLOADS[args.workload]
+    workload_name = w.name + ("_sparse_2of4" if args.sparse else "")
     if args.traffic_from:
-        p = g.plan(w.M, w.N, w.K, 1 << 20, 1 << 20, 1 << 20, config=args.config)
-        return traffic_from(args.traffic_from, w.name, g.config_name(p["config"]))
+        if args.sparse:
+            p = g.plan_sp(w.M, w.N, w.K, 1 << 20, 1 << 20, 1 << 20, 1 << 20, config=args.config)
+            name = g.sp_config_name(p["config"])
+        else:
+            p = g.plan(w.M, w.N, w.K, 1 << 20, 1 << 20, 1 << 20, config=args.config)
+            name = g.config_name(p["config"])
+        return traffic_from(args.traffic_from, workload_name, name)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     a, b = workloads.make_inputs(w)
@@ -271,7 +282,7 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic",
-        "config": {"workload": w.name + ("_sparse_2of4" if args.sparse else ""), "M": w.M, "N": w.N, "K": w.K,
+        "config": {"workload": workload_name, "M": w.M, "N": w.N, "K": w.K,
                    "epilogue": epi, "inputs": f"{w.dist} seed {w.seed}" + (", A pruned to 2:4" if args.sparse else ""),
                    "kernel": config_name},
         "pct_of_peak": round(100.0 * value / PEAK_TFLOPS, 2),
@@ -281,7 +292,7 @@ def main() -> int:
             "peak": round(PEAK_TFLOPS, 1),
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_TFLOPS, 4),
-            "traffic": None if args.sparse else measured_traffic(w.name, config_name),
+            "traffic": measured_traffic(workload_name, config_name),
             "kernel_ms_mean": round(float(launch_ms.mean()), 5),
             "kernel_ms_median": round(float(np.median(launch_ms)), 5),
             "kernel_ms_min": round(float(launch_ms.min()), 5),
@@ -298,7 +309,8 @@ def main() -> int:
         rnd = g.probe_mfma_tflops(g.PROBE_RANDOM_CHANGING + extra)
         const = g.probe_mfma_tflops(g.PROBE_CONSTANT + extra)
         out["roofline"]["mfma_only_ceiling"] = {
-            "instruction": "v_mfma_f32_16x16x32_f16" if m16 else "v_mfma_f32_32x32x16_f16",
+            "instruction": ("v_mfma_f32_16x16x32_f16" if m16 else "v_mfma_f32_32x32x16_f16")
+            + (" (dense; a v_smfmac_f32_32x32x32_f16 does as many kept products per cycle)" if args.sparse else ""),
             "random_operands": round(rnd, 1), "constant_operands": round(const, 1), "unit": "TFLOP/s",
             "achieved_over_random_ceiling": round(achieved / rnd, 3)}
     if not args.no_cpu_baseline:
