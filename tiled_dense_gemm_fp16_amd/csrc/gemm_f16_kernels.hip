@@ -53,6 +53,28 @@
 #ifndef GEMM_F16_NO_XCD_REMAP
 #define GEMM_F16_NO_XCD_REMAP 0
 #endif
+// Placement of the k step's other instructions among its MFMAs: after every
+// READ_EVERY-th MFMA come READS_PER_MFMA LDS fragment reads, and after every
+// VMEM_EVERY-th MFMA one direct tile load.  32x32x16 tiles: two reads after
+// every MFMA, a load after every MFMA (two reads: +4 % on 128x128 tiles over
+// one).  16x16x32 tiles (M16_*): one read and one load after every second
+// MFMA, measured +3 % over the 32x32 placement on 8192^3 in all four
+// layouts (one read per MFMA: +1.5 %; loads every third MFMA: the same).
+#ifndef GEMM_F16_READS_PER_MFMA
+#define GEMM_F16_READS_PER_MFMA 2
+#endif
+#ifndef GEMM_F16_VMEM_EVERY
+#define GEMM_F16_VMEM_EVERY 1
+#endif
+#ifndef GEMM_F16_M16_READS_PER_MFMA
+#define GEMM_F16_M16_READS_PER_MFMA 1
+#endif
+#ifndef GEMM_F16_M16_READ_EVERY
+#define GEMM_F16_M16_READ_EVERY 2
+#endif
+#ifndef GEMM_F16_M16_VMEM_EVERY
+#define GEMM_F16_M16_VMEM_EVERY 2
+#endif
 
 namespace gemm_f16_impl {
 
@@ -642,21 +664,23 @@ gemm_f16_kernel(KernelArgs args)
     constexpr int kMfmaPerStep = T::TM * T::TN;
     constexpr int kReadsPerStep = M16 ? (A_ROWS_K ? 1 : 2) * T::TM + (B_ROWS_K ? 1 : 2) * T::TN
                                       : T::TM + (SPARSE ? 4 : 2) * T::TN;
-    // Reads go two per MFMA (measured: +4 % for 128x128 tiles over one per
-    // MFMA, and no loss elsewhere), so that the next step's fragments are
-    // requested early in the current one.
-    constexpr int kReadsPerMfma = 2;
+    // The next step's fragment reads are requested during the current step's
+    // MFMAs, at the rate set by the placement switches above.
+    constexpr int kReadsPerMfma = M16 ? GEMM_F16_M16_READS_PER_MFMA : GEMM_F16_READS_PER_MFMA;
+    constexpr int kReadEvery = M16 ? GEMM_F16_M16_READ_EVERY : 1;
+    static_assert(!M16 || kMfmaPerStep / kReadEvery * kReadsPerMfma >= kReadsPerStep, "every read has a slot");
+    constexpr int kVmemEvery = M16 ? GEMM_F16_M16_VMEM_EVERY : GEMM_F16_VMEM_EVERY;
     auto interleave = [&](int n_vmem, int n_dswrite) {
 #pragma unroll
         for (int i = 0; i < kMfmaPerStep; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // one MFMA
 #pragma unroll
             for (int r = 0; r < kReadsPerMfma; ++r)
-                if (i * kReadsPerMfma + r < kReadsPerStep)
+                if (i % kReadEvery == 0 && (i / kReadEvery) * kReadsPerMfma + r < kReadsPerStep)
                     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
             if (i < n_dswrite)
                 __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);      // one LDS write
-            if (i < n_vmem)
+            if (i % kVmemEvery == 0 && i / kVmemEvery < n_vmem)
                 __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);      // one global load
         }
     };
