@@ -63,6 +63,9 @@
 #ifndef GEMM_F16_READS_PER_MFMA
 #define GEMM_F16_READS_PER_MFMA 2
 #endif
+#ifndef GEMM_F16_READ_EVERY
+#define GEMM_F16_READ_EVERY 1
+#endif
 #ifndef GEMM_F16_VMEM_EVERY
 #define GEMM_F16_VMEM_EVERY 1
 #endif
@@ -666,8 +669,11 @@ gemm_f16_kernel(KernelArgs args)
                                       : T::TM + (SPARSE ? 4 : 2) * T::TN;
     // The next step's fragment reads are requested during the current step's
     // MFMAs, at the rate set by the placement switches above.
-    constexpr int kReadsPerMfma = M16 ? GEMM_F16_M16_READS_PER_MFMA : GEMM_F16_READS_PER_MFMA;
-    constexpr int kReadEvery = M16 ? GEMM_F16_M16_READ_EVERY : 1;
+    // the 8-wave register-staged tile takes one read per MFMA (+2-3 % on the
+    // 3000x5000x4100 workload it serves; the 4-wave staged 128x128 tile lost 5 %)
+    constexpr int kReadsPerMfma = M16 ? GEMM_F16_M16_READS_PER_MFMA
+                                      : (!DIRECT && T::kWaves == 8) ? 1 : GEMM_F16_READS_PER_MFMA;
+    constexpr int kReadEvery = M16 ? GEMM_F16_M16_READ_EVERY : GEMM_F16_READ_EVERY;
     static_assert(!M16 || kMfmaPerStep / kReadEvery * kReadsPerMfma >= kReadsPerStep, "every read has a slot");
     constexpr int kVmemEvery = M16 ? GEMM_F16_M16_VMEM_EVERY : GEMM_F16_VMEM_EVERY;
     auto interleave = [&](int n_vmem, int n_dswrite) {
