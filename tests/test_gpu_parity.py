@@ -82,6 +82,47 @@ def test_ragged_shapes(shape, epilogue):
         check(a, b, epilogue, config=c, label=f"config {g.config_name(c)}")
 
 
+# A's rows only 4-byte aligned (K = 2, 4 or 6 mod 8) while B's rows allow
+# 16-byte loads (N % 8 == 0): the configuration that moves A with 4-byte
+# direct loads; K tails end inside a 16-byte chunk.
+A4 = "256x256x64_s2_direct_m16_a4"
+A4_SHAPES = [(300, 264, 130), (520, 392, 198), (257, 520, 66), (64, 64, 2), (511, 264, 4100)]
+
+
+def a4_config():
+    return [c for c in range(g.num_configs()) if g.config_name(c) == A4][0]
+
+
+@pytest.mark.parametrize("shape", A4_SHAPES)
+@pytest.mark.parametrize("epilogue", ["none", "relu"])
+def test_a_rows_4byte_direct_loads(shape, epilogue):
+    M, N, K = shape
+    c = a4_config()
+    p = g.plan(M, N, K, 1 << 20, 1 << 20, 1 << 20, config=c)
+    assert p["vec_a"] == 2 and p["vec_b"] == 8 and p["direct_lds"] == 1
+    a, b = workloads.draw(M, N, K, "uniform", 3 * M + N + K)
+    check(a, b, epilogue, config=c, label="A 4-byte direct")
+
+
+def test_a_rows_4byte_direct_loads_nt_offset_pointer():
+    """B given N x K with a 16-byte aligned pitch, A's pointer only 4-byte
+    aligned (a view two elements into a buffer)."""
+    M, N, K = 300, 264, 136
+    c = a4_config()
+    a, b = workloads.draw(M, N, K, "uniform", 1234)
+    buf = torch.zeros(M * K + 8, dtype=torch.float16, device=DEV)
+    a_dev = buf[2:2 + M * K].view(M, K)
+    a_dev.copy_(a.to(DEV))
+    bt = b.t().contiguous().to(DEV)
+    p = g.plan(M, N, K, a_dev.data_ptr(), bt.data_ptr(), 1 << 20, config=c, trans_b=True)
+    assert p["vec_a"] == 2 and p["direct_lds"] == 1
+    print(f"[parity] A 4-byte direct, NT, A pointer offset by 4 bytes, {M}x{N}x{K}", flush=True)
+    out = g.gemm(a_dev, bt, config=c, trans_b=True)
+    torch.cuda.synchronize()
+    res = oracle.compare(u16(out), oracle.gemm(u16(a), u16(b)))
+    assert res["pass"], res
+
+
 def test_misaligned_pointers():
     # operands and output that start one element into a buffer are only
     # 2-byte aligned; with K, N not multiples of 8 every vector width drops

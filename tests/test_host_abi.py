@@ -113,9 +113,11 @@ def test_plan_geometry_and_vector_widths():
     assert p["tiles_m"] == -(-3000 // p["block_m"]) and p["tiles_n"] == -(-5000 // p["block_n"])
     assert p["grid"] == p["tiles_m"] * p["tiles_n"]
     assert p["k_tiles"] == -(-4100 // p["block_k"])
-    assert p["vec_a"] == 4                       # K = 4100: rows only 8-byte aligned
+    # K = 4100: A's rows only 8-byte aligned; B's allow 16-byte loads, so A
+    # moves straight to LDS in 4-byte pieces (measured: +11 % over 8-byte
+    # register-staged vectors on this shape)
+    assert p["vec_a"] == 2 and p["direct_lds"] == 1
     assert p["vec_b"] == 8 and p["vec_c"] == 8          # N = 5000: 16-byte stores of C
-    assert p["direct_lds"] == 0                  # 16-byte direct loads need 16-byte rows
     assert p["flops"] == 2.0 * 3000 * 5000 * 4100
     assert p["min_bytes"] == 2.0 * (3000 * 4100 + 4100 * 5000 + 3000 * 5000)
     # odd pitches and 2-byte-aligned pointers
@@ -237,13 +239,15 @@ def test_tuned_table_drives_the_automatic_choice():
         key = (lm, ln, lk, ta, tb, aligned)
         assert key not in seen
         seen.add(key)
-        pad = 0 if aligned else 4
-        M, N, K = (1 << lm) + pad, (1 << ln) + pad, (1 << lk) + pad
+        # class 1: aligned pitches; 0: every pitch off by 4 elements; 2: only K (A's pitch)
+        pm, pn, pk = {1: (0, 0, 0), 0: (4, 4, 4), 2: (0, 0, 4)}[aligned]
+        M, N, K = (1 << lm) + pm, (1 << ln) + pn, (1 << lk) + pk
         p = g.plan(M, N, K, FAKE, FAKE, FAKE, trans_a=bool(ta), trans_b=bool(tb))
         assert p["config"] == cfg, (key, p["config"])
         want = g.plan(M, N, K, FAKE, FAKE, FAKE, config=cfg, trans_a=bool(ta), trans_b=bool(tb), splits=splits)
         assert p["splits"] == want["splits"] and p["k_split"] == want["k_split"], key
-        assert (p["vec_a"] == 8 and p["vec_b"] == 8) == bool(aligned)
+        assert (p["vec_a"] == 8 and p["vec_b"] == 8) == (aligned == 1)
+        assert aligned != 2 or (not ta and not tb and p["vec_b"] == 8)
     # far from every swept shape the analytic model decides (no table hit):
     # a deep K under a one-tile output is split
     p = g.plan(24, 24, 1 << 20, FAKE, FAKE, FAKE)

@@ -20,28 +20,29 @@ namespace gemm_f16_impl {
 // (512 per lane per SIMD, VGPRs + AGPRs as the compiler reports them).
 constexpr int kNN = 1, kNT = 2, kAllLayouts = 15;   // masks over bit 2 trans_a + trans_b
 const ConfigDesc kConfigs[kNumConfigs] = {
-    {"256x256x64_s2_direct", 256, 256, 64, 2, 4, true, 8, kAllLayouts, 1},
-    {"256x128x64_s3_direct", 256, 128, 64, 3, 4, true, 8, kAllLayouts, 1},
-    {"128x128x64_s3_direct", 128, 128, 64, 3, 4, true, 8, kAllLayouts, 1},
-    {"128x128x32_s2_staged", 128, 128, 32, 2, 4, false, 1, kAllLayouts, 2},
-    {"64x64x64_s2_staged", 64, 64, 64, 2, 4, false, 1, kAllLayouts, 5},
-    {"256x256x32_s4_direct", 256, 256, 32, 4, 4, true, 8, kNN, 1},
-    {"256x256x32_s5_direct", 256, 256, 32, 5, 4, true, 8, kNN, 1},
-    {"256x256x64_s2_direct_w8n", 256, 256, 64, 2, 8, true, 8, kAllLayouts, 1},
-    {"256x256x32_s5_direct_w8n", 256, 256, 32, 5, 8, true, 8, kNN, 1},
-    {"256x256x64_s2_direct_w8m", 256, 256, 64, 2, 8, true, 8, kNN, 1},
-    {"256x256x64_s2_staged_w8", 256, 256, 64, 2, 8, false, 4, kAllLayouts, 1},
-    {"256x128x64_s2_staged", 256, 128, 64, 2, 4, false, 4, kNN, 1},
-    {"256x256x64_s2_direct_m16", 256, 256, 64, 2, 4, true, 8, kAllLayouts, 1},
+    {"256x256x64_s2_direct", 256, 256, 64, 2, 4, true, 8, 8, kAllLayouts, 1},
+    {"256x128x64_s3_direct", 256, 128, 64, 3, 4, true, 8, 8, kAllLayouts, 1},
+    {"128x128x64_s3_direct", 128, 128, 64, 3, 4, true, 8, 8, kAllLayouts, 1},
+    {"128x128x32_s2_staged", 128, 128, 32, 2, 4, false, 1, 1, kAllLayouts, 2},
+    {"64x64x64_s2_staged", 64, 64, 64, 2, 4, false, 1, 1, kAllLayouts, 5},
+    {"256x256x32_s4_direct", 256, 256, 32, 4, 4, true, 8, 8, kNN, 1},
+    {"256x256x32_s5_direct", 256, 256, 32, 5, 4, true, 8, 8, kNN, 1},
+    {"256x256x64_s2_direct_w8n", 256, 256, 64, 2, 8, true, 8, 8, kAllLayouts, 1},
+    {"256x256x32_s5_direct_w8n", 256, 256, 32, 5, 8, true, 8, 8, kNN, 1},
+    {"256x256x64_s2_direct_w8m", 256, 256, 64, 2, 8, true, 8, 8, kNN, 1},
+    {"256x256x64_s2_staged_w8", 256, 256, 64, 2, 8, false, 4, 4, kAllLayouts, 1},
+    {"256x128x64_s2_staged", 256, 128, 64, 2, 4, false, 4, 4, kNN, 1},
+    {"256x256x64_s2_direct_m16", 256, 256, 64, 2, 4, true, 8, 8, kAllLayouts, 1},
+    {"256x256x64_s2_direct_m16_a4", 256, 256, 64, 2, 4, true, 2, 8, kNN | kNT, 1},
 };
 
 // Sparse configurations (2:4 A): fields as above; every one takes A as
 // compressed values + positions and B as K x N.
 const ConfigDesc kSpConfigs[kNumSpConfigs] = {
-    {"sp_256x256x64_s3_w8", 256, 256, 64, 3, 8, true, 8, kNN | kNT, 1},
-    {"sp_128x128x64_s3", 128, 128, 64, 3, 4, true, 8, kNN | kNT, 1},
-    {"sp_256x256x64_s3", 256, 256, 64, 3, 4, true, 8, kNN | kNT, 1},
-    {"sp_256x256x64_s3_spread", 256, 256, 64, 3, 4, true, 8, kNN | kNT, 1},
+    {"sp_256x256x64_s3_w8", 256, 256, 64, 3, 8, true, 8, 8, kNN | kNT, 1},
+    {"sp_128x128x64_s3", 128, 128, 64, 3, 4, true, 8, 8, kNN | kNT, 1},
+    {"sp_256x256x64_s3", 256, 256, 64, 3, 4, true, 8, 8, kNN | kNT, 1},
+    {"sp_256x256x64_s3_spread", 256, 256, 64, 3, 4, true, 8, 8, kNN | kNT, 1},
 };
 
 namespace {
@@ -102,6 +103,7 @@ double config_efficiency(int c)
 {
     switch (c) {
     case 12: return 1.06;   // 256x256x64 direct, 4 waves, 16x16x32 MFMAs
+    case 13: return 0.95;   // the same with 4-byte loads of A (A rows 4-byte aligned)
     case 7: return 1.00;    // 256x256x64 direct, 8 waves
     case 0: return 0.97;    // 256x256x64 direct, 4 waves
     case 1: return 0.90;    // 256x128x64 direct
@@ -118,14 +120,15 @@ bool config_fits(int c, int va, int vb, bool ta, bool tb)
 {
     if (!(kConfigs[c].layouts & (1 << (2 * (int)ta + (int)tb))))
         return false;
-    return va >= kConfigs[c].min_vec && vb >= kConfigs[c].min_vec;
+    return va >= kConfigs[c].min_vec && vb >= kConfigs[c].min_vec_b;
 }
 
-// Vector width a configuration loads with, given the widest the pitch allows.
-int kernel_vec(const ConfigDesc &d, int v, bool transposed)
+// Vector width a configuration loads an operand with (is_a: A, else B),
+// given the widest the pitch allows.
+int kernel_vec(const ConfigDesc &d, int v, bool transposed, bool is_a)
 {
     if (d.direct)
-        return 8;
+        return is_a ? d.min_vec : d.min_vec_b;
     if (d.min_vec >= 4)
         return v >= 8 ? 8 : 4;              // wide register-staged tiles
     if (transposed)
@@ -171,8 +174,8 @@ void fill_plan(int c, int64_t M, int64_t N, int64_t K, int va, int vb, int vc, b
     p->stages = d.stages;
     p->threads = 64 * d.waves;
     p->direct_lds = d.direct ? 1 : 0;
-    p->vec_a = kernel_vec(d, va, tr);
-    p->vec_b = kernel_vec(d, vb, tr);
+    p->vec_a = kernel_vec(d, va, tr, true);
+    p->vec_b = kernel_vec(d, vb, tr, false);
     p->vec_c = vc;
     p->tiles_m = ceil_div(M, d.block_m);
     p->tiles_n = ceil_div(N, d.block_n);
@@ -195,7 +198,8 @@ void fill_plan(int c, int64_t M, int64_t N, int64_t K, int va, int vb, int vc, b
 struct TunedEntry {
     int lm, ln, lk;        // log2 of the swept M, N, K
     int trans_a, trans_b;
-    int aligned;           // 1: pitches allowed 16-byte loads of both operands
+    int aligned;           // 1: pitches allowed 16-byte loads of both operands; 2: of B only,
+                           // A's rows 4-byte aligned (A . B and A . B^T); 0: otherwise
     int config;
     int splits;
     double tflops;
@@ -208,7 +212,7 @@ const TunedEntry kTuned[] = {
 // The tuned entry for the nearest swept shape (in log2 M, N, K) with the same
 // layout and alignment, if one lies within a factor of two overall; null
 // otherwise.
-const TunedEntry *tuned_entry(int64_t M, int64_t N, int64_t K, bool ta, bool tb, bool aligned, int va, int vb)
+const TunedEntry *tuned_entry(int64_t M, int64_t N, int64_t K, bool ta, bool tb, int aligned, int va, int vb)
 {
     const double lm = log2((double)(M > 0 ? M : 1)), ln = log2((double)(N > 0 ? N : 1));
     const double lk = log2((double)(K > 0 ? K : 1));
@@ -217,7 +221,7 @@ const TunedEntry *tuned_entry(int64_t M, int64_t N, int64_t K, bool ta, bool tb,
     for (const TunedEntry &e : kTuned) {
         if (e.config < 0)
             break;
-        if (e.trans_a != (int)ta || e.trans_b != (int)tb || e.aligned != (int)aligned)
+        if (e.trans_a != (int)ta || e.trans_b != (int)tb || e.aligned != aligned)
             continue;
         const double d = sqrt((lm - e.lm) * (lm - e.lm) + (ln - e.ln) * (ln - e.ln) + (lk - e.lk) * (lk - e.lk));
         if (d < best_d && e.config < kNumConfigs && config_fits(e.config, va, vb, ta, tb)) {
@@ -320,7 +324,13 @@ gemm_f16_status_t make_plan(int64_t M, int64_t N, int64_t K, const void *A, bool
     int c = config;
     Split sp = {1, K};
     if (c == GEMM_F16_CONFIG_AUTO) {
-        const TunedEntry *e = tuned_entry(M, N, K, ta, tb, va == 8 && vb == 8, va, vb);
+        // alignment class of the table: both operands 16-byte (1), only B (2,
+        // A stored M x K with 4-byte rows), neither (0); a class-2 shape with
+        // no class-2 entry near it takes the class-0 entries
+        const int cls = (va == 8 && vb == 8) ? 1 : (!ta && va >= 2 && vb == 8) ? 2 : 0;
+        const TunedEntry *e = tuned_entry(M, N, K, ta, tb, cls, va, vb);
+        if (!e && cls == 2)
+            e = tuned_entry(M, N, K, ta, tb, 0, va, vb);
         if (e && (splits == GEMM_F16_SPLITS_AUTO || splits == e->splits)) {
             c = e->config;
             sp = split_geometry(kConfigs[c], K, e->splits);

@@ -32,17 +32,19 @@ struct ConfigDesc {
     int stages;
     int waves;            // wave64s per workgroup (4: one per SIMD, 8: two)
     bool direct;          // operands move global -> LDS with buffer_load ... lds
-    int min_vec;          // smallest vector width (elements) of A and B loads it accepts
+    int min_vec;          // smallest vector width (elements) of A loads it accepts
+    int min_vec_b;        // ... of B loads
     int layouts;          // layouts compiled, bit 2 trans_a + trans_b: 1 = A . B only, 15 = all four
     int occupancy;        // workgroups resident per CU (LDS and register limits)
 };
 
-constexpr int kNumConfigs = 13;
+constexpr int kNumConfigs = 14;
 extern const ConfigDesc kConfigs[kNumConfigs];
 
 // Launch configuration `config` with `grid` workgroups on `s`.
 // va / vb: elements per global load of A / B (8, 4, 2 or 1; direct configs
-// require 8, transposed layouts of register-staged configs 8 or 1).
+// load 8, or A 2 where the configuration's min_vec is 2; transposed layouts
+// of register-staged configs 8 or 1).
 // trans_a: A is stored K x M; trans_b: B is stored N x K.  Returns the
 // launch status.
 hipError_t launch(int config, const KernelArgs &a, int va, int vb, bool trans_a, bool trans_b, int64_t grid,

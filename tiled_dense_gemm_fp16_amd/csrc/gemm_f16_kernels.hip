@@ -275,19 +275,28 @@ struct Operand {
     static constexpr int CHUNKS = ROW / 8;                   // 16-byte chunks per row
     static constexpr int WAVES = THREADS / 64;
     static_assert(CHUNKS >= 2 && (CHUNKS & (CHUNKS - 1)) == 0, "rows of a power-of-two number of chunks");
-    // direct: one wave instruction fills 1 KiB of LDS, lane l at byte 16 l
-    static constexpr int DMA = STAGE * 2 / (THREADS * 16);   // loads per thread per stage
-    static_assert(!DIRECT || STAGE * 2 % (THREADS * 16) == 0, "whole block-wide 16-byte loads");
-    static_assert(!DIRECT || V == 8, "direct loads move 16-byte chunks");
-    static_assert(!DIRECT || ROW * 2 <= 1024, "a row fits in one wave's KiB");
-    static constexpr int ROWS_PER_KB = DIRECT ? 1024 / (ROW * 2) : 1;
+    // direct: each lane moves WB bytes per load, so one wave instruction
+    // fills 64 WB bytes of LDS, lane l at byte WB l.  16-byte chunks, or
+    // 4-byte pieces (V = 2) for a k-rows operand whose rows are only 4-byte
+    // aligned; the LDS layout is the same either way.
+    static constexpr int WB = DIRECT ? 2 * V : 16;
+    static constexpr int WAVE_BYTES = 64 * WB;
+    static constexpr int DMA = STAGE * 2 / (THREADS * WB);   // loads per thread per stage
+    static_assert(!DIRECT || STAGE * 2 % (THREADS * WB) == 0, "whole block-wide loads");
+    static_assert(!DIRECT || V == 8 || (V == 2 && ROWS_K && CHUNKS == 8),
+                  "direct loads move 16-byte chunks, or 4-byte pieces of 128-byte k rows");
+    static_assert(!DIRECT || ROW * 2 <= WAVE_BYTES, "a row fits in one wave instruction");
+    static constexpr int ROWS_PER_LOAD = DIRECT ? WAVE_BYTES / (ROW * 2) : 1;
     // consecutive direct loads of a thread are ROW_STEP rows apart, a multiple
     // of the swizzle period, so they share one column and one base offset
-    static constexpr int ROW_STEP = WAVES * ROWS_PER_KB;
-    // swz_b16 repeats every 16 rows, but its bit from row bit 3 flips every 8:
-    // loads whose row step is an odd multiple of 8 alternate between two columns
-    static constexpr bool ALT_COLUMN = DIRECT && !ROWS_K && M16 && (ROW_STEP / 8) % 2 == 1;
-    static_assert(!DIRECT || ROW_STEP % (ROWS_K ? 16 : (M16 ? 8 : 4)) == 0, "row step keeps the swizzle phase");
+    static constexpr int ROW_STEP = WAVES * ROWS_PER_LOAD;
+    // ... except: swz_b16 repeats every 16 rows, but its bit from row bit 3
+    // flips every 8, and swz_a of 8-chunk rows (period 16) flips its bit 2
+    // with row bit 3; loads whose row step is an odd multiple of 8 then
+    // alternate between two columns
+    static constexpr bool ALT_COLUMN = DIRECT && (ROWS_K ? CHUNKS == 8 : M16) && (ROW_STEP / 8) % 2 == 1;
+    static_assert(!DIRECT || ROW_STEP % (ROWS_K ? (CHUNKS == 8 ? 8 : 16) : (M16 ? 8 : 4)) == 0,
+                  "row step keeps the swizzle phase");
     // staged: vectors of V halves through registers
     static constexpr int VECS = STAGE / V / THREADS;
     static_assert(DIRECT || STAGE % (V * THREADS) == 0, "staged tiles split evenly over the threads");
@@ -312,7 +321,8 @@ struct Operand {
     __amdgpu_buffer_rsrc_t panel;   // ROWS_K: the workgroup's BMN rows
     uint32_t off0, step;   // direct: byte offset of the first chunk, distance between loads
     uint32_t alt;          // direct, ALT_COLUMN: offset change (mod 2^32) on odd loads
-    int kcol0;             // direct, ROWS_K: k column of the thread's chunks
+    int kcol0;             // direct, ROWS_K: k column of the thread's even loads
+    int kcol1;             // ... and of its odd loads
     uint32_t offv[VEC_DIV];
     int kcolv[VEC_DIV];
     int ldsv[VEC_DIV];
@@ -331,19 +341,22 @@ struct Operand {
             panel = make_rsrc(X + (int64_t)mn0 * ld, (uint32_t)rows * (uint32_t)ld * 2u);
         }
         if constexpr (DIRECT) {
-            const int byte = wave * 1024 + lane * 16;
+            const int byte = wave * WAVE_BYTES + lane * WB;
             const int r = byte / (ROW * 2);
-            const int c = (((byte % (ROW * 2)) / 16) ^ swz(r)) * 8;
+            const int pos = (byte % (ROW * 2)) / 16;        // 16-byte chunk of the LDS row
+            const int sub = (byte % 16) / 2;                // element inside it (4-byte pieces)
+            const int c = (pos ^ swz(r)) * 8 + sub;
             kcol0 = c;
             off0 = ((uint32_t)r * (uint32_t)ld + (uint32_t)(ROWS_K ? c : mn0 + c)) * 2u;
             step = (uint32_t)ROW_STEP * (uint32_t)ld * 2u;
             if constexpr (ALT_COLUMN) {
-                // row r + ROW_STEP flips swz_b16's 2-chunk term: the chunk moves by +-2
-                const int pos = (byte % (ROW * 2)) / 16;
-                const int c_odd = (pos ^ swz(r + ROW_STEP)) * 8;
+                // row r + ROW_STEP flips one bit of the row's XOR: the chunk moves
+                const int c_odd = (pos ^ swz(r + ROW_STEP)) * 8 + sub;
                 alt = (uint32_t)((c_odd - c) * 2);
+                kcol1 = c_odd;
             } else {
                 alt = 0;
+                kcol1 = c;
             }
         } else {
 #pragma unroll
@@ -376,15 +389,20 @@ struct Operand {
             rs = make_rsrc(X + (int64_t)k0 * ld, (uint32_t)rows * (uint32_t)ld * 2u);
         }
         if constexpr (DIRECT) {
-            // ROWS_K: K % 8 == 0, so a chunk is wholly inside or wholly past the row end
-            const uint32_t mask = ROWS_K ? oob_unless(k0 + kcol0 < K) : 0u;
+            // ROWS_K: K % V == 0, so a load is wholly inside or wholly past the row end
+            const uint32_t mask0 = ROWS_K ? oob_unless(k0 + kcol0 < K) : 0u;
+            const uint32_t mask1 = ROWS_K ? oob_unless(k0 + kcol1 < K) : 0u;
 #pragma unroll
             for (int i = 0; i < DMA; ++i) {
                 if (i * nparts / DMA != part)
                     continue;
-                const uint32_t off = (off0 + shift + (uint32_t)i * step + ((ALT_COLUMN && (i & 1)) ? alt : 0u)) | mask;
-                LDS_AS void *d = (LDS_AS void *)(dst + (wave + WAVES * i) * 512);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d, 16, off, 0, 0, 0);
+                const bool odd = ALT_COLUMN && (i & 1);
+                const uint32_t off = (off0 + shift + (uint32_t)i * step + (odd ? alt : 0u)) | (odd ? mask1 : mask0);
+                LDS_AS void *d = (LDS_AS void *)(dst + (wave + WAVES * i) * (WAVE_BYTES / 2));
+                if constexpr (WB == 16)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d, 16, off, 0, 0, 0);
+                else
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d, 4, off, 0, 0, 0);
             }
         } else {
             (void)dst;
@@ -1214,6 +1232,12 @@ static hipError_t launch_transposed(int config, const KernelArgs &a, int va, int
     case 7: return launch_one<256, 256, 64, 2, 4, 2, true, 8, 8, AR, BR, 2>(a, grid, s);
     case 10: return launch_staged_wide<256, 256, 64, 2, 4, 2, AR, BR>(a, va, vb, grid, s);
     case 12: return launch_one<256, 256, 64, 2, 2, 2, true, 8, 8, AR, BR, 2, false, true>(a, grid, s);
+    case 13:
+        // A stored M x K with 4-byte direct loads: B given N x K (NT) only
+        if constexpr (AR)
+            return launch_one<256, 256, 64, 2, 2, 2, true, 2, 8, AR, BR, 2, false, true>(a, grid, s);
+        else
+            return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
     }
 }
@@ -1244,6 +1268,7 @@ hipError_t launch(int config, const KernelArgs &a, int va, int vb, bool trans_a,
     case 10: return launch_staged_wide<256, 256, 64, 2, 4, 2, AR, BR>(a, va, vb, grid, s);
     case 11: return launch_staged_wide<256, 128, 64, 2, 2, 2, AR, BR>(a, va, vb, grid, s);
     case 12: return launch_one<256, 256, 64, 2, 2, 2, true, 8, 8, AR, BR, 2, false, true>(a, grid, s);
+    case 13: return launch_one<256, 256, 64, 2, 2, 2, true, 2, 8, AR, BR, 2, false, true>(a, grid, s);
     default: return hipErrorInvalidValue;
     }
 }

@@ -85,19 +85,22 @@ def _time(fn, flops, target_s=0.03):
     return flops / (ms * 1e-3) / 1e12
 
 
-def sweep(sizes_mn, sizes_k, layouts, log):
+def sweep(sizes_mn, sizes_k, layouts, log, classes=(1, 0, 2)):
     import torch
 
     import tiled_dense_gemm_fp16_amd as g
 
     rows = []
-    for aligned in (True, False):
+    for aligned in classes:
         for M in sizes_mn:
             for N in sizes_mn:
                 for K in sizes_k:
-                    # misaligned: every pitch odd by 4 elements (8-byte rows only)
-                    m, n, k = (M, N, K) if aligned else (M + 4, N + 4, K + 4)
+                    # class 0: every pitch off by 4 elements (8-byte rows only);
+                    # class 2: only K (A's pitch as M x K), for A . B
+                    m, n, k = {1: (M, N, K), 0: (M + 4, N + 4, K + 4), 2: (M, N, K + 4)}[aligned]
                     for ta, tb in layouts:
+                        if aligned == 2 and (ta or tb):
+                            continue
                         a = torch.randn((k, m) if ta else (m, k), device="cuda").half()
                         b = (torch.randn((n, k) if tb else (k, n), device="cuda") / math.sqrt(k)).half()
                         c = torch.empty((m, n), device="cuda", dtype=torch.float16)
@@ -121,7 +124,7 @@ def sweep(sizes_mn, sizes_k, layouts, log):
                                 if best is None or tf > results[best]:
                                     best = key
                         rec = {"M": m, "N": n, "K": k, "trans_a": int(ta), "trans_b": int(tb),
-                               "aligned": int(aligned), "best": best, "tflops": results}
+                               "aligned": aligned, "best": best, "tflops": results}
                         rows.append(rec)
                         print(json.dumps(rec), file=log, flush=True)
                         if log is not sys.stdout:
@@ -137,7 +140,8 @@ def write_table(rows, path, note):
         "// tiled_dense_gemm_fp16_amd/tune.py; do not edit by hand.",
         f"// {note}",
         "// fields: log2 M, log2 N, log2 K (of the swept shape), trans_a, trans_b,",
-        "// pitches aligned to 16 bytes (1) or not (0), best configuration, K splits, its TFLOP/s",
+        "// pitches aligned to 16 bytes (1), only B's (2: A's rows 4-byte aligned) or neither (0),",
+        "// best configuration, K splits, its TFLOP/s",
     ]
     for r in rows:
         if r["best"] is None:
@@ -154,6 +158,8 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--layouts", default="nn,nt,tn,tt",
                     help="comma-separated layouts to sweep (n: as stored, t: given transposed)")
+    ap.add_argument("--classes", default="1,0,2",
+                    help="alignment classes to sweep: 1 aligned, 0 every pitch off by 4, 2 only K off by 4 (NN)")
     ap.add_argument("--out", default=OUT)
     ap.add_argument("--log", default=None, help="also write every measurement (JSON lines) here")
     ap.add_argument("--from-log", nargs="+", default=None, metavar="LOG",
@@ -172,7 +178,7 @@ def main() -> int:
     codes = {"nn": (False, False), "nt": (False, True), "tn": (True, False), "tt": (True, True)}
     layouts = [codes[x] for x in args.layouts.split(",")]
     log = open(args.log, "w") if args.log else sys.stdout
-    rows = sweep(SIZES_MN, SIZES_K, layouts, log)
+    rows = sweep(SIZES_MN, SIZES_K, layouts, log, tuple(int(x) for x in args.classes.split(",")))
     dev = torch.cuda.get_device_properties(0)
     note = (f"swept {datetime.date.today().isoformat()} on {dev.name} "
             f"({getattr(dev, 'gcnArchName', '?')}, {dev.multi_processor_count} CUs)")
