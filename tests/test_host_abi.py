@@ -215,6 +215,25 @@ def test_python_wrapper_argument_checks():
         g.gemm(a.float(), a)
 
 
+def test_only_a_misaligned_takes_four_byte_direct_loads():
+    """A stored M x K whose rows or pointer are only 4-byte aligned, B's
+    16-byte aligned: A moves straight to LDS in 4-byte pieces.  An odd K, or
+    A given K x M, never takes that path."""
+    a4 = "256x256x64_s2_direct_m16_a4"
+    for kw in ({}, {"trans_b": True}):
+        p = g.plan(8192, 8192, 8192, FAKE + 4, FAKE, FAKE, **kw)          # A's pointer 4-byte aligned
+        assert g.config_name(p["config"]) == a4 and (p["vec_a"], p["vec_b"], p["direct_lds"]) == (2, 8, 1), kw
+    p = g.plan(8192, 8192, 8194, FAKE, FAKE, FAKE)                        # A's rows 4-byte aligned
+    assert g.config_name(p["config"]) == a4 and p["vec_a"] == 2
+    p = g.plan(8192, 8192, 8193, FAKE, FAKE, FAKE)                        # odd K: 2-byte rows
+    assert g.config_name(p["config"]) != a4 and p["vec_a"] == 1
+    p = g.plan(8192, 8192, 8192, FAKE + 4, FAKE, FAKE, trans_a=True)      # A given K x M
+    assert g.config_name(p["config"]) != a4
+    with pytest.raises(g.GemmError):                                       # B's rows must allow 16 bytes
+        g.plan(8192, 8196, 8194, FAKE, FAKE, FAKE, config=[c for c in range(g.num_configs())
+                                                            if g.config_name(c) == a4][0])
+
+
 TUNED = os.path.join(ROOT, "tiled_dense_gemm_fp16_amd", "csrc", "gemm_f16_tuned.inc")
 
 
