@@ -9,8 +9,12 @@ The roofline entry reports the GEMM kernel's achieved TFLOP/s (2 M N K per
 launch over the average launch duration, timed with events on the launch
 stream) against MI355X's dense FP16 MFMA peak; ``traffic`` is the HBM bytes
 per launch measured by rocprofv3 counters for this exact kernel source (null
-when the source has changed since they were taken).  The CPU baseline times
-the plain oracle on a bounded block of the same product.
+when the source has changed since they were taken).  ``clock_normalised`` is
+the fraction of the peak at the clock the chip actually ran: the matrix
+cores' busy cycles over the CUs' busy cycles from the same counter runs, with
+the average shader clock that fraction and the live throughput imply (null
+under the same condition).  The CPU baseline times the plain oracle on a
+bounded block of the same product.
 """
 from __future__ import annotations
 
@@ -24,7 +28,8 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_TFLOPS = 256 * 2.4e9 * 4096 / 1e12          # 256 CUs x 2.4 GHz x 4096 flop/clk/CU (dense FP16 MFMA)
+PEAK_FLOPS_PER_CLOCK = 256 * 4096                   # 256 CUs x 4096 flop/clk/CU (dense FP16 MFMA)
+PEAK_TFLOPS = PEAK_FLOPS_PER_CLOCK * 2.4e9 / 1e12  # at the 2.4 GHz peak clock
 METRIC = "fp16 GEMM TFLOP/s at 1 MI355X and % of dense FP16 MFMA peak"
 SPARSE_METRIC = ("2:4-sparse fp16 GEMM TFLOP/s at 1 MI355X (2 flop per product of a kept value: "
                  "M N K per call) and % of dense FP16 MFMA peak")
@@ -45,9 +50,9 @@ def traffic_file(workload: str) -> str:
     return os.path.join(PROFILES, f"traffic_{workload}.json")
 
 
-def measured_traffic(workload: str, config_name: str):
-    """HBM bytes per launch from the committed counter summary, if it was taken
-    on the current kernel source, this workload and this configuration."""
+def measured_counters(workload: str, config_name: str):
+    """The committed counter summary of this workload, if it was taken on the
+    current kernel source and this configuration; else None."""
     try:
         with open(traffic_file(workload)) as f:
             t = json.load(f)
@@ -56,7 +61,30 @@ def measured_traffic(workload: str, config_name: str):
     if (t.get("kernel_sha256") != kernel_source_hash() or t.get("workload") != workload
             or t.get("kernel_config") != config_name):
         return None
+    return t
+
+
+def measured_traffic(workload: str, config_name: str):
+    """HBM bytes per launch from the committed counter summary (see measured_counters)."""
+    t = measured_counters(workload, config_name)
+    if t is None:
+        return None
     return float(t["fetch_bytes_per_launch"]) + float(t["write_bytes_per_launch"])
+
+
+def clock_normalised(workload: str, config_name: str, achieved_tflops: float):
+    """Fraction of the peak at the clock the chip actually ran: the matrix
+    cores' busy cycles over the CUs' busy cycles (SQ_VALU_MFMA_BUSY_CYCLES per
+    SIMD, SQ_BUSY_CU_CYCLES per CU, from the committed counter summary of the
+    same kernel source), and the average shader clock that this fraction and
+    the live throughput imply (CUs x 4096 flop per cycle at full rate)."""
+    t = measured_counters(workload, config_name)
+    if t is None or "mfma_busy_frac" not in t:
+        return None
+    frac = float(t["mfma_busy_frac"])
+    return {"frac": round(frac, 4),
+            "implied_sclk_ghz": round(achieved_tflops * 1e12 / (frac * PEAK_FLOPS_PER_CLOCK) / 1e9, 3),
+            "counters": "SQ_VALU_MFMA_BUSY_CYCLES / (4 SQ_BUSY_CU_CYCLES), rocprofv3 --pmc, same kernel source"}
 
 
 def cpu_baseline(a, b, w, budget_s: float, sparse=None):
@@ -147,6 +175,23 @@ def traffic_from(directory: str, workload: str, config_name: str) -> int:
             raise SystemExit(f"no {counter} rows for {kernel!r} in {paths[0]}")
         return statistics.median(vals)
 
+    def busy_fraction(kernel):
+        """Median over dispatches of the matrix cores' busy share, if the SQ pass is there."""
+        import csv
+        import collections
+
+        paths = glob.glob(os.path.join(directory, "sq", "**", "*counter_collection.csv"), recursive=True)
+        if not paths:
+            return None
+        per = collections.defaultdict(lambda: collections.defaultdict(float))
+        with open(paths[0]) as f:
+            for r in csv.DictReader(f):
+                if kernel in r["Kernel_Name"]:
+                    per[int(r["Dispatch_Id"])][r["Counter_Name"]] += float(r["Counter_Value"])
+        fr = [d["SQ_VALU_MFMA_BUSY_CYCLES"] / (4.0 * d["SQ_BUSY_CU_CYCLES"]) for d in per.values()
+              if d.get("SQ_BUSY_CU_CYCLES")]
+        return statistics.median(fr) if fr else None
+
     copy_fetch = one("copy_fetch", "FETCH_SIZE", "copyBuffer")
     copy_write = one("copy_write", "WRITE_SIZE", "copyBuffer")
     f_fetch = COPY_BYTES / (copy_fetch * 1024.0)
@@ -157,6 +202,9 @@ def traffic_from(directory: str, workload: str, config_name: str) -> int:
            "fetch_bytes_per_launch": fetch, "write_bytes_per_launch": write,
            "fetch_calibration": f_fetch, "write_calibration": f_write,
            "copy_fetch_kib": copy_fetch, "copy_write_kib": copy_write}
+    busy = busy_fraction("gemm_f16_kernel")
+    if busy is not None:
+        rec["mfma_busy_frac"] = busy
     with open(traffic_file(workload), "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec), flush=True)
@@ -293,6 +341,7 @@ def main() -> int:
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_TFLOPS, 4),
             "traffic": measured_traffic(workload_name, config_name),
+            "clock_normalised": clock_normalised(workload_name, config_name, achieved),
             "kernel_ms_mean": round(float(launch_ms.mean()), 5),
             "kernel_ms_median": round(float(np.median(launch_ms)), 5),
             "kernel_ms_min": round(float(launch_ms.min()), 5),
