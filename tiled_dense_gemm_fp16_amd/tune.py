@@ -21,6 +21,7 @@ import datetime
 import json
 import math
 import os
+import statistics
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -123,13 +124,32 @@ def sweep(sizes_mn, sizes_k, layouts, log, classes=(1, 0, 2)):
                                 results[key] = round(tf, 1)
                                 if best is None or tf > results[best]:
                                     best = key
+                        # near-ties (within 5 % of the best) are timed again, three
+                        # rounds interleaved, so that clock drift between the first
+                        # pass's measurements does not decide them; best median wins
+                        retimed = None
+                        if best is not None:
+                            top = sorted(results, key=results.get, reverse=True)
+                            top = [key for key in top if results[key] >= 0.95 * results[best]][:3]
+                            if len(top) > 1:
+                                again = {key: [] for key in top}
+                                for _ in range(3):
+                                    for key in top:
+                                        cfg_r, sp_r = (int(x) for x in key.split(":"))
+                                        again[key].append(_time(
+                                            lambda: g.gemm(a, b, out=c, config=cfg_r, trans_a=ta, trans_b=tb,
+                                                           splits=sp_r), 2.0 * m * n * k))
+                                retimed = {key: round(statistics.median(v), 1) for key, v in again.items()}
+                                best = max(retimed, key=retimed.get)
                         rec = {"M": m, "N": n, "K": k, "trans_a": int(ta), "trans_b": int(tb),
                                "aligned": aligned, "best": best, "tflops": results}
+                        if retimed:
+                            rec["retimed"] = retimed
                         rows.append(rec)
                         print(json.dumps(rec), file=log, flush=True)
                         if log is not sys.stdout:
                             print(f"{m}x{n}x{k} ta={int(ta)} tb={int(tb)}: {best} "
-                                  f"{results.get(best, 0.0)} TF/s", flush=True)
+                                  f"{(retimed or results).get(best, 0.0)} TF/s", flush=True)
                         del a, b, c
     return rows
 
@@ -148,8 +168,9 @@ def write_table(rows, path, note):
             continue
         lm, ln, lk = (round(math.log2(r[x])) for x in ("M", "N", "K"))
         cfg, sp = r["best"].split(":")
+        tf = (r.get("retimed") or r["tflops"])[r["best"]]
         lines.append(f"{{{lm}, {ln}, {lk}, {r['trans_a']}, {r['trans_b']}, {r['aligned']}, {cfg}, {sp}, "
-                     f"{r['tflops'][r['best']]:.1f}}},")
+                     f"{tf:.1f}}},")
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
 
