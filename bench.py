@@ -9,12 +9,8 @@ The roofline entry reports the GEMM kernel's achieved TFLOP/s (2 M N K per
 launch over the average launch duration, timed with events on the launch
 stream) against MI355X's dense FP16 MFMA peak; ``traffic`` is the HBM bytes
 per launch measured by rocprofv3 counters for this exact kernel source (null
-when the source has changed since they were taken).  ``clock_normalised`` is
-the fraction of the peak at the clock the chip actually ran: the matrix
-cores' busy cycles over the CUs' busy cycles from the same counter runs, with
-the average shader clock that fraction and the live throughput imply (null
-under the same condition).  The CPU baseline times the plain oracle on a
-bounded block of the same product.
+when the source has changed since they were taken).  The CPU baseline times
+the plain oracle on a bounded block of the same product.
 """
 from __future__ import annotations
 
@@ -34,8 +30,9 @@ METRIC = "fp16 GEMM TFLOP/s at 1 MI355X and % of dense FP16 MFMA peak"
 SPARSE_METRIC = ("2:4-sparse fp16 GEMM TFLOP/s at 1 MI355X (2 flop per product of a kept value: "
                  "M N K per call) and % of dense FP16 MFMA peak")
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = [os.path.join(ROOT, "tiled_dense_gemm_fp16_amd", "csrc", f)
-                  for f in ("gemm_f16_kernels.hip", "gemm_f16_internal.h", "gemm_f16_api.cpp")]
+CSRC = os.path.join(ROOT, "tiled_dense_gemm_fp16_amd", "csrc")
+KERNEL_SOURCES = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
+                        if f.endswith((".hip", ".h", ".cpp")) and not f.startswith("mfma_probe"))
 
 
 def kernel_source_hash() -> str:
@@ -72,19 +69,16 @@ def measured_traffic(workload: str, config_name: str):
     return float(t["fetch_bytes_per_launch"]) + float(t["write_bytes_per_launch"])
 
 
-def clock_normalised(workload: str, config_name: str, achieved_tflops: float):
-    """Fraction of the peak at the clock the chip actually ran: the matrix
-    cores' busy cycles over the CUs' busy cycles (SQ_VALU_MFMA_BUSY_CYCLES per
-    SIMD, SQ_BUSY_CU_CYCLES per CU, from the committed counter summary of the
-    same kernel source), and the average shader clock that this fraction and
-    the live throughput imply (CUs x 4096 flop per cycle at full rate)."""
-    t = measured_counters(workload, config_name)
-    if t is None or "mfma_busy_frac" not in t:
-        return None
-    frac = float(t["mfma_busy_frac"])
-    return {"frac": round(frac, 4),
-            "implied_sclk_ghz": round(achieved_tflops * 1e12 / (frac * PEAK_FLOPS_PER_CLOCK) / 1e9, 3),
-            "counters": "SQ_VALU_MFMA_BUSY_CYCLES / (4 SQ_BUSY_CU_CYCLES), rocprofv3 --pmc, same kernel source"}
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+
+    return platform.processor() or "unknown"
 
 
 def cpu_baseline(a, b, w, budget_s: float, sparse=None):
@@ -123,6 +117,7 @@ def cpu_baseline(a, b, w, budget_s: float, sparse=None):
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": oracle.cpu_threads(),
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": f"{len(rows)} seeded rows x {len(cols)} seeded columns of C at full K={w.K} "
                   f"({flops / 1e9:.1f} GFLOP, fp64 accumulation) in {dt:.1f} s",
@@ -332,6 +327,7 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": workload_name, "M": w.M, "N": w.N, "K": w.K,
                    "epilogue": epi, "inputs": f"{w.dist} seed {w.seed}" + (", A pruned to 2:4" if args.sparse else ""),
+                   "sha256_A": workloads.sha256(a), "sha256_B": workloads.sha256(b),
                    "kernel": config_name},
         "pct_of_peak": round(100.0 * value / PEAK_TFLOPS, 2),
         "roofline": {
@@ -341,19 +337,21 @@ def main() -> int:
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_TFLOPS, 4),
             "traffic": measured_traffic(workload_name, config_name),
-            "clock_normalised": clock_normalised(workload_name, config_name, achieved),
             "kernel_ms_mean": round(float(launch_ms.mean()), 5),
             "kernel_ms_median": round(float(np.median(launch_ms)), 5),
             "kernel_ms_min": round(float(launch_ms.min()), 5),
+            "kernel_ms_p90": round(float(np.percentile(launch_ms, 90)), 5),
             "algorithmic_flops": flops,
             "algorithmic_bytes": float(plan["min_bytes"]),
         },
-        "spot_check": {"n": spot["n"], "pass": spot["pass"], "max_ulp_err": spot["max_ulp_err"]},
+        "spot_check": {"block": f"{len(rows)}x{len(cols)} seeded rows x columns of C",
+                       "elements": spot["n"], "n_fail": spot.get("n_fail"), "pass": spot["pass"],
+                       "max_ulp_err": spot["max_ulp_err"], "max_abs_err": spot.get("max_abs_err")},
     }
     if not args.no_ceiling:
         # the matrix cores' sustained rate on register operands alone, for the
         # kernel's MFMA instruction, with constant and with changing random bits
-        m16 = (not args.sparse) and config_name.endswith("_m16")
+        m16 = (not args.sparse) and "_m16" in config_name
         extra = g.PROBE_MFMA16 if m16 else 0
         rnd = g.probe_mfma_tflops(g.PROBE_RANDOM_CHANGING + extra)
         const = g.probe_mfma_tflops(g.PROBE_CONSTANT + extra)

@@ -23,33 +23,27 @@
  * N multiples of 8) selects the fastest kernels, other shapes run a slower
  * path that gives the same results (never an error).
  *
- * Ownership: all three buffers belong to the caller.  The only device memory
- * the library itself allocates is a split-K workspace (below), one buffer
- * per device and stream, grown on demand and kept until
- * gemm_f16_release_workspaces().  It is safe to call from several host
- * threads.
+ * Ownership: all buffers belong to the caller.  The library allocates no
+ * device memory, keeps no per-call state and never synchronises with the
+ * host or the stream; it is safe to call from several host threads.
  *
  * Split-K: when a problem has too few output tiles to fill the GPU's 256
  * CUs, the K loop of each tile may be divided into `splits` ranges run by
- * separate workgroups ("TileLang：比 Triton 低一层的 tile 语言", section
- * "工程上的几个注意点", names persistent / stream-K scheduling as the remedy
- * for grids smaller than the machine).  Each range writes fp32 partial sums
- * to a workspace of splits x M x N fp32; a second kernel adds the partials
- * in split order, applies the epilogue and rounds once to binary16.  The
- * automatic choice (gemm_f16, and CONFIG_AUTO in gemm_f16_ex /
- * gemm_f16_trans) may split and then uses the library's workspace for the
- * stream; if that buffer would have to grow while the stream is being
- * captured into a graph, or cannot be allocated, the call runs unsplit.  A
- * graph that captured a split call holds that buffer's address: keep the
- * graph's stream from needing a larger buffer, and do not call
- * gemm_f16_release_workspaces(), while the graph may still be launched.
+ * separate workgroups (a fixed-order form of the persistent / stream-K
+ * scheduling that "5分钟上手TileLang：GPU内核开发指南", section
+ * "进阶方向：从 GEMM 到真实模型算子", lists among the GEMM variants).  Each
+ * range writes fp32 partial sums to a workspace of splits x M x N fp32 that
+ * the caller passes to gemm_f16_split; a second kernel adds the partials in
+ * split order, applies the epilogue and rounds once to binary16.  gemm_f16,
+ * gemm_f16_ex and gemm_f16_trans take no workspace and always run one
+ * kernel over the whole of K; gemm_f16_plan_split says whether, and with how
+ * large a workspace, a split would pay for a shape.
  *
  * Execution: asynchronous on the given HIP stream (a hipStream_t passed as
- * void*; NULL is the default stream).  No host synchronisation, except that
- * growing the library's workspace waits for the stream's earlier work.  The
- * result is deterministic: no atomics, and split partials are added in a
- * fixed order, so it is bitwise reproducible run to run for a given shape,
- * kernel configuration and split count.
+ * void*; NULL is the default stream), so every entry point may be captured
+ * into a HIP graph.  The result is deterministic: no atomics, and split
+ * partials are added in a fixed order, so it is bitwise reproducible run to
+ * run for a given shape, kernel configuration and split count.
  *
  * Errors: arguments are validated before any HIP call; on error nothing is
  * launched and C is untouched.  A launch error is reported as
@@ -82,11 +76,10 @@ typedef enum gemm_f16_status {
     GEMM_F16_ERROR_LAUNCH_FAILED = 5,
     /* a dimension beyond the library's limits (see GEMM_F16_MAX_*) */
     GEMM_F16_ERROR_UNSUPPORTED_SIZE = 6,
-    /* gemm_f16_split: the caller's workspace is smaller than the plan's
-     * workspace_bytes, or the library's could not be allocated (or would
-     * have to grow during graph capture) */
+    /* gemm_f16_split: the plan splits K but no workspace was given, or the
+     * caller's workspace is smaller than the plan's workspace_bytes */
     GEMM_F16_ERROR_WORKSPACE = 7,
-    /* a HIP runtime call other than a launch failed (workspace management) */
+    /* a HIP runtime call other than a launch failed */
     GEMM_F16_ERROR_RUNTIME = 8
 } gemm_f16_status_t;
 
@@ -95,18 +88,25 @@ typedef enum gemm_f16_epilogue {
     GEMM_F16_EPILOGUE_RELU = 1    /* C = rne16(max(A . B, 0)); -0 becomes +0 */
 } gemm_f16_epilogue_t;
 
-/* Size limits: M at most 2^31 - 1; K and N at most 2^22, so that the panel
- * of A, B or C one workgroup addresses (at most 256 rows) spans at most
- * 2 GiB and fits a 32-bit buffer offset; and at most 2^31 - 1 output tiles. */
+/* Size limits.  Every global access goes through a buffer range of at most
+ * 2 GiB addressed with 32-bit byte offsets: the panel of at most 256 rows of
+ * A (stored M x K), of B (stored N x K) or of C that one workgroup touches,
+ * and the k slice of at most 64 rows of A (stored K x M) or of B (stored
+ * K x N) that one pipeline stage loads.  Hence K and N at most 2^22 (256
+ * rows of pitch K or N), M at most 2^24 when A is stored K x M (64 rows of
+ * pitch M), M at most 2^31 - 1 otherwise, and at most 2^31 - 1 workgroups.
+ * Larger shapes return GEMM_F16_ERROR_UNSUPPORTED_SIZE. */
 #define GEMM_F16_MAX_DIM ((int64_t)2147483647)
 #define GEMM_F16_MAX_K ((int64_t)1 << 22)
 #define GEMM_F16_MAX_N ((int64_t)1 << 22)
+#define GEMM_F16_MAX_M_TRANS_A ((int64_t)1 << 24)
 
 /* Automatic kernel choice for gemm_f16_ex / gemm_f16_plan. */
 #define GEMM_F16_CONFIG_AUTO (-1)
 
-/* Automatic split count for gemm_f16_split / gemm_f16_plan_split, and the
- * largest count accepted. */
+/* Automatic split count for gemm_f16_split / gemm_f16_plan_split (the
+ * measured table or the time model decides; 1 when a split does not pay),
+ * and the largest count accepted. */
 #define GEMM_F16_SPLITS_AUTO 0
 #define GEMM_F16_MAX_SPLITS 64
 
@@ -129,9 +129,9 @@ gemm_f16_status_t gemm_f16(int64_t M, int64_t N, int64_t K,
  * As gemm_f16, with an explicit kernel configuration: an index in
  * [0, gemm_f16_num_configs()) or GEMM_F16_CONFIG_AUTO.  A configuration that
  * cannot run this shape or alignment (gemm_f16_plan says why) returns
- * GEMM_F16_ERROR_INVALID_VALUE.  An explicit configuration runs unsplit (one
- * kernel, no workspace).  Intended for tests and tuning sweeps; every
- * configuration computes the same function.
+ * GEMM_F16_ERROR_INVALID_VALUE.  Runs unsplit (one kernel, no workspace),
+ * like gemm_f16.  Intended for tests and tuning sweeps; every configuration
+ * computes the same function.
  */
 gemm_f16_status_t gemm_f16_ex(int64_t M, int64_t N, int64_t K,
                               const void *A, const void *B, void *C,
@@ -163,29 +163,21 @@ gemm_f16_status_t gemm_f16_trans(int64_t M, int64_t N, int64_t K,
  *                     every split spans whole K tiles (gemm_f16_plan_split
  *                     reports the count used; 1 means one kernel and no
  *                     workspace).
- *   workspace       : NULL for the library's buffer for this device and
- *                     stream, or a caller-owned device buffer of
- *                     workspace_bytes bytes, 16-byte aligned, overlapping
- *                     none of A, B, C, and at least the plan's
- *                     workspace_bytes long (else GEMM_F16_ERROR_WORKSPACE).
- *                     Its contents are scratch; calls that share one buffer
- *                     must be ordered (one stream).
+ *   workspace       : a caller-owned device buffer of workspace_bytes
+ *                     bytes, 16-byte aligned, overlapping none of A, B, C,
+ *                     and at least the plan's workspace_bytes long.  NULL
+ *                     (with workspace_bytes 0) is accepted only when the
+ *                     plan does not split; otherwise, as for a buffer that is
+ *                     too small, GEMM_F16_ERROR_WORKSPACE is returned before
+ *                     anything is launched.  Its contents are scratch; calls
+ *                     that share one buffer must be ordered (one stream).
  *   workspace_bytes : size of the caller's buffer; 0 when workspace is NULL.
- * Unlike the automatic path this never falls back to an unsplit run: a
- * library workspace that cannot be obtained returns
- * GEMM_F16_ERROR_WORKSPACE.  Other arguments and errors as gemm_f16_trans.
+ * Other arguments and errors as gemm_f16_trans.
  */
 gemm_f16_status_t gemm_f16_split(int64_t M, int64_t N, int64_t K,
                                  const void *A, int trans_a, const void *B, int trans_b,
                                  void *C, int epilogue, int config, int splits,
                                  void *workspace, int64_t workspace_bytes, void *stream);
-
-/*
- * Free the library's split-K workspaces on every device (waiting for each
- * device's work first).  Later calls allocate again when they need to.
- * Returns GEMM_F16_ERROR_RUNTIME if a HIP call failed.
- */
-gemm_f16_status_t gemm_f16_release_workspaces(void);
 
 /*
  * 2:4 structured-sparse A.  The pages name 2:4 sparse GEMM (`T.gemm_sp`)
@@ -257,10 +249,11 @@ typedef struct gemm_f16_plan {
 } gemm_f16_plan_t;
 
 /*
- * Describe the kernel a call with these arguments would launch (config may
- * be GEMM_F16_CONFIG_AUTO).  Pointers are used only for alignment checks and
- * may be NULL-but-aligned stand-ins (any multiple of 16) when only the shape
- * matters.  Pure host logic: no HIP call, no GPU needed.
+ * Describe the kernel a call of gemm_f16 / gemm_f16_ex with these arguments
+ * would launch (config may be GEMM_F16_CONFIG_AUTO; the plan never splits).
+ * Pointers are used only for alignment checks and may be NULL-but-aligned
+ * stand-ins (any multiple of 16) when only the shape matters.  Pure host
+ * logic: no HIP call, no GPU needed.
  */
 gemm_f16_status_t gemm_f16_plan(int64_t M, int64_t N, int64_t K,
                                 const void *A, const void *B, const void *C,
@@ -278,7 +271,9 @@ gemm_f16_status_t gemm_f16_plan_sp(int64_t M, int64_t N, int64_t K, const void *
                                    const void *B, int trans_b, const void *C, int config,
                                    gemm_f16_plan_t *plan);
 
-/* As gemm_f16_plan_trans, for gemm_f16_split with the given split request. */
+/* As gemm_f16_plan_trans, for gemm_f16_split with the given split request
+ * (GEMM_F16_SPLITS_AUTO: the split the measured table or the time model
+ * prefers, with the workspace_bytes the caller must then provide). */
 gemm_f16_status_t gemm_f16_plan_split(int64_t M, int64_t N, int64_t K,
                                       const void *A, int trans_a, const void *B, int trans_b,
                                       const void *C, int config, int splits, gemm_f16_plan_t *plan);

@@ -57,7 +57,7 @@ def test_probe_library_exports_its_header():
 
 
 def test_status_strings():
-    for st in range(0, 7):
+    for st in range(0, 9):
         assert g.status_string(st) != "unknown status"
     assert g.status_string(99) == "unknown status"
 
@@ -240,37 +240,105 @@ TUNED = os.path.join(ROOT, "tiled_dense_gemm_fp16_amd", "csrc", "gemm_f16_tuned.
 def tuned_entries():
     rows = []
     for line in open(TUNED):
-        m = re.match(r"\{\s*(-?\d+(?:\s*,\s*-?\d+){7})\s*,\s*([\d.]+)\s*\},", line)
+        m = re.match(r"\{\s*(-?\d+(?:\s*,\s*-?\d+){7})\s*,\s*([\d.]+)\s*,\s*(-?\d+)\s*,\s*([\d.]+)\s*\},",
+                     line)
         if m:
-            rows.append(tuple(int(x) for x in m.group(1).split(",")))
+            rows.append(tuple(int(x) for x in m.group(1).split(",")) + (int(m.group(3)),))
     return rows
 
 
 def test_tuned_table_drives_the_automatic_choice():
-    """Every entry of the measured table names a configuration that accepts
-    its shape, and the planner picks it (and its split count) for exactly
-    that shape."""
+    """Every entry of the measured table names configurations that accept
+    its shape; for exactly that shape the planner picks the entry's unsplit
+    configuration for the workspace-free entry points and its configuration
+    and split count for gemm_f16_split with SPLITS_AUTO."""
     rows = tuned_entries()
     assert rows, "the measured configuration table is empty"
     seen = set()
-    for lm, ln, lk, ta, tb, aligned, cfg, splits in rows:
-        assert 0 <= cfg < g.num_configs() and 1 <= splits <= g.MAX_SPLITS
+    for lm, ln, lk, ta, tb, aligned, cfg, splits, cfg1 in rows:
+        assert 0 <= cfg < g.num_configs() and 0 <= cfg1 < g.num_configs() and 1 <= splits <= g.MAX_SPLITS
+        assert splits > 1 or cfg == cfg1
         key = (lm, ln, lk, ta, tb, aligned)
         assert key not in seen
         seen.add(key)
         # class 1: aligned pitches; 0: every pitch off by 4 elements; 2: only K (A's pitch)
         pm, pn, pk = {1: (0, 0, 0), 0: (4, 4, 4), 2: (0, 0, 4)}[aligned]
         M, N, K = (1 << lm) + pm, (1 << ln) + pn, (1 << lk) + pk
-        p = g.plan(M, N, K, FAKE, FAKE, FAKE, trans_a=bool(ta), trans_b=bool(tb))
-        assert p["config"] == cfg, (key, p["config"])
-        want = g.plan(M, N, K, FAKE, FAKE, FAKE, config=cfg, trans_a=bool(ta), trans_b=bool(tb), splits=splits)
-        assert p["splits"] == want["splits"] and p["k_split"] == want["k_split"], key
+        kw = dict(trans_a=bool(ta), trans_b=bool(tb))
+        p = g.plan(M, N, K, FAKE, FAKE, FAKE, **kw)
+        assert p["config"] == cfg1 and p["splits"] == 1 and p["workspace_bytes"] == 0, (key, p["config"])
+        q = g.plan(M, N, K, FAKE, FAKE, FAKE, splits=g.SPLITS_AUTO, **kw)
+        assert q["config"] == cfg, (key, q["config"])
+        want = g.plan(M, N, K, FAKE, FAKE, FAKE, config=cfg, splits=splits, **kw)
+        assert q["splits"] == want["splits"] and q["k_split"] == want["k_split"], key
         assert (p["vec_a"] == 8 and p["vec_b"] == 8) == (aligned == 1)
         assert aligned != 2 or (not ta and not tb and p["vec_b"] == 8)
     # far from every swept shape the analytic model decides (no table hit):
-    # a deep K under a one-tile output is split
-    p = g.plan(24, 24, 1 << 20, FAKE, FAKE, FAKE)
+    # a deep K under a one-tile output is split when a workspace may be used
+    p = g.plan(24, 24, 1 << 20, FAKE, FAKE, FAKE, splits=g.SPLITS_AUTO)
     assert p["splits"] > 1 and p["workspace_bytes"] == p["splits"] * 24 * 24 * 4
+
+
+def test_workspace_free_entry_points_never_split():
+    """gemm_f16, gemm_f16_ex and gemm_f16_trans take no workspace: their
+    plans run one kernel over all of K even where gemm_f16_split would
+    split (table hits and model choices alike)."""
+    for M, N, K in [(1024, 1024, 8192), (512, 512, 8192), (96, 96, 30000), (24, 24, 1 << 20), (512, 512, 2048)]:
+        for ta, tb in [(False, False), (False, True), (True, False), (True, True)]:
+            auto = g.plan(M, N, K, FAKE, FAKE, FAKE, trans_a=ta, trans_b=tb)
+            assert auto["splits"] == 1 and auto["workspace_bytes"] == 0 and auto["k_split"] == K
+            assert auto["grid"] == auto["tiles_m"] * auto["tiles_n"]
+        split = g.plan(M, N, K, FAKE, FAKE, FAKE, splits=g.SPLITS_AUTO)
+        assert split["splits"] > 1 and split["workspace_bytes"] == split["splits"] * M * N * 4, (M, N, K)
+        for c in range(g.num_configs()):
+            try:
+                p = g.plan(M, N, K, FAKE, FAKE, FAKE, config=c)
+            except g.GemmError:
+                continue
+            assert p["splits"] == 1 and p["workspace_bytes"] == 0
+
+
+def test_split_without_a_workspace_is_refused_before_any_launch():
+    # 1024 x 1024 x 8192: the planner splits it; no workspace means status 7,
+    # returned by validation (so also on a host without a GPU)
+    st = g.lib().gemm_f16_split(1024, 1024, 8192, FAKE, 0, FAKE * 64, 0, FAKE * 128, 0, g.CONFIG_AUTO,
+                                g.SPLITS_AUTO, None, 0, None)
+    assert st == 7
+    st = g.lib().gemm_f16_split(1024, 1024, 8192, FAKE, 0, FAKE * 64, 0, FAKE * 128, 0, 2, 4, None, 0, None)
+    assert st == 7
+
+
+def test_library_imports_no_allocation_or_synchronisation():
+    """The shared library does not even import the HIP calls that allocate
+    or free device or host memory, or that wait for a stream or the device:
+    no call path can reach them."""
+    import shutil
+    import subprocess
+
+    nm = shutil.which("nm") or "/opt/rocm/llvm/bin/llvm-nm"
+    out = subprocess.run([nm, "-D", "--undefined-only", g.LIB_PATH], capture_output=True, text=True, check=True)
+    imported = {line.split()[-1].split("@")[0] for line in out.stdout.splitlines() if line.strip()}
+    hip = {name for name in imported if name.startswith("hip")}
+    assert "hipGetDevice" in hip                      # the import list was read
+    forbidden = re.compile(r"^hip(Ext)?(Malloc|Free|HostAlloc|HostMalloc|HostFree|MemAlloc|MemPool|"
+                           r"StreamSynchronize|DeviceSynchronize|EventSynchronize|Memcpy$|Memset$|"
+                           r"MemcpyHtoD$|MemcpyDtoH$|MemcpyDtoD$)")
+    assert not sorted(n for n in hip if forbidden.match(n)), hip
+
+
+def test_transposed_a_size_limit():
+    """A stored K x M: a 64-row k slice of pitch M must fit a 2 GiB buffer
+    range, so M is at most 2^24 there (status 6 beyond, before any launch)."""
+    for M in (1 << 25, (1 << 24) + 1, 1 << 26):
+        with pytest.raises(g.GemmError) as e:
+            g.plan(M, 64, 64, FAKE, FAKE, FAKE, trans_a=True)
+        assert e.value.status == 6
+        assert g.gemm_f16_raw(M, 64, 64, FAKE, FAKE * 3, FAKE * 2, 0, trans_a=True) == 6
+        assert g.lib().gemm_f16_split(M, 64, 64, FAKE, 1, FAKE * 3, 0, FAKE * 2, 0, -1, 2, None, 0, None) == 6
+    p = g.plan(1 << 24, 64, 64, FAKE, FAKE, FAKE, trans_a=True)
+    assert p["tiles_m"] == (1 << 24) // p["block_m"]
+    # the same M with A stored M x K is fine
+    g.plan(1 << 25, 64, 64, FAKE, FAKE, FAKE)
 
 
 # ---- split-K planning and workspace validation (host logic only) ----

@@ -53,7 +53,6 @@ SIGNATURES = {
     "gemm_f16_trans": ([_i64, _i64, _i64, _vp, _int, _vp, _int, _vp, _int, _int, _vp], _int),
     "gemm_f16_plan": ([_i64, _i64, _i64, _vp, _vp, _vp, _int, ctypes.POINTER(Plan)], _int),
     "gemm_f16_split": ([_i64, _i64, _i64, _vp, _int, _vp, _int, _vp, _int, _int, _int, _vp, _i64, _vp], _int),
-    "gemm_f16_release_workspaces": ([], _int),
     "gemm_f16_plan_trans": ([_i64, _i64, _i64, _vp, _int, _vp, _int, _vp, _int, ctypes.POINTER(Plan)], _int),
     "gemm_f16_plan_split": ([_i64, _i64, _i64, _vp, _int, _vp, _int, _vp, _int, _int, ctypes.POINTER(Plan)],
                             _int),
@@ -114,9 +113,9 @@ def plan(M: int, N: int, K: int, A_ptr: int = 0, B_ptr: int = 0, C_ptr: int = 0,
          config: int = CONFIG_AUTO, trans_a: bool = False, trans_b: bool = False,
          splits: int | None = None) -> dict:
     """How a call would run this shape (pure host logic, no GPU needed):
-    gemm_f16 / gemm_f16_trans when ``splits`` is None, else gemm_f16_split
-    with that request.  Pointers only matter for alignment; 0 stands for an
-    aligned buffer."""
+    gemm_f16 / gemm_f16_trans (never split) when ``splits`` is None, else
+    gemm_f16_split with that request (SPLITS_AUTO: the planner's choice).
+    Pointers only matter for alignment; 0 stands for an aligned buffer."""
     p = Plan()
     if splits is None:
         st = lib().gemm_f16_plan_trans(M, N, K, A_ptr or None, int(trans_a), B_ptr or None, int(trans_b),
@@ -141,11 +140,22 @@ def gemm_f16_raw(M: int, N: int, K: int, A_ptr: int, B_ptr: int, C_ptr: int, epi
     return int(lib().gemm_f16_ex(M, N, K, A, B, C, epilogue, config, S))
 
 
-def release_workspaces() -> None:
-    """Free the library's split-K workspaces (gemm_f16_release_workspaces)."""
-    st = lib().gemm_f16_release_workspaces()
-    if st != SUCCESS:
-        raise GemmError(st, "gemm_f16_release_workspaces")
+_split_plans: dict = {}
+
+
+def _auto_split(M, N, K, a, b, out, config, trans_a, trans_b, splits):
+    """(splits, workspace_bytes) that gemm_f16_split would use for this call,
+    cached per shape, layout, configuration and pointer alignment."""
+    key = (M, N, K, a.data_ptr() % 16, b.data_ptr() % 16, out.data_ptr() % 16, config, trans_a, trans_b, splits)
+    hit = _split_plans.get(key)
+    if hit is None:
+        p = plan(M, N, K, a.data_ptr() or 16, b.data_ptr() or 16, out.data_ptr() or 16, config=config,
+                 trans_a=trans_a, trans_b=trans_b, splits=splits)
+        hit = (p["splits"], p["workspace_bytes"])
+        if len(_split_plans) > 4096:
+            _split_plans.clear()
+        _split_plans[key] = hit
+    return hit
 
 
 def gemm(a, b, epilogue: str = "none", out=None, config: int = CONFIG_AUTO, stream=None,
@@ -154,12 +164,16 @@ def gemm(a, b, epilogue: str = "none", out=None, config: int = CONFIG_AUTO, stre
 
     a is M x K (or K x M with ``trans_a``), b is K x N (or N x K with
     ``trans_b``).  Returns ``out`` (allocated as an M x N float16 tensor when
-    not given).  The kernel is enqueued on ``stream`` (default: torch's
+    not given).  The kernels are enqueued on ``stream`` (default: torch's
     current stream) and the call returns without synchronising.
 
-    ``splits`` (None: the automatic choice of gemm_f16 / gemm_f16_trans, or
-    SPLITS_AUTO / a count) and ``workspace`` (None: the library's buffer, or
-    a contiguous GPU tensor used as scratch) go to gemm_f16_split.
+    ``splits``: None lets the planner split K when that pays for the shape
+    (gemm_f16_split with SPLITS_AUTO), 1 runs one kernel (gemm_f16 /
+    gemm_f16_ex / gemm_f16_trans), a larger count asks for that split.  A
+    split needs a workspace of fp32 partial sums: ``workspace`` (a contiguous
+    GPU tensor used as scratch) or, when it is None, one taken from torch's
+    caching allocator on ``stream`` for this call.  The C library itself
+    never allocates.
     """
     import torch
 
@@ -191,8 +205,16 @@ def gemm(a, b, epilogue: str = "none", out=None, config: int = CONFIG_AUTO, stre
             raise ValueError("workspace is on another device")
     if stream is None:
         stream = torch.cuda.current_stream(a.device)
+    request = SPLITS_AUTO if splits is None else int(splits)
     with torch.cuda.device(a.device):
-        if splits is None and workspace is None:
+        if workspace is None and request != 1 and M > 0 and N > 0:
+            n_split, ws_bytes = _auto_split(M, N, K, a, b, out, config, trans_a, trans_b, request)
+            if n_split > 1:
+                with torch.cuda.stream(stream):
+                    workspace = torch.empty(-(-ws_bytes // 4), dtype=torch.float32, device=a.device)
+            else:
+                request = 1
+        if workspace is None and request in (1, SPLITS_AUTO):
             st = gemm_f16_raw(M, N, K, a.data_ptr(), b.data_ptr(), out.data_ptr(), _EPILOGUES[epilogue],
                               stream.cuda_stream, config, trans_a, trans_b)
         else:
@@ -200,8 +222,7 @@ def gemm(a, b, epilogue: str = "none", out=None, config: int = CONFIG_AUTO, stre
             ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
             st = lib().gemm_f16_split(M, N, K, a.data_ptr() or None, int(trans_a), b.data_ptr() or None,
                                       int(trans_b), out.data_ptr() or None, _EPILOGUES[epilogue], config,
-                                      SPLITS_AUTO if splits is None else int(splits), ws_ptr or None,
-                                      ws_bytes, stream.cuda_stream or None)
+                                      request, ws_ptr or None, ws_bytes, stream.cuda_stream or None)
     if st != SUCCESS:
         raise GemmError(st, "gemm_f16")
     return out

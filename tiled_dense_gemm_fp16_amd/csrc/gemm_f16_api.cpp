@@ -9,7 +9,6 @@
 
 #include <algorithm>
 #include <mutex>
-#include <vector>
 
 #include "gemm_f16.h"
 #include "gemm_f16_internal.h"
@@ -25,15 +24,12 @@ const ConfigDesc kConfigs[kNumConfigs] = {
     {"128x128x64_s3_direct", 128, 128, 64, 3, 4, true, 8, 8, kAllLayouts, 1},
     {"128x128x32_s2_staged", 128, 128, 32, 2, 4, false, 1, 1, kAllLayouts, 2},
     {"64x64x64_s2_staged", 64, 64, 64, 2, 4, false, 1, 1, kAllLayouts, 5},
-    {"256x256x32_s4_direct", 256, 256, 32, 4, 4, true, 8, 8, kNN, 1},
-    {"256x256x32_s5_direct", 256, 256, 32, 5, 4, true, 8, 8, kNN, 1},
     {"256x256x64_s2_direct_w8n", 256, 256, 64, 2, 8, true, 8, 8, kAllLayouts, 1},
-    {"256x256x32_s5_direct_w8n", 256, 256, 32, 5, 8, true, 8, 8, kNN, 1},
-    {"256x256x64_s2_direct_w8m", 256, 256, 64, 2, 8, true, 8, 8, kNN, 1},
     {"256x256x64_s2_staged_w8", 256, 256, 64, 2, 8, false, 4, 4, kAllLayouts, 1},
     {"256x128x64_s2_staged", 256, 128, 64, 2, 4, false, 4, 4, kNN, 1},
     {"256x256x64_s2_direct_m16", 256, 256, 64, 2, 4, true, 8, 8, kAllLayouts, 1},
     {"256x256x64_s2_direct_m16_a4", 256, 256, 64, 2, 4, true, 2, 8, kNN | kNT, 1},
+    {"256x256x32_s4_direct_m16", 256, 256, 32, 4, 4, true, 8, 8, kAllLayouts, 1},
 };
 
 // Sparse configurations (2:4 A): fields as above; every one takes A as
@@ -76,12 +72,16 @@ bool overlaps(const void *a, int64_t a_bytes, const void *b, int64_t b_bytes)
     return a0 < b0 + (uintptr_t)b_bytes && b0 < a0 + (uintptr_t)a_bytes;
 }
 
-gemm_f16_status_t validate(int64_t M, int64_t N, int64_t K, const void *A, const void *B,
+gemm_f16_status_t validate(int64_t M, int64_t N, int64_t K, const void *A, bool trans_a, const void *B,
                            const void *C, bool check_c_overlap)
 {
     if (M < 0 || N < 0 || K < 0)
         return GEMM_F16_ERROR_INVALID_VALUE;
     if (M > GEMM_F16_MAX_DIM || N > GEMM_F16_MAX_N || K > GEMM_F16_MAX_K)
+        return GEMM_F16_ERROR_UNSUPPORTED_SIZE;
+    // A stored K x M: one k slice of it (up to 64 rows of pitch M) is one
+    // buffer range addressed with 32-bit byte offsets
+    if (trans_a && M > GEMM_F16_MAX_M_TRANS_A)
         return GEMM_F16_ERROR_UNSUPPORTED_SIZE;
     const bool a_nonempty = M > 0 && K > 0, b_nonempty = K > 0 && N > 0, c_nonempty = M > 0 && N > 0;
     if ((a_nonempty && !A) || (b_nonempty && !B) || (c_nonempty && !C))
@@ -97,19 +97,19 @@ gemm_f16_status_t validate(int64_t M, int64_t N, int64_t K, const void *A, const
 
 // Relative throughput a workgroup of each configuration sustains, from
 // measurements on MI355X (8192^3 and 4096^3, random fp16 operands): larger
-// tiles reuse each LDS byte more.  Used only to rank configurations; 0 marks
-// a configuration kept for tests and sweeps but never chosen automatically.
+// tiles reuse each LDS byte more.  Used only to rank configurations.
 double config_efficiency(int c)
 {
     switch (c) {
-    case 12: return 1.06;   // 256x256x64 direct, 4 waves, 16x16x32 MFMAs
-    case 13: return 0.95;   // the same with 4-byte loads of A (A rows 4-byte aligned)
-    case 7: return 1.00;    // 256x256x64 direct, 8 waves
+    case 8: return 1.06;    // 256x256x64 direct, 4 waves, 16x16x32 MFMAs
+    case 9: return 0.95;    // the same with 4-byte loads of A (A rows 4-byte aligned)
+    case 10: return 1.05;   // 256x256x32 direct, 4 stages, 16x16x32 MFMAs
+    case 5: return 1.00;    // 256x256x64 direct, 8 waves
     case 0: return 0.97;    // 256x256x64 direct, 4 waves
     case 1: return 0.90;    // 256x128x64 direct
-    case 10: return 0.85;   // 256x256x64 register-staged, 8 waves (vectors of 4 or 8)
+    case 6: return 0.85;    // 256x256x64 register-staged, 8 waves (vectors of 4 or 8)
     case 2: return 0.76;    // 128x128x64 direct
-    case 11: return 0.66;   // 256x128x64 register-staged (vectors of 4 or 8)
+    case 7: return 0.66;    // 256x128x64 register-staged (vectors of 4 or 8)
     case 3: return 0.46;    // 128x128x32 register-staged, any alignment
     case 4: return 0.25;    // 64x64x64 register-staged, any alignment
     default: return 0.0;
@@ -194,7 +194,8 @@ void fill_plan(int c, int64_t M, int64_t N, int64_t K, int va, int vb, int vc, b
 // ---- automatic choice ---------------------------------------------------------
 // Measured table (tiled_dense_gemm_fp16_amd/tune.py): for swept shapes,
 // layouts and pitch alignments, the configuration and split count that ran
-// fastest.
+// fastest, and the fastest configuration run unsplit (what a call without a
+// workspace runs).
 struct TunedEntry {
     int lm, ln, lk;        // log2 of the swept M, N, K
     int trans_a, trans_b;
@@ -203,10 +204,12 @@ struct TunedEntry {
     int config;
     int splits;
     double tflops;
+    int config_unsplit;
+    double tflops_unsplit;
 };
 const TunedEntry kTuned[] = {
 #include "gemm_f16_tuned.inc"
-    {-1, -1, -1, -1, -1, -1, -1, 0, 0.0}   // end marker
+    {-1, -1, -1, -1, -1, -1, -1, 0, 0.0, -1, 0.0}   // end marker
 };
 
 // The tuned entry for the nearest swept shape (in log2 M, N, K) with the same
@@ -224,7 +227,8 @@ const TunedEntry *tuned_entry(int64_t M, int64_t N, int64_t K, bool ta, bool tb,
         if (e.trans_a != (int)ta || e.trans_b != (int)tb || e.aligned != aligned)
             continue;
         const double d = sqrt((lm - e.lm) * (lm - e.lm) + (ln - e.ln) * (ln - e.ln) + (lk - e.lk) * (lk - e.lk));
-        if (d < best_d && e.config < kNumConfigs && config_fits(e.config, va, vb, ta, tb)) {
+        if (d < best_d && e.config < kNumConfigs && config_fits(e.config, va, vb, ta, tb) &&
+            e.config_unsplit >= 0 && e.config_unsplit < kNumConfigs && config_fits(e.config_unsplit, va, vb, ta, tb)) {
             best = &e;
             best_d = d;
         }
@@ -331,12 +335,16 @@ gemm_f16_status_t make_plan(int64_t M, int64_t N, int64_t K, const void *A, bool
         const TunedEntry *e = tuned_entry(M, N, K, ta, tb, cls, va, vb);
         if (!e && cls == 2)
             e = tuned_entry(M, N, K, ta, tb, 0, va, vb);
-        if (e && (splits == GEMM_F16_SPLITS_AUTO || splits == e->splits)) {
+        if (e && splits == 1) {
+            c = e->config_unsplit;
+        } else if (e && (splits == GEMM_F16_SPLITS_AUTO || splits == e->splits)) {
             c = e->config;
             sp = split_geometry(kConfigs[c], K, e->splits);
             if (sp.splits > 1 && ((int64_t)sp.splits * M * N * 4 > kAutoWorkspaceMax ||
-                                  !split_addressable(kConfigs[c], N)))
+                                  !split_addressable(kConfigs[c], N))) {
+                c = e->config_unsplit;
                 sp = {1, K};
+            }
         } else {
             c = choose_config(M, N, K, va, vb, ta, tb, splits, &sp);
         }
@@ -376,58 +384,6 @@ gemm_f16_status_t check_device(int *device)
     return g_dev_state[dev] == 1 ? GEMM_F16_SUCCESS : GEMM_F16_ERROR_UNSUPPORTED_DEVICE;
 }
 
-// ---- library-owned split-K workspaces -----------------------------------------
-// One buffer per (device, stream): work on one stream runs in order, so calls
-// on a stream can share its buffer; calls on different streams never do.
-struct OwnedWorkspace {
-    int dev;
-    hipStream_t stream;
-    void *ptr;
-    int64_t bytes;
-};
-std::mutex g_ws_mutex;                 // held from lookup until the kernels are enqueued
-std::vector<OwnedWorkspace> g_ws;
-
-// With g_ws_mutex held: the buffer of (dev, s), grown to at least `bytes`.
-// Growing first waits for the stream's queued work (which may still use the
-// old buffer); it is refused while the stream is being captured into a graph.
-gemm_f16_status_t owned_workspace(int dev, hipStream_t s, int64_t bytes, void **out)
-{
-    OwnedWorkspace *w = nullptr;
-    for (OwnedWorkspace &x : g_ws)
-        if (x.dev == dev && x.stream == s) {
-            w = &x;
-            break;
-        }
-    if (w && w->bytes >= bytes) {
-        *out = w->ptr;
-        return GEMM_F16_SUCCESS;
-    }
-    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone)
-        return GEMM_F16_ERROR_WORKSPACE;
-    if (!w) {
-        g_ws.push_back({dev, s, nullptr, 0});
-        w = &g_ws.back();
-    }
-    if (w->ptr) {
-        if (hipStreamSynchronize(s) != hipSuccess || hipFree(w->ptr) != hipSuccess)
-            return GEMM_F16_ERROR_RUNTIME;
-        w->ptr = nullptr;
-        w->bytes = 0;
-    }
-    const int64_t want = ceil_div(bytes, (int64_t)2 << 20) * ((int64_t)2 << 20);
-    void *p = nullptr;
-    if (hipMalloc(&p, (size_t)want) != hipSuccess) {
-        (void)hipGetLastError();
-        return GEMM_F16_ERROR_WORKSPACE;
-    }
-    w->ptr = p;
-    w->bytes = want;
-    *out = p;
-    return GEMM_F16_SUCCESS;
-}
-
 // Enqueue a planned call; W is the split-K workspace (plan->splits > 1).
 gemm_f16_status_t launch_plan(const gemm_f16_plan_t &plan, int64_t M, int64_t N, int64_t K, const void *A,
                               bool ta, const void *B, bool tb, void *C, int epilogue, void *W, hipStream_t s)
@@ -453,14 +409,14 @@ gemm_f16_status_t launch_plan(const gemm_f16_plan_t &plan, int64_t M, int64_t N,
     return e == hipSuccess ? GEMM_F16_SUCCESS : GEMM_F16_ERROR_LAUNCH_FAILED;
 }
 
-// workspace: the caller's buffer (workspace_bytes long) or null for the
-// library's own.  fallback: if the library's buffer cannot be had (graph
-// capture, allocation failure), run unsplit instead of failing.
+// workspace: the caller's buffer (workspace_bytes long), or null: a plan
+// that splits then fails with GEMM_F16_ERROR_WORKSPACE before any HIP call.
+// The library allocates no device memory and never waits on the stream.
 gemm_f16_status_t run(int64_t M, int64_t N, int64_t K, const void *A, bool ta, const void *B, bool tb, void *C,
                       int epilogue, int config, int splits, void *workspace, int64_t workspace_bytes,
-                      bool fallback, void *stream)
+                      void *stream)
 {
-    gemm_f16_status_t st = validate(M, N, K, A, B, C, true);
+    gemm_f16_status_t st = validate(M, N, K, A, ta, B, C, true);
     if (st != GEMM_F16_SUCCESS)
         return st;
     if (epilogue != GEMM_F16_EPILOGUE_NONE && epilogue != GEMM_F16_EPILOGUE_RELU)
@@ -473,7 +429,9 @@ gemm_f16_status_t run(int64_t M, int64_t N, int64_t K, const void *A, bool ta, c
         return st;
     if (M == 0 || N == 0)
         return GEMM_F16_SUCCESS;
-    if (plan.splits > 1 && workspace) {
+    if (plan.splits > 1) {
+        if (!workspace)
+            return GEMM_F16_ERROR_WORKSPACE;
         if ((uintptr_t)workspace % 16 != 0)
             return GEMM_F16_ERROR_MISALIGNED;
         if (workspace_bytes < plan.workspace_bytes)
@@ -487,20 +445,7 @@ gemm_f16_status_t run(int64_t M, int64_t N, int64_t K, const void *A, bool ta, c
     st = check_device(&dev);
     if (st != GEMM_F16_SUCCESS)
         return st;
-    hipStream_t s = (hipStream_t)stream;
-    if (plan.splits <= 1 || workspace)
-        return launch_plan(plan, M, N, K, A, ta, B, tb, C, epilogue, workspace, s);
-    std::lock_guard<std::mutex> lock(g_ws_mutex);
-    void *w = nullptr;
-    st = owned_workspace(dev, s, plan.workspace_bytes, &w);
-    if (st == GEMM_F16_ERROR_WORKSPACE && fallback) {
-        st = make_plan(M, N, K, A, ta, B, tb, C, config, 1, &plan);
-        if (st != GEMM_F16_SUCCESS)
-            return st;
-    } else if (st != GEMM_F16_SUCCESS) {
-        return st;
-    }
-    return launch_plan(plan, M, N, K, A, ta, B, tb, C, epilogue, w, s);
+    return launch_plan(plan, M, N, K, A, ta, B, tb, C, epilogue, workspace, (hipStream_t)stream);
 }
 
 // ---- 2:4 structured-sparse A -------------------------------------------------
@@ -599,15 +544,13 @@ extern "C" {
 gemm_f16_status_t gemm_f16(int64_t M, int64_t N, int64_t K, const void *A, const void *B, void *C,
                            int epilogue, void *stream)
 {
-    return run(M, N, K, A, false, B, false, C, epilogue, GEMM_F16_CONFIG_AUTO, GEMM_F16_SPLITS_AUTO, nullptr, 0,
-               true, stream);
+    return run(M, N, K, A, false, B, false, C, epilogue, GEMM_F16_CONFIG_AUTO, 1, nullptr, 0, stream);
 }
 
 gemm_f16_status_t gemm_f16_ex(int64_t M, int64_t N, int64_t K, const void *A, const void *B, void *C,
                               int epilogue, int config, void *stream)
 {
-    const int splits = config == GEMM_F16_CONFIG_AUTO ? GEMM_F16_SPLITS_AUTO : 1;
-    return run(M, N, K, A, false, B, false, C, epilogue, config, splits, nullptr, 0, true, stream);
+    return run(M, N, K, A, false, B, false, C, epilogue, config, 1, nullptr, 0, stream);
 }
 
 gemm_f16_status_t gemm_f16_trans(int64_t M, int64_t N, int64_t K, const void *A, int trans_a, const void *B,
@@ -615,8 +558,7 @@ gemm_f16_status_t gemm_f16_trans(int64_t M, int64_t N, int64_t K, const void *A,
 {
     if ((trans_a != 0 && trans_a != 1) || (trans_b != 0 && trans_b != 1))
         return GEMM_F16_ERROR_INVALID_VALUE;
-    const int splits = config == GEMM_F16_CONFIG_AUTO ? GEMM_F16_SPLITS_AUTO : 1;
-    return run(M, N, K, A, trans_a != 0, B, trans_b != 0, C, epilogue, config, splits, nullptr, 0, true, stream);
+    return run(M, N, K, A, trans_a != 0, B, trans_b != 0, C, epilogue, config, 1, nullptr, 0, stream);
 }
 
 gemm_f16_status_t gemm_f16_split(int64_t M, int64_t N, int64_t K, const void *A, int trans_a, const void *B,
@@ -626,7 +568,7 @@ gemm_f16_status_t gemm_f16_split(int64_t M, int64_t N, int64_t K, const void *A,
     if ((trans_a != 0 && trans_a != 1) || (trans_b != 0 && trans_b != 1))
         return GEMM_F16_ERROR_INVALID_VALUE;
     return run(M, N, K, A, trans_a != 0, B, trans_b != 0, C, epilogue, config, splits, workspace,
-               workspace_bytes, false, stream);
+               workspace_bytes, stream);
 }
 
 gemm_f16_status_t gemm_f16_plan(int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *C,
@@ -639,8 +581,7 @@ gemm_f16_status_t gemm_f16_plan_trans(int64_t M, int64_t N, int64_t K, const voi
                                       const void *B, int trans_b, const void *C, int config,
                                       gemm_f16_plan_t *plan)
 {
-    const int splits = config == GEMM_F16_CONFIG_AUTO ? GEMM_F16_SPLITS_AUTO : 1;
-    return gemm_f16_plan_split(M, N, K, A, trans_a, B, trans_b, C, config, splits, plan);
+    return gemm_f16_plan_split(M, N, K, A, trans_a, B, trans_b, C, config, 1, plan);
 }
 
 gemm_f16_status_t gemm_f16_plan_split(int64_t M, int64_t N, int64_t K, const void *A, int trans_a,
@@ -649,7 +590,7 @@ gemm_f16_status_t gemm_f16_plan_split(int64_t M, int64_t N, int64_t K, const voi
 {
     if (!plan || (trans_a != 0 && trans_a != 1) || (trans_b != 0 && trans_b != 1))
         return GEMM_F16_ERROR_INVALID_VALUE;
-    gemm_f16_status_t st = validate(M, N, K, A, B, C, false);
+    gemm_f16_status_t st = validate(M, N, K, A, trans_a != 0, B, C, false);
     if (st != GEMM_F16_SUCCESS)
         return st;
     return make_plan(M, N, K, A, trans_a != 0, B, trans_b != 0, C, config, splits, plan);
@@ -741,26 +682,6 @@ const char *gemm_f16_sp_config_name(int config)
     return kSpConfigs[config].name;
 }
 
-gemm_f16_status_t gemm_f16_release_workspaces(void)
-{
-    std::lock_guard<std::mutex> lock(g_ws_mutex);
-    if (g_ws.empty())
-        return GEMM_F16_SUCCESS;
-    int cur = -1;
-    if (hipGetDevice(&cur) != hipSuccess)
-        return GEMM_F16_ERROR_RUNTIME;
-    gemm_f16_status_t st = GEMM_F16_SUCCESS;
-    for (OwnedWorkspace &w : g_ws) {
-        // hipFree waits for the device's work, which may still read the buffer
-        if (w.ptr && (hipSetDevice(w.dev) != hipSuccess || hipFree(w.ptr) != hipSuccess))
-            st = GEMM_F16_ERROR_RUNTIME;
-    }
-    g_ws.clear();
-    if (hipSetDevice(cur) != hipSuccess)
-        st = GEMM_F16_ERROR_RUNTIME;
-    return st;
-}
-
 int gemm_f16_num_configs(void) { return kNumConfigs; }
 
 const char *gemm_f16_config_name(int config)
@@ -787,7 +708,7 @@ const char *gemm_f16_status_string(gemm_f16_status_t status)
     case GEMM_F16_ERROR_UNSUPPORTED_DEVICE: return "device is not gfx950";
     case GEMM_F16_ERROR_LAUNCH_FAILED: return "kernel launch failed";
     case GEMM_F16_ERROR_UNSUPPORTED_SIZE: return "size beyond the library's limits";
-    case GEMM_F16_ERROR_WORKSPACE: return "split-K workspace too small or not obtainable";
+    case GEMM_F16_ERROR_WORKSPACE: return "split-K workspace missing or too small";
     case GEMM_F16_ERROR_RUNTIME: return "HIP runtime call failed";
     }
     return "unknown status";

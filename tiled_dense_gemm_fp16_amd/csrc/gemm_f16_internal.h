@@ -1,5 +1,6 @@
 // gemm_f16_internal.h -- shared between the host API (gemm_f16_api.cpp) and
-// the gfx950 kernels (gemm_f16_kernels.hip).  Not part of the public ABI.
+// the gfx950 kernels (gemm_f16_tile.h and the gemm_f16_*.hip files that
+// instantiate it).  Not part of the public ABI.
 #ifndef GEMM_F16_INTERNAL_H
 #define GEMM_F16_INTERNAL_H
 
@@ -38,7 +39,7 @@ struct ConfigDesc {
     int occupancy;        // workgroups resident per CU (LDS and register limits)
 };
 
-constexpr int kNumConfigs = 14;
+constexpr int kNumConfigs = 11;
 extern const ConfigDesc kConfigs[kNumConfigs];
 
 // Launch configuration `config` with `grid` workgroups on `s`.
@@ -49,6 +50,11 @@ extern const ConfigDesc kConfigs[kNumConfigs];
 // launch status.
 hipError_t launch(int config, const KernelArgs &a, int va, int vb, bool trans_a, bool trans_b, int64_t grid,
                   hipStream_t s);
+// ... per layout: A . B, A . B^T, A^T . B, A^T . B^T (one source file each)
+hipError_t launch_nn(int config, const KernelArgs &a, int va, int vb, int64_t grid, hipStream_t s);
+hipError_t launch_nt(int config, const KernelArgs &a, int va, int vb, int64_t grid, hipStream_t s);
+hipError_t launch_tn(int config, const KernelArgs &a, int va, int vb, int64_t grid, hipStream_t s);
+hipError_t launch_tt(int config, const KernelArgs &a, int va, int vb, int64_t grid, hipStream_t s);
 
 // 2:4 sparse A: compress M x K (K % 16 == 0) to vals (M x K/2) and meta
 // (M x K/16 words); vec: A and vals 16-byte aligned.

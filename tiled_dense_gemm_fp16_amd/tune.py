@@ -8,8 +8,11 @@ section "å·¥ç¨‹ä¸Šçš„å‡ ä¸ªæ³¨æ„ç‚¹"; "5åˆ†é’Ÿä¸Šæ‰‹TileLangï¼šGPUå†…æ ¸å¼€å‘æ
 times every configuration that accepts each shape of a grid (three sizes per
 dimension, four layouts, aligned and misaligned pitches), unsplit and with
 K split 2 to 16 ways, and writes ``csrc/gemm_f16_tuned.inc``, a table the
-host planner consults before its analytic model.  Rebuild the library
-afterwards.
+host planner consults before its analytic model: per shape the fastest
+configuration and split count, and the fastest configuration unsplit (what
+a call without a workspace runs).  Measurements are logged by configuration
+name, so a log stays usable when configurations are added or removed.
+Rebuild the library afterwards.
 
     python -m tiled_dense_gemm_fp16_amd.tune [--layouts nn,nt,tn,tt] [--out PATH] [--log LOG]
     python -m tiled_dense_gemm_fp16_amd.tune --from-log LOG [LOG ...] [--out PATH]
@@ -32,7 +35,7 @@ SIZES_K = [512, 2048, 8192]
 LAYOUTS = [(False, False), (False, True), (True, False), (True, True)]
 SPLITS = [1, 2, 4, 8, 16]
 WORKSPACE_MAX = 256 << 20     # the planner's limit for automatic splits
-_SIDE = None                  # one capture stream for the whole sweep (one library workspace)
+_SIDE = None                  # one capture stream for the whole sweep
 
 
 def _time(fn, flops, target_s=0.03):
@@ -48,10 +51,6 @@ def _time(fn, flops, target_s=0.03):
         _SIDE = torch.cuda.Stream()
     side = _SIDE
     fn()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        fn()                  # sizes the library's split-K workspace for the capture stream
-    torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     s.record()
@@ -92,6 +91,7 @@ def sweep(sizes_mn, sizes_k, layouts, log, classes=(1, 0, 2)):
     import tiled_dense_gemm_fp16_amd as g
 
     rows = []
+    ws = torch.empty(WORKSPACE_MAX // 4, dtype=torch.float32, device="cuda")   # every split's workspace
     for aligned in classes:
         for M in sizes_mn:
             for N in sizes_mn:
@@ -108,6 +108,7 @@ def sweep(sizes_mn, sizes_k, layouts, log, classes=(1, 0, 2)):
                         best = None
                         results = {}
                         for cfg in range(g.num_configs()):
+                            name = g.config_name(cfg)
                             for sp in SPLITS:
                                 try:
                                     p = g.plan(m, n, k, a.data_ptr(), b.data_ptr(), c.data_ptr(), config=cfg,
@@ -119,8 +120,8 @@ def sweep(sizes_mn, sizes_k, layouts, log, classes=(1, 0, 2)):
                                                or p["workspace_bytes"] > WORKSPACE_MAX):
                                     continue
                                 tf = _time(lambda: g.gemm(a, b, out=c, config=cfg, trans_a=ta, trans_b=tb,
-                                                          splits=sp), 2.0 * m * n * k)
-                                key = f"{cfg}:{sp}"
+                                                          splits=sp, workspace=ws), 2.0 * m * n * k)
+                                key = f"{name}:{sp}"
                                 results[key] = round(tf, 1)
                                 if best is None or tf > results[best]:
                                     best = key
@@ -133,12 +134,14 @@ def sweep(sizes_mn, sizes_k, layouts, log, classes=(1, 0, 2)):
                             top = [key for key in top if results[key] >= 0.95 * results[best]][:3]
                             if len(top) > 1:
                                 again = {key: [] for key in top}
+                                index = {g.config_name(i): i for i in range(g.num_configs())}
                                 for _ in range(3):
                                     for key in top:
-                                        cfg_r, sp_r = (int(x) for x in key.split(":"))
+                                        name_r, sp_r = key.split(":")
+                                        cfg_r, sp_r = index[name_r], int(sp_r)
                                         again[key].append(_time(
                                             lambda: g.gemm(a, b, out=c, config=cfg_r, trans_a=ta, trans_b=tb,
-                                                           splits=sp_r), 2.0 * m * n * k))
+                                                           splits=sp_r, workspace=ws), 2.0 * m * n * k))
                                 retimed = {key: round(statistics.median(v), 1) for key, v in again.items()}
                                 best = max(retimed, key=retimed.get)
                         rec = {"M": m, "N": n, "K": k, "trans_a": int(ta), "trans_b": int(tb),
@@ -154,23 +157,40 @@ def sweep(sizes_mn, sizes_k, layouts, log, classes=(1, 0, 2)):
     return rows
 
 
-def write_table(rows, path, note):
+def choose(r, names):
+    """(config, splits, TFLOP/s) of the fastest run and (config, TFLOP/s) of
+    the fastest unsplit run of one sweep record, over the configurations in
+    ``names`` (the library's current list); None if none of them ran.  Keys
+    re-timed in interleaved rounds take their re-timed medians."""
+    index = {n: i for i, n in enumerate(names)}
+    vals = {k: v for k, v in {**r["tflops"], **(r.get("retimed") or {})}.items() if k.split(":")[0] in index}
+    if not vals:
+        return None
+    retimed = {k: v for k, v in (r.get("retimed") or {}).items() if k in vals}
+    best = max(retimed or vals, key=(retimed or vals).get)
+    unsplit = {k: v for k, v in vals.items() if k.endswith(":1")}
+    best1 = max(unsplit, key=unsplit.get)
+    name, sp = best.split(":")
+    return (index[name], int(sp), vals[best]), (index[best1.split(":")[0]], unsplit[best1])
+
+
+def write_table(rows, path, note, names):
     lines = [
         "// gemm_f16_tuned.inc -- measured configuration table, written by",
         "// tiled_dense_gemm_fp16_amd/tune.py; do not edit by hand.",
         f"// {note}",
         "// fields: log2 M, log2 N, log2 K (of the swept shape), trans_a, trans_b,",
         "// pitches aligned to 16 bytes (1), only B's (2: A's rows 4-byte aligned) or neither (0),",
-        "// best configuration, K splits, its TFLOP/s",
+        "// best configuration, K splits, its TFLOP/s, best configuration unsplit, its TFLOP/s",
     ]
     for r in rows:
-        if r["best"] is None:
+        picked = choose(r, names)
+        if picked is None:
             continue
+        (cfg, sp, tf), (cfg1, tf1) = picked
         lm, ln, lk = (round(math.log2(r[x])) for x in ("M", "N", "K"))
-        cfg, sp = r["best"].split(":")
-        tf = (r.get("retimed") or r["tflops"])[r["best"]]
         lines.append(f"{{{lm}, {ln}, {lk}, {r['trans_a']}, {r['trans_b']}, {r['aligned']}, {cfg}, {sp}, "
-                     f"{tf:.1f}}},")
+                     f"{tf:.1f}, {cfg1}, {tf1:.1f}}},")
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
 
@@ -186,9 +206,12 @@ def main() -> int:
     ap.add_argument("--from-log", nargs="+", default=None, metavar="LOG",
                     help="write the table from earlier sweeps' logs instead of measuring")
     args = ap.parse_args()
+    import tiled_dense_gemm_fp16_amd as g
+
+    names = [g.config_name(c) for c in range(g.num_configs())]
     if args.from_log:
         rows = [json.loads(line) for path in args.from_log for line in open(path) if line.strip()]
-        write_table(rows, args.out, f"combined from {len(args.from_log)} sweep log(s)")
+        write_table(rows, args.out, f"combined from {len(args.from_log)} sweep log(s)", names)
         print(f"wrote {args.out} ({len(rows)} shapes)", flush=True)
         return 0
     import torch
@@ -203,7 +226,7 @@ def main() -> int:
     dev = torch.cuda.get_device_properties(0)
     note = (f"swept {datetime.date.today().isoformat()} on {dev.name} "
             f"({getattr(dev, 'gcnArchName', '?')}, {dev.multi_processor_count} CUs)")
-    write_table(rows, args.out, note)
+    write_table(rows, args.out, note, names)
     print(f"wrote {args.out} ({len(rows)} shapes)", flush=True)
     return 0
 
