@@ -80,7 +80,10 @@ typedef enum gemm_f16_status {
      * caller's workspace is smaller than the plan's workspace_bytes */
     GEMM_F16_ERROR_WORKSPACE = 7,
     /* a HIP runtime call other than a launch failed */
-    GEMM_F16_ERROR_RUNTIME = 8
+    GEMM_F16_ERROR_RUNTIME = 8,
+    /* gemm_f16_split_static: the plan's workspace_bytes exceeds
+     * GEMM_F16_STATIC_WORKSPACE_BYTES */
+    GEMM_F16_ERROR_SCRATCH_LIMIT = 9
 } gemm_f16_status_t;
 
 typedef enum gemm_f16_epilogue {
@@ -178,6 +181,28 @@ gemm_f16_status_t gemm_f16_split(int64_t M, int64_t N, int64_t K,
                                  const void *A, int trans_a, const void *B, int trans_b,
                                  void *C, int epilogue, int config, int splits,
                                  void *workspace, int64_t workspace_bytes, void *stream);
+
+/*
+ * gemm_f16_split without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the fp32 partial sums go to a static
+ * device array of GEMM_F16_STATIC_WORKSPACE_BYTES that the library holds on
+ * each GPU it runs on from module load until the process ends.  The call
+ * allocates and frees nothing and does not synchronise; the first call on a
+ * device looks up that device's copy of the array.
+ *   Arguments, layouts and splits as gemm_f16_split.  A plan whose
+ *   workspace_bytes (gemm_f16_plan_split) exceeds the array returns
+ *   GEMM_F16_ERROR_SCRATCH_LIMIT before anything is launched.
+ *   Every call on one GPU uses the same array and leaves its last contents
+ *   there (no part of it needs to start at zero: each partial sum is written
+ *   before it is read).  Calls that may overlap on one GPU -- on different
+ *   streams, or from several host threads without ordering -- race on it;
+ *   order them on one stream.
+ */
+#define GEMM_F16_STATIC_WORKSPACE_BYTES ((int64_t)32 << 20)
+gemm_f16_status_t gemm_f16_split_static(int64_t M, int64_t N, int64_t K,
+                                        const void *A, int trans_a, const void *B, int trans_b,
+                                        void *C, int epilogue, int config, int splits, void *stream);
 
 /*
  * 2:4 structured-sparse A.  The pages name 2:4 sparse GEMM (`T.gemm_sp`)

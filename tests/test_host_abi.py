@@ -308,6 +308,20 @@ def test_split_without_a_workspace_is_refused_before_any_launch():
     assert st == 7
 
 
+def test_static_scratch_entry_point_limit_before_any_launch():
+    """gemm_f16_split_static refuses, before any HIP call, a split whose
+    partial sums exceed its static scratch (status 9); argument errors come
+    first, as for gemm_f16_split."""
+    call = g.lib().gemm_f16_split_static
+    # 4096 x 4096 split 2: 128 MiB of partial sums > 32 MiB
+    assert call(4096, 4096, 8192, FAKE, 0, FAKE * 128, 0, FAKE * 256, 0, 2, 2, None) == 9
+    assert g.STATIC_WORKSPACE_BYTES == 32 << 20
+    assert call(4096, 4096, 8192, FAKE, 2, FAKE * 128, 0, FAKE * 256, 0, 2, 2, None) == 1      # bad flag
+    assert call(-1, 4, 4, FAKE, 0, FAKE * 3, 0, FAKE * 2, 0, -1, 0, None) == 1                  # negative M
+    assert call(4, 4, 4, FAKE, 0, FAKE * 3, 0, FAKE * 2, 0, -1, g.MAX_SPLITS + 1, None) == 1    # split count
+    assert call(0, 4, 4, 0, 0, FAKE * 3, 0, 0, 0, -1, 0, None) == 0                            # empty output
+
+
 def test_library_imports_no_allocation_or_synchronisation():
     """The shared library does not even import the HIP calls that allocate
     or free device or host memory, or that wait for a stream or the device:

@@ -24,6 +24,7 @@ EPILOGUE_RELU = 1
 CONFIG_AUTO = -1
 SPLITS_AUTO = 0
 MAX_SPLITS = 64
+STATIC_WORKSPACE_BYTES = 32 << 20
 _EPILOGUES = {"none": EPILOGUE_NONE, "relu": EPILOGUE_RELU}
 
 # exported symbols and their ctypes signatures (mirrors include/gemm_f16.h)
@@ -53,6 +54,7 @@ SIGNATURES = {
     "gemm_f16_trans": ([_i64, _i64, _i64, _vp, _int, _vp, _int, _vp, _int, _int, _vp], _int),
     "gemm_f16_plan": ([_i64, _i64, _i64, _vp, _vp, _vp, _int, ctypes.POINTER(Plan)], _int),
     "gemm_f16_split": ([_i64, _i64, _i64, _vp, _int, _vp, _int, _vp, _int, _int, _int, _vp, _i64, _vp], _int),
+    "gemm_f16_split_static": ([_i64, _i64, _i64, _vp, _int, _vp, _int, _vp, _int, _int, _int, _vp], _int),
     "gemm_f16_plan_trans": ([_i64, _i64, _i64, _vp, _int, _vp, _int, _vp, _int, ctypes.POINTER(Plan)], _int),
     "gemm_f16_plan_split": ([_i64, _i64, _i64, _vp, _int, _vp, _int, _vp, _int, _int, ctypes.POINTER(Plan)],
                             _int),

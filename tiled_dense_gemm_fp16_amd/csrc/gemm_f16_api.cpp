@@ -571,6 +571,37 @@ gemm_f16_status_t gemm_f16_split(int64_t M, int64_t N, int64_t K, const void *A,
                workspace_bytes, stream);
 }
 
+gemm_f16_status_t gemm_f16_split_static(int64_t M, int64_t N, int64_t K, const void *A, int trans_a,
+                                        const void *B, int trans_b, void *C, int epilogue, int config, int splits,
+                                        void *stream)
+{
+    static_assert(GEMM_F16_STATIC_WORKSPACE_BYTES == kStaticScratchBytes, "header and library agree");
+    if ((trans_a != 0 && trans_a != 1) || (trans_b != 0 && trans_b != 1))
+        return GEMM_F16_ERROR_INVALID_VALUE;
+    // validate and plan first (no HIP call), so that an oversized split is
+    // refused before the scratch is looked up
+    gemm_f16_status_t st = validate(M, N, K, A, trans_a != 0, B, C, true);
+    if (st != GEMM_F16_SUCCESS)
+        return st;
+    gemm_f16_plan_t plan;
+    st = make_plan(M, N, K, A, trans_a != 0, B, trans_b != 0, C, config, splits, &plan);
+    if (st != GEMM_F16_SUCCESS)
+        return st;
+    if (plan.workspace_bytes > kStaticScratchBytes)
+        return GEMM_F16_ERROR_SCRATCH_LIMIT;
+    void *scratch = nullptr;
+    if (plan.splits > 1 && M > 0 && N > 0) {
+        int dev = -1;
+        st = check_device(&dev);
+        if (st != GEMM_F16_SUCCESS)
+            return st;
+        if (static_scratch(&scratch) != hipSuccess)
+            return GEMM_F16_ERROR_RUNTIME;
+    }
+    return run(M, N, K, A, trans_a != 0, B, trans_b != 0, C, epilogue, config, splits, scratch,
+               scratch ? kStaticScratchBytes : 0, stream);
+}
+
 gemm_f16_status_t gemm_f16_plan(int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *C,
                                 int config, gemm_f16_plan_t *plan)
 {
@@ -710,6 +741,7 @@ const char *gemm_f16_status_string(gemm_f16_status_t status)
     case GEMM_F16_ERROR_UNSUPPORTED_SIZE: return "size beyond the library's limits";
     case GEMM_F16_ERROR_WORKSPACE: return "split-K workspace missing or too small";
     case GEMM_F16_ERROR_RUNTIME: return "HIP runtime call failed";
+    case GEMM_F16_ERROR_SCRATCH_LIMIT: return "split needs more than the static split-K scratch holds";
     }
     return "unknown status";
 }

@@ -67,6 +67,13 @@ constexpr int kNumSpConfigs = 4;
 extern const ConfigDesc kSpConfigs[kNumSpConfigs];
 hipError_t launch_sparse(int config, const KernelArgs &a, bool trans_b, int64_t grid, hipStream_t s);
 
+// Static split-K scratch (gemm_f16_split_static): kStaticScratchBytes of
+// device memory per GPU.  static_scratch() returns the current device's copy
+// (looked up once per device; no allocation).
+constexpr int64_t kStaticScratchBytes = (int64_t)32 << 20;
+constexpr int kMaxScratchDevices = 64;
+hipError_t static_scratch(void **ptr);
+
 // Split-K reduction: C = rne16(epi(W[0] + ... + W[splits-1])) over M x N
 // elements (relu: 1 for the ReLU epilogue).  vec4: N % 4 == 0, C 8-byte and
 // W 16-byte aligned.

@@ -1,9 +1,41 @@
 // gemm_f16_kernels.hip -- the split-K reduction kernel and the dispatch of
 // a planned call to the kernel of its layout (the tile kernel itself is in
 // gemm_f16_tile.h).
+#include <mutex>
+
 #include "gemm_f16_tile.h"
 
 namespace gemm_f16_impl {
+
+// ---- static split-K scratch -------------------------------------------------------
+// Device memory for the split-K partial sums of gemm_f16_split_static, for
+// callers that cannot allocate: one array per GPU, held from module load
+// until the process ends.  Host code never uses this name as an address
+// (there it is only a host-side stand-in): static_scratch() looks up each
+// device's own copy once and every kernel argument, copy or fill uses that.
+static __device__ __align__(256) float scratch[kStaticScratchBytes / sizeof(float)];
+
+hipError_t static_scratch(void **ptr)
+{
+    static std::mutex mutex;
+    static void *addr[kMaxScratchDevices];
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxScratchDevices)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mutex);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return e;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
 
 // ---- split-K reduction ---------------------------------------------------------
 // C = rne16(epi(sum over s of W[s])) elementwise, the splits added in index
