@@ -55,6 +55,12 @@ def _lib():
         lib.oracle_cpu_threads.argtypes = []
         lib.oracle_cpu_threads.restype = ctypes.c_int
         lib.oracle_gemm_f16.argtypes = [i64, i64, i64, u16p, u16p, ctypes.c_int, u16p, ctypes.c_int]
+        lib.oracle_gemm_f16_scaled.argtypes = [i64, i64, i64, u16p, u16p, ctypes.c_double, ctypes.c_int, u16p,
+                                               ctypes.c_int]
+        lib.oracle_gemm_f16_scaled.restype = ctypes.c_int
+        lib.oracle_gemm_f16_sampled_scaled.argtypes = [i64, i64, i64, u16p, u16p, i64p, i64, i64p, i64,
+                                                       ctypes.c_double, ctypes.c_int, u16p, ctypes.c_int]
+        lib.oracle_gemm_f16_sampled_scaled.restype = ctypes.c_int
         lib.oracle_gemm_f16.restype = ctypes.c_int
         lib.oracle_gemm_f16_sampled.argtypes = [i64, i64, i64, u16p, u16p, i64p, i64, i64p, i64,
                                                 ctypes.c_int, u16p, ctypes.c_int]
@@ -106,12 +112,21 @@ def encode(x) -> np.ndarray:
     return out
 
 
+def as_binary32(scale) -> float:
+    """The exact value of ``scale`` rounded to binary32, the precision in
+    which the library takes the epilogue's scale."""
+    return float(np.float32(scale))
+
+
 def gemm(A, B, relu: bool = False, threads: int = 0, trans_a: bool = False,
-         trans_b: bool = False) -> np.ndarray:
-    """C = rne16(epi(op(A) . op(B))) for binary16 operands; returns uint16 (M x N).
+         trans_b: bool = False, scale: float = 1.0) -> np.ndarray:
+    """C = rne16(epi(scale * (op(A) . op(B)))) for binary16 operands; returns
+    uint16 (M x N).
 
     op(X) is X, or its transpose when the flag is set (A given K x M, B given
-    N x K); the transpose is a plain array copy before the product."""
+    N x K); the transpose is a plain array copy before the product.  ``scale``
+    is used at its exact value: pass ``as_binary32(s)`` to mirror a binary32
+    scale."""
     A = _as_bits(A, "A")
     B = _as_bits(B, "B")
     if trans_a:
@@ -123,15 +138,16 @@ def gemm(A, B, relu: bool = False, threads: int = 0, trans_a: bool = False,
     M, K = A.shape
     N = B.shape[1]
     C = np.zeros((M, N), dtype=np.uint16)
-    rc = _lib().oracle_gemm_f16(M, N, K, _ptr(A, ctypes.c_uint16), _ptr(B, ctypes.c_uint16),
-                                int(bool(relu)), _ptr(C, ctypes.c_uint16), int(threads))
+    rc = _lib().oracle_gemm_f16_scaled(M, N, K, _ptr(A, ctypes.c_uint16), _ptr(B, ctypes.c_uint16),
+                                       float(scale), int(bool(relu)), _ptr(C, ctypes.c_uint16), int(threads))
     if rc != 0:
-        raise RuntimeError("oracle_gemm_f16 failed")
+        raise RuntimeError("oracle_gemm_f16_scaled failed")
     return C
 
 
-def gemm_sampled(A, B, rows, cols, relu: bool = False, threads: int = 0) -> np.ndarray:
-    """The block C[rows x cols] of rne16(epi(A . B)); returns uint16 (len(rows) x len(cols))."""
+def gemm_sampled(A, B, rows, cols, relu: bool = False, threads: int = 0, scale: float = 1.0) -> np.ndarray:
+    """The block C[rows x cols] of rne16(epi(scale * (A . B))); returns uint16
+    (len(rows) x len(cols))."""
     A = _as_bits(A, "A")
     B = _as_bits(B, "B")
     if A.ndim != 2 or B.ndim != 2 or A.shape[1] != B.shape[0]:
@@ -141,10 +157,10 @@ def gemm_sampled(A, B, rows, cols, relu: bool = False, threads: int = 0) -> np.n
     rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
     cols = np.ascontiguousarray(np.asarray(cols, dtype=np.int64))
     C = np.zeros((rows.size, cols.size), dtype=np.uint16)
-    rc = _lib().oracle_gemm_f16_sampled(M, N, K, _ptr(A, ctypes.c_uint16), _ptr(B, ctypes.c_uint16),
-                                        _ptr(rows, ctypes.c_int64), rows.size,
-                                        _ptr(cols, ctypes.c_int64), cols.size,
-                                        int(bool(relu)), _ptr(C, ctypes.c_uint16), int(threads))
+    rc = _lib().oracle_gemm_f16_sampled_scaled(M, N, K, _ptr(A, ctypes.c_uint16), _ptr(B, ctypes.c_uint16),
+                                               _ptr(rows, ctypes.c_int64), rows.size,
+                                               _ptr(cols, ctypes.c_int64), cols.size, float(scale),
+                                               int(bool(relu)), _ptr(C, ctypes.c_uint16), int(threads))
     if rc != 0:
         raise RuntimeError("oracle_gemm_f16_sampled failed (bad index or allocation failure)")
     return C

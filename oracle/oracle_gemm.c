@@ -1,5 +1,5 @@
 /*
- * oracle_gemm.c -- CPU oracle for the tiled FP16 GEMM  C = epi(A . B).
+ * oracle_gemm.c -- CPU oracle for the tiled FP16 GEMM  C = epi(alpha (A . B)).
  *
  * TEST INFRASTRUCTURE ONLY.  This file is the slow, plain reference that the
  * GPU library is checked against.  Only the test suite, the smoke check and
@@ -7,7 +7,7 @@
  * It shares no code, header, table or constant with the HIP library.
  *
  * What it computes (the plain definition the tiled method reaches):
- *   C[i][j] = rne16( epi( sum_{k=0}^{K-1} a(A[i][k]) * a(B[k][j]) ) )
+ *   C[i][j] = rne16( epi( alpha * sum_{k=0}^{K-1} a(A[i][k]) * a(B[k][j]) ) )
  * - A is M x K and B is K x N, both row-major IEEE binary16 bit patterns.
  *   ("TileLang：比 Triton 低一层的 tile 语言", section "第一个 kernel：GEMM":
  *   each output tile is the product of an A row-panel and a B column-panel.)
@@ -15,9 +15,15 @@
  *   The pages keep the accumulator in fp32 and convert to fp16 only in the
  *   final copy ("5分钟上手TileLang：GPU内核开发指南", section "避坑与调参");
  *   the oracle uses fp64, which is at least as accurate, and rounds once.
+ * - alpha scales the fp32 result block before anything else touches it, as
+ *   the pages' FlashAttention forward scales its score block Q . K^T
+ *   ("TileLang：比 Triton 低一层的 tile 语言", section "FlashAttention：在线
+ *   softmax 写成 tile 代码").  alpha = 1 is the plain product.  The caller
+ *   passes alpha's exact value (the library takes it as a binary32); the
+ *   product with the fp64 sum is taken in fp64.
  * - epi is the identity or the ReLU max(x, 0) of the quickstart's fused
  *   epilogue ("TileLang：让GPU编程像Python一样简单的高性能计算新范式",
- *   section "并行计算的优雅表达").
+ *   section "并行计算的优雅表达"), applied after the scale.
  * - rne16 rounds to the nearest binary16 value, ties to even (IEEE default).
  *
  * Every product of two binary16 values is exact in binary64 (at most 22
@@ -116,6 +122,7 @@ typedef struct {
     uint16_t *C;            /* nrows x ncols */
     const int64_t *rows;    /* which A rows, length nrows */
     int64_t K, ncols;
+    double scale;
     int relu;
     int64_t r_begin, r_end; /* this worker's slice of the nrows output rows */
     int status;
@@ -142,7 +149,7 @@ static void *oracle_worker(void *p)
         }
         uint16_t *crow = j->C + r * j->ncols;
         for (int64_t c = 0; c < j->ncols; ++c) {
-            double v = acc[c];
+            double v = j->scale * acc[c];
             if (j->relu)
                 v = v > 0.0 ? v : 0.0;
             crow[c] = oracle_f16_encode(v);
@@ -153,14 +160,15 @@ static void *oracle_worker(void *p)
     return NULL;
 }
 
-/* C[r][c] = rne16(epi(sum_k A[rows[r]][k] * B[k][cols[c]])) for the given
- * row and column index lists (the full product when they are 0..M-1 and
- * 0..N-1).  Returns 0 on success, -1 on bad arguments or allocation failure. */
-int oracle_gemm_f16_sampled(int64_t M, int64_t N, int64_t K,
-                            const uint16_t *A, const uint16_t *B,
-                            const int64_t *rows, int64_t nrows,
-                            const int64_t *cols, int64_t ncols,
-                            int relu, uint16_t *C, int nthreads)
+/* C[r][c] = rne16(epi(scale * sum_k A[rows[r]][k] * B[k][cols[c]])) for
+ * the given row and column index lists (the full product when they are
+ * 0..M-1 and 0..N-1).  Returns 0 on success, -1 on bad arguments or
+ * allocation failure. */
+int oracle_gemm_f16_sampled_scaled(int64_t M, int64_t N, int64_t K,
+                                   const uint16_t *A, const uint16_t *B,
+                                   const int64_t *rows, int64_t nrows,
+                                   const int64_t *cols, int64_t ncols,
+                                   double scale, int relu, uint16_t *C, int nthreads)
 {
     if (M < 0 || N < 0 || K < 0 || nrows < 0 || ncols < 0)
         return -1;
@@ -201,6 +209,7 @@ int oracle_gemm_f16_sampled(int64_t M, int64_t N, int64_t K,
         jobs[t].rows = rows;
         jobs[t].K = K;
         jobs[t].ncols = ncols;
+        jobs[t].scale = scale;
         jobs[t].relu = relu;
         jobs[t].r_begin = nrows * t / nthreads;
         jobs[t].r_end = nrows * (t + 1) / nthreads;
@@ -227,10 +236,20 @@ int oracle_gemm_f16_sampled(int64_t M, int64_t N, int64_t K,
     return rc;
 }
 
+/* The unscaled block (scale 1). */
+int oracle_gemm_f16_sampled(int64_t M, int64_t N, int64_t K,
+                            const uint16_t *A, const uint16_t *B,
+                            const int64_t *rows, int64_t nrows,
+                            const int64_t *cols, int64_t ncols,
+                            int relu, uint16_t *C, int nthreads)
+{
+    return oracle_gemm_f16_sampled_scaled(M, N, K, A, B, rows, nrows, cols, ncols, 1.0, relu, C, nthreads);
+}
+
 /* The full product: every row and every column. */
-int oracle_gemm_f16(int64_t M, int64_t N, int64_t K,
-                    const uint16_t *A, const uint16_t *B, int relu,
-                    uint16_t *C, int nthreads)
+int oracle_gemm_f16_scaled(int64_t M, int64_t N, int64_t K,
+                           const uint16_t *A, const uint16_t *B, double scale, int relu,
+                           uint16_t *C, int nthreads)
 {
     if (M < 0 || N < 0 || K < 0)
         return -1;
@@ -247,8 +266,15 @@ int oracle_gemm_f16(int64_t M, int64_t N, int64_t K,
         rows[i] = i;
     for (int64_t j = 0; j < N; ++j)
         cols[j] = j;
-    int rc = oracle_gemm_f16_sampled(M, N, K, A, B, rows, M, cols, N, relu, C, nthreads);
+    int rc = oracle_gemm_f16_sampled_scaled(M, N, K, A, B, rows, M, cols, N, scale, relu, C, nthreads);
     free(rows);
     free(cols);
     return rc;
+}
+
+int oracle_gemm_f16(int64_t M, int64_t N, int64_t K,
+                    const uint16_t *A, const uint16_t *B, int relu,
+                    uint16_t *C, int nthreads)
+{
+    return oracle_gemm_f16_scaled(M, N, K, A, B, 1.0, relu, C, nthreads);
 }

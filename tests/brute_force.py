@@ -51,7 +51,8 @@ def round_to_f16(x: Fraction) -> int:
     return sign | (bits[lo] if bits[lo] % 2 == 0 else bits[hi])
 
 
-def gemm(A_bits: np.ndarray, B_bits: np.ndarray, relu: bool = False) -> np.ndarray:
+def gemm(A_bits: np.ndarray, B_bits: np.ndarray, relu: bool = False, scale: Fraction = Fraction(1)) -> np.ndarray:
+    """rne16(epi(scale * exact sum)); a zero result is returned as +0."""
     M, K = A_bits.shape
     K2, N = B_bits.shape
     assert K == K2
@@ -60,7 +61,7 @@ def gemm(A_bits: np.ndarray, B_bits: np.ndarray, relu: bool = False) -> np.ndarr
     out = np.zeros((M, N), dtype=np.uint16)
     for i in range(M):
         for j in range(N):
-            s = sum((a[i][k] * b[k][j] for k in range(K)), Fraction(0))
+            s = scale * sum((a[i][k] * b[k][j] for k in range(K)), Fraction(0))
             if relu and s < 0:
                 s = Fraction(0)
             out[i, j] = round_to_f16(s)

@@ -24,6 +24,8 @@ import torch
 
 import oracle
 import workloads
+from fractions import Fraction
+
 from tests import brute_force
 
 
@@ -209,3 +211,69 @@ def test_transposed_operands_match_brute_force(ta, tb):
     opA = np.ascontiguousarray(A.T) if ta else A
     opB = np.ascontiguousarray(B.T) if tb else B
     assert np.array_equal(oracle.gemm(A, B, trans_a=ta, trans_b=tb), brute_force.gemm(opA, opB))
+
+
+# ---- the scale epilogue: C = rne16(epi(alpha * sum)) ----------------------------
+# alpha as a binary32 (the library's precision for it), used at its exact value
+
+@pytest.mark.parametrize("alpha", [0.1, -1.5, 1.0 / np.sqrt(128.0), 3.0, -0.0078125])
+@pytest.mark.parametrize("relu", [False, True])
+def test_scaled_brute_force_exact(alpha, relu):
+    """Against exact rational arithmetic with Fraction(alpha): bit-identical,
+    except that a zero result may carry either sign in the oracle (IEEE
+    products keep the sign of a zero; the rational reference has none)."""
+    a32 = oracle.as_binary32(alpha)
+    for M, N, K in [(2, 3, 5), (5, 8, 3), (3, 2, 16), (4, 4, 40)]:
+        rng = np.random.default_rng(M * 1000 + N * 100 + K + int(relu))
+        A = exact_range_operands(rng, (M, K))
+        B = exact_range_operands(rng, (K, N))
+        ref = brute_force.gemm(A, B, relu=relu, scale=Fraction(a32))
+        got = oracle.gemm(A, B, relu=relu, scale=a32)
+        zero = (ref & 0x7FFF) == 0
+        assert np.array_equal(got[~zero], ref[~zero]), (alpha, relu, M, N, K)
+        assert np.all((got[zero] & 0x7FFF) == 0)
+
+
+def test_scale_one_is_the_plain_product():
+    A, B = workloads.draw(37, 29, 90, "uniform", 11)
+    A, B = bits(A), bits(B)
+    for relu in (False, True):
+        assert np.array_equal(oracle.gemm(A, B, relu=relu, scale=1.0), oracle.gemm(A, B, relu=relu))
+        assert np.array_equal(oracle.gemm_sampled(A, B, [0, 5, 36], [1, 28], relu=relu, scale=1.0),
+                              oracle.gemm(A, B, relu=relu)[[0, 5, 36]][:, [1, 28]])
+
+
+@pytest.mark.parametrize("e", [-4, -1, 3])
+def test_power_of_two_scale_commutes_with_rounding(e):
+    """alpha = 2^e: rne16(2^e s) = 2^e rne16(s) wherever neither rounding
+    leaves the normal range, so the scaled result is the plain one times 2^e,
+    bit for bit."""
+    A, B = workloads.draw(40, 50, 60, "uniform", 12)
+    A, B = bits(A), bits(B)
+    c = oracle.decode(oracle.gemm(A, B))
+    cs = oracle.decode(oracle.gemm(A, B, scale=2.0 ** e))
+    normal = (np.abs(c) >= 2.0 ** -14) & (np.abs(c) * 2.0 ** e >= 2.0 ** -14) & (np.abs(c) * 2.0 ** e < 60000)
+    assert normal.mean() > 0.9
+    assert np.array_equal(cs[normal], c[normal] * 2.0 ** e)
+
+
+def test_relu_applies_after_the_scale():
+    """With a negative scale the positive results come from negative sums:
+    relu(-0.5 s) is max(-0.5 rne16(s), 0), exactly (a power-of-two scale);
+    a ReLU before the scale would leave nothing positive."""
+    A, B = workloads.draw(33, 45, 70, "uniform", 13)
+    A, B = bits(A), bits(B)
+    c = oracle.decode(oracle.gemm(A, B))
+    r = oracle.gemm(A, B, relu=True, scale=-0.5)
+    want = np.maximum(-0.5 * c, 0.0)
+    normal = (np.abs(c) >= 2.0 ** -13) | (c == 0)
+    assert (want > 0).any() and (want == 0).any()
+    assert np.array_equal(oracle.decode(r)[normal], want[normal])
+    assert np.all(r[want == 0] == 0)                            # +0, never -0
+
+
+def test_zero_scale_gives_zeros():
+    A, B = workloads.draw(16, 24, 32, "uniform", 14)
+    A, B = bits(A), bits(B)
+    assert np.all((oracle.gemm(A, B, scale=0.0) & 0x7FFF) == 0)
+    assert np.all(oracle.gemm(A, B, scale=0.0, relu=True) == 0)
