@@ -183,6 +183,28 @@ gemm_f16_status_t gemm_f16_split(int64_t M, int64_t N, int64_t K,
                                  void *workspace, int64_t workspace_bytes, void *stream);
 
 /*
+ * C = epi(alpha * (op(A) . op(B))): the fp32 result block is multiplied by
+ * alpha (an fp32 value) before the epilogue and the single rounding to
+ * binary16.  This is the scaling the pages apply to the score block of the
+ * transpose_B product, Q . K^T, before anything else touches it
+ * ("TileLang：比 Triton 低一层的 tile 语言", section "FlashAttention：在线
+ * softmax 写成 tile 代码").  With epilogue RELU the result is
+ * rne16(max(alpha * sum, 0)).  alpha = 1 gives exactly gemm_f16_trans's
+ * result; any alpha is accepted (IEEE arithmetic for NaN or inf).  Other
+ * arguments, layouts and errors as gemm_f16_trans (runs unsplit).
+ */
+gemm_f16_status_t gemm_f16_scaled(int64_t M, int64_t N, int64_t K,
+                                  const void *A, int trans_a, const void *B, int trans_b,
+                                  void *C, float alpha, int epilogue, int config, void *stream);
+
+/* gemm_f16_split with the scale of gemm_f16_scaled (applied by the
+ * reduction to the sum of the partials, in fp32). */
+gemm_f16_status_t gemm_f16_split_scaled(int64_t M, int64_t N, int64_t K,
+                                        const void *A, int trans_a, const void *B, int trans_b,
+                                        void *C, float alpha, int epilogue, int config, int splits,
+                                        void *workspace, int64_t workspace_bytes, void *stream);
+
+/*
  * gemm_f16_split without a workspace argument, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid allocation): the fp32 partial sums go to a static

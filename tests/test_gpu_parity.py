@@ -336,3 +336,63 @@ def test_workload_sampled(name):
     got = u16(c[torch.from_numpy(edge_r).to(DEV)][:, torch.from_numpy(edge_c).to(DEV)])
     res = oracle.compare(got, oracle.gemm_sampled(u16(a), u16(b), edge_r, edge_c))
     assert res["pass"], res
+
+
+# ---- the scale epilogue: C = rne16(epi(alpha * (op(A) . op(B)))) ----------------
+# the pages scale the fp32 score block of the transpose_B product before anything
+# else touches it ("TileLang：比 Triton 低一层的 tile 语言", section "FlashAttention：
+# 在线 softmax 写成 tile 代码"); the scale there is 1/sqrt(dim) * log2(e)
+
+def qk_scale(dim):
+    return float(1.0 / np.sqrt(dim) * 1.44269504)
+
+
+def stored_operands(M, N, K, ta, tb, seed, dist="uniform"):
+    a, b = workloads.draw(M, N, K, dist, seed)
+    return a, b, (a.t().contiguous() if ta else a), (b.t().contiguous() if tb else b)
+
+
+@pytest.mark.parametrize("ta,tb", [(False, False), (False, True), (True, False), (True, True)])
+def test_scale_epilogue_every_config(ta, tb):
+    M, N, K = 300, 264, 136
+    a, b, a_st, b_st = stored_operands(M, N, K, ta, tb, 31 + 2 * ta + tb)
+    ad, bd = a_st.to(DEV), b_st.to(DEV)
+    for epilogue, alpha in (("none", qk_scale(K)), ("relu", -0.75), ("none", -3.0)):
+        ref = oracle.gemm(u16(a), u16(b), relu=(epilogue == "relu"), scale=oracle.as_binary32(alpha))
+        for c in configs_for(M, N, K, trans_a=ta, trans_b=tb):
+            print(f"[scale] ta={int(ta)} tb={int(tb)} epi={epilogue} alpha={alpha:.6g} config={c}", flush=True)
+            got = g.gemm(ad, bd, epilogue=epilogue, config=c, trans_a=ta, trans_b=tb, alpha=alpha, splits=1)
+            torch.cuda.synchronize()
+            res = oracle.compare(u16(got), ref)
+            assert res["pass"], (ta, tb, epilogue, alpha, c, res)
+
+
+def test_power_of_two_scale_is_exact():
+    """alpha = 2^e: the fp32 product is exact and RNE commutes with it, so
+    the scaled result is the unscaled one times 2^e, bit for bit, wherever
+    neither leaves the normal range (every layout, automatic configuration)."""
+    M, N, K = 1024, 768, 1024
+    for ta, tb in [(False, False), (False, True), (True, False), (True, True)]:
+        _, _, a_st, b_st = stored_operands(M, N, K, ta, tb, 40 + 2 * ta + tb)
+        ad, bd = a_st.to(DEV), b_st.to(DEV)
+        plain = oracle.decode(u16(g.gemm(ad, bd, trans_a=ta, trans_b=tb, splits=1)))
+        for e in (-3, 2):
+            scaled = oracle.decode(u16(g.gemm(ad, bd, trans_a=ta, trans_b=tb, alpha=2.0 ** e, splits=1)))
+            ok = (np.abs(plain) >= 2.0 ** -14) & (np.abs(plain) * 2.0 ** e >= 2.0 ** -14)
+            assert ok.mean() > 0.9
+            assert np.array_equal(scaled[ok], plain[ok] * 2.0 ** e), (ta, tb, e)
+        one = u16(g.gemm(ad, bd, trans_a=ta, trans_b=tb, alpha=1.0, splits=1))
+        assert np.array_equal(oracle.decode(one), plain)
+
+
+def test_scaled_score_block_shape():
+    """The score-block shape of an attention layer (2048 queries x 2304 keys,
+    head dimension 1024 as K), B given N x K as in Q . K^T, scaled by the
+    pages' 1/sqrt(dim) log2(e): full parity with the automatic choice."""
+    M, N, K = 2048, 2304, 1024
+    a, b, a_st, b_st = stored_operands(M, N, K, False, True, 50, dist="normal")
+    alpha = qk_scale(K)
+    got = g.gemm(a_st.to(DEV), b_st.to(DEV), trans_b=True, alpha=alpha, splits=1)
+    torch.cuda.synchronize()
+    res = oracle.compare(u16(got), oracle.gemm(u16(a), u16(b), scale=oracle.as_binary32(alpha)))
+    assert res["pass"], res

@@ -224,3 +224,21 @@ def test_split_in_a_captured_graph():
         g.gemm(case.ad, case.bd, splits=3)     # eager split work between the replays
         torch.cuda.synchronize()
     del graph
+
+
+def test_split_scaled():
+    """The scale of the scaled entry points on the split path: the reduction
+    multiplies the sum of the partials by alpha before the ReLU."""
+    for ta, tb, shape in [(False, False, (300, 264, 1000)), (False, True, (130, 72, 777)),
+                          (True, True, (257, 520, 600))]:
+        case = Case(*shape, ta=ta, tb=tb, seed=60 + shape[2])
+        for alpha, epilogue in ((-0.6, "relu"), (0.0883883, "none")):
+            ref = oracle.gemm(u16(case.a), u16(case.b), relu=(epilogue == "relu"), trans_a=ta, trans_b=tb,
+                              scale=oracle.as_binary32(alpha))
+            for c in configs_for(*shape, ta, tb):
+                print(f"[split-scaled] {shape} ta={int(ta)} tb={int(tb)} config={c} alpha={alpha}", flush=True)
+                out = g.gemm(case.ad, case.bd, epilogue=epilogue, config=c, trans_a=ta, trans_b=tb, splits=3,
+                             alpha=alpha)
+                torch.cuda.synchronize()
+                res = oracle.compare(u16(out), ref)
+                assert res["pass"], (shape, c, alpha, res)

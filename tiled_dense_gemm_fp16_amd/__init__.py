@@ -55,6 +55,9 @@ SIGNATURES = {
     "gemm_f16_plan": ([_i64, _i64, _i64, _vp, _vp, _vp, _int, ctypes.POINTER(Plan)], _int),
     "gemm_f16_split": ([_i64, _i64, _i64, _vp, _int, _vp, _int, _vp, _int, _int, _int, _vp, _i64, _vp], _int),
     "gemm_f16_split_static": ([_i64, _i64, _i64, _vp, _int, _vp, _int, _vp, _int, _int, _int, _vp], _int),
+    "gemm_f16_scaled": ([_i64, _i64, _i64, _vp, _int, _vp, _int, _vp, ctypes.c_float, _int, _int, _vp], _int),
+    "gemm_f16_split_scaled": ([_i64, _i64, _i64, _vp, _int, _vp, _int, _vp, ctypes.c_float, _int, _int, _int,
+                               _vp, _i64, _vp], _int),
     "gemm_f16_plan_trans": ([_i64, _i64, _i64, _vp, _int, _vp, _int, _vp, _int, ctypes.POINTER(Plan)], _int),
     "gemm_f16_plan_split": ([_i64, _i64, _i64, _vp, _int, _vp, _int, _vp, _int, _int, ctypes.POINTER(Plan)],
                             _int),
@@ -161,8 +164,9 @@ def _auto_split(M, N, K, a, b, out, config, trans_a, trans_b, splits):
 
 
 def gemm(a, b, epilogue: str = "none", out=None, config: int = CONFIG_AUTO, stream=None,
-         trans_a: bool = False, trans_b: bool = False, splits: int | None = None, workspace=None):
-    """C = epi(op(a) @ op(b)) for 2-D contiguous float16 GPU tensors.
+         trans_a: bool = False, trans_b: bool = False, splits: int | None = None, workspace=None,
+         alpha: float = 1.0):
+    """C = epi(alpha * (op(a) @ op(b))) for 2-D contiguous float16 GPU tensors.
 
     a is M x K (or K x M with ``trans_a``), b is K x N (or N x K with
     ``trans_b``).  Returns ``out`` (allocated as an M x N float16 tensor when
@@ -175,7 +179,8 @@ def gemm(a, b, epilogue: str = "none", out=None, config: int = CONFIG_AUTO, stre
     split needs a workspace of fp32 partial sums: ``workspace`` (a contiguous
     GPU tensor used as scratch) or, when it is None, one taken from torch's
     caching allocator on ``stream`` for this call.  The C library itself
-    never allocates.
+    never allocates.  ``alpha`` (taken as an fp32 value) scales the result
+    before the epilogue (gemm_f16_scaled / gemm_f16_split_scaled).
     """
     import torch
 
@@ -216,15 +221,26 @@ def gemm(a, b, epilogue: str = "none", out=None, config: int = CONFIG_AUTO, stre
                     workspace = torch.empty(-(-ws_bytes // 4), dtype=torch.float32, device=a.device)
             else:
                 request = 1
+        scaled = float(alpha) != 1.0
         if workspace is None and request in (1, SPLITS_AUTO):
-            st = gemm_f16_raw(M, N, K, a.data_ptr(), b.data_ptr(), out.data_ptr(), _EPILOGUES[epilogue],
-                              stream.cuda_stream, config, trans_a, trans_b)
+            if scaled:
+                st = lib().gemm_f16_scaled(M, N, K, a.data_ptr() or None, int(trans_a), b.data_ptr() or None,
+                                           int(trans_b), out.data_ptr() or None, float(alpha), _EPILOGUES[epilogue],
+                                           config, stream.cuda_stream or None)
+            else:
+                st = gemm_f16_raw(M, N, K, a.data_ptr(), b.data_ptr(), out.data_ptr(), _EPILOGUES[epilogue],
+                                  stream.cuda_stream, config, trans_a, trans_b)
         else:
             ws_ptr = workspace.data_ptr() if workspace is not None else None
             ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-            st = lib().gemm_f16_split(M, N, K, a.data_ptr() or None, int(trans_a), b.data_ptr() or None,
-                                      int(trans_b), out.data_ptr() or None, _EPILOGUES[epilogue], config,
-                                      request, ws_ptr or None, ws_bytes, stream.cuda_stream or None)
+            args = (M, N, K, a.data_ptr() or None, int(trans_a), b.data_ptr() or None, int(trans_b),
+                    out.data_ptr() or None)
+            if scaled:
+                st = lib().gemm_f16_split_scaled(*args, float(alpha), _EPILOGUES[epilogue], config, request,
+                                                 ws_ptr or None, ws_bytes, stream.cuda_stream or None)
+            else:
+                st = lib().gemm_f16_split(*args, _EPILOGUES[epilogue], config, request, ws_ptr or None, ws_bytes,
+                                          stream.cuda_stream or None)
     if st != SUCCESS:
         raise GemmError(st, "gemm_f16")
     return out

@@ -386,7 +386,8 @@ gemm_f16_status_t check_device(int *device)
 
 // Enqueue a planned call; W is the split-K workspace (plan->splits > 1).
 gemm_f16_status_t launch_plan(const gemm_f16_plan_t &plan, int64_t M, int64_t N, int64_t K, const void *A,
-                              bool ta, const void *B, bool tb, void *C, int epilogue, void *W, hipStream_t s)
+                              bool ta, const void *B, bool tb, void *C, float alpha, int epilogue, void *W,
+                              hipStream_t s)
 {
     KernelArgs a;
     a.A = (const _Float16 *)A;
@@ -399,13 +400,14 @@ gemm_f16_status_t launch_plan(const gemm_f16_plan_t &plan, int64_t M, int64_t N,
     a.tiles_n = (int)plan.tiles_n;
     a.group_m = GEMM_F16_GROUP_M;
     a.relu = epilogue == GEMM_F16_EPILOGUE_RELU ? 1 : 0;
+    a.alpha = alpha;
     a.vec_c = plan.vec_c;
     a.k_split = (int)plan.k_split;
     a.W = plan.splits > 1 ? (float *)W : nullptr;
     a.meta = nullptr;
     hipError_t e = launch(plan.config, a, plan.vec_a, plan.vec_b, ta, tb, plan.grid, s);
     if (e == hipSuccess && plan.splits > 1)
-        e = launch_reduce((const float *)W, (_Float16 *)C, M, N, plan.splits, a.relu, plan.vec_c >= 4, s);
+        e = launch_reduce((const float *)W, (_Float16 *)C, M, N, plan.splits, alpha, a.relu, plan.vec_c >= 4, s);
     return e == hipSuccess ? GEMM_F16_SUCCESS : GEMM_F16_ERROR_LAUNCH_FAILED;
 }
 
@@ -413,7 +415,7 @@ gemm_f16_status_t launch_plan(const gemm_f16_plan_t &plan, int64_t M, int64_t N,
 // that splits then fails with GEMM_F16_ERROR_WORKSPACE before any HIP call.
 // The library allocates no device memory and never waits on the stream.
 gemm_f16_status_t run(int64_t M, int64_t N, int64_t K, const void *A, bool ta, const void *B, bool tb, void *C,
-                      int epilogue, int config, int splits, void *workspace, int64_t workspace_bytes,
+                      float alpha, int epilogue, int config, int splits, void *workspace, int64_t workspace_bytes,
                       void *stream)
 {
     gemm_f16_status_t st = validate(M, N, K, A, ta, B, C, true);
@@ -445,7 +447,7 @@ gemm_f16_status_t run(int64_t M, int64_t N, int64_t K, const void *A, bool ta, c
     st = check_device(&dev);
     if (st != GEMM_F16_SUCCESS)
         return st;
-    return launch_plan(plan, M, N, K, A, ta, B, tb, C, epilogue, workspace, (hipStream_t)stream);
+    return launch_plan(plan, M, N, K, A, ta, B, tb, C, alpha, epilogue, workspace, (hipStream_t)stream);
 }
 
 // ---- 2:4 structured-sparse A -------------------------------------------------
@@ -544,13 +546,13 @@ extern "C" {
 gemm_f16_status_t gemm_f16(int64_t M, int64_t N, int64_t K, const void *A, const void *B, void *C,
                            int epilogue, void *stream)
 {
-    return run(M, N, K, A, false, B, false, C, epilogue, GEMM_F16_CONFIG_AUTO, 1, nullptr, 0, stream);
+    return run(M, N, K, A, false, B, false, C, 1.0f, epilogue, GEMM_F16_CONFIG_AUTO, 1, nullptr, 0, stream);
 }
 
 gemm_f16_status_t gemm_f16_ex(int64_t M, int64_t N, int64_t K, const void *A, const void *B, void *C,
                               int epilogue, int config, void *stream)
 {
-    return run(M, N, K, A, false, B, false, C, epilogue, config, 1, nullptr, 0, stream);
+    return run(M, N, K, A, false, B, false, C, 1.0f, epilogue, config, 1, nullptr, 0, stream);
 }
 
 gemm_f16_status_t gemm_f16_trans(int64_t M, int64_t N, int64_t K, const void *A, int trans_a, const void *B,
@@ -558,7 +560,25 @@ gemm_f16_status_t gemm_f16_trans(int64_t M, int64_t N, int64_t K, const void *A,
 {
     if ((trans_a != 0 && trans_a != 1) || (trans_b != 0 && trans_b != 1))
         return GEMM_F16_ERROR_INVALID_VALUE;
-    return run(M, N, K, A, trans_a != 0, B, trans_b != 0, C, epilogue, config, 1, nullptr, 0, stream);
+    return run(M, N, K, A, trans_a != 0, B, trans_b != 0, C, 1.0f, epilogue, config, 1, nullptr, 0, stream);
+}
+
+gemm_f16_status_t gemm_f16_scaled(int64_t M, int64_t N, int64_t K, const void *A, int trans_a, const void *B,
+                                  int trans_b, void *C, float alpha, int epilogue, int config, void *stream)
+{
+    if ((trans_a != 0 && trans_a != 1) || (trans_b != 0 && trans_b != 1))
+        return GEMM_F16_ERROR_INVALID_VALUE;
+    return run(M, N, K, A, trans_a != 0, B, trans_b != 0, C, alpha, epilogue, config, 1, nullptr, 0, stream);
+}
+
+gemm_f16_status_t gemm_f16_split_scaled(int64_t M, int64_t N, int64_t K, const void *A, int trans_a,
+                                        const void *B, int trans_b, void *C, float alpha, int epilogue, int config,
+                                        int splits, void *workspace, int64_t workspace_bytes, void *stream)
+{
+    if ((trans_a != 0 && trans_a != 1) || (trans_b != 0 && trans_b != 1))
+        return GEMM_F16_ERROR_INVALID_VALUE;
+    return run(M, N, K, A, trans_a != 0, B, trans_b != 0, C, alpha, epilogue, config, splits, workspace,
+               workspace_bytes, stream);
 }
 
 gemm_f16_status_t gemm_f16_split(int64_t M, int64_t N, int64_t K, const void *A, int trans_a, const void *B,
@@ -567,7 +587,7 @@ gemm_f16_status_t gemm_f16_split(int64_t M, int64_t N, int64_t K, const void *A,
 {
     if ((trans_a != 0 && trans_a != 1) || (trans_b != 0 && trans_b != 1))
         return GEMM_F16_ERROR_INVALID_VALUE;
-    return run(M, N, K, A, trans_a != 0, B, trans_b != 0, C, epilogue, config, splits, workspace,
+    return run(M, N, K, A, trans_a != 0, B, trans_b != 0, C, 1.0f, epilogue, config, splits, workspace,
                workspace_bytes, stream);
 }
 
@@ -598,7 +618,7 @@ gemm_f16_status_t gemm_f16_split_static(int64_t M, int64_t N, int64_t K, const v
         if (static_scratch(&scratch) != hipSuccess)
             return GEMM_F16_ERROR_RUNTIME;
     }
-    return run(M, N, K, A, trans_a != 0, B, trans_b != 0, C, epilogue, config, splits, scratch,
+    return run(M, N, K, A, trans_a != 0, B, trans_b != 0, C, 1.0f, epilogue, config, splits, scratch,
                scratch ? kStaticScratchBytes : 0, stream);
 }
 
@@ -696,6 +716,7 @@ gemm_f16_status_t gemm_f16_sp(int64_t M, int64_t N, int64_t K, const void *vals,
     a.tiles_n = (int)plan.tiles_n;
     a.group_m = GEMM_F16_GROUP_M;
     a.relu = epilogue == GEMM_F16_EPILOGUE_RELU ? 1 : 0;
+    a.alpha = 1.0f;
     a.vec_c = 1;
     a.k_split = (int)K;
     a.W = nullptr;

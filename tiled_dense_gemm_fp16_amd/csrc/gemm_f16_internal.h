@@ -18,7 +18,8 @@ struct KernelArgs {
     int M, N, K;
     int tiles_m, tiles_n;
     int group_m;         // tile rows walked together by the tile remap
-    int relu;            // 1: max(acc, 0) before the fp16 conversion
+    int relu;            // 1: max(alpha acc, 0) before the fp16 conversion
+    float alpha;         // the result block is scaled by alpha first (1: the plain product)
     int vec_c;           // 8: 16-byte stores of C are aligned (LDS-staged write-back);
                          // 4: 8-byte stores; 1: 2-byte stores
     int k_split;         // K elements per workgroup (a multiple of the tile depth); >= K unless split
@@ -74,11 +75,11 @@ constexpr int64_t kStaticScratchBytes = (int64_t)32 << 20;
 constexpr int kMaxScratchDevices = 64;
 hipError_t static_scratch(void **ptr);
 
-// Split-K reduction: C = rne16(epi(W[0] + ... + W[splits-1])) over M x N
+// Split-K reduction: C = rne16(epi(alpha (W[0] + ... + W[splits-1]))) over M x N
 // elements (relu: 1 for the ReLU epilogue).  vec4: N % 4 == 0, C 8-byte and
 // W 16-byte aligned.
-hipError_t launch_reduce(const float *W, _Float16 *C, int64_t M, int64_t N, int splits, int relu, bool vec4,
-                         hipStream_t s);
+hipError_t launch_reduce(const float *W, _Float16 *C, int64_t M, int64_t N, int splits, float alpha, int relu,
+                         bool vec4, hipStream_t s);
 
 } // namespace gemm_f16_impl
 

@@ -38,7 +38,7 @@ hipError_t static_scratch(void **ptr)
 }
 
 // ---- split-K reduction ---------------------------------------------------------
-// C = rne16(epi(sum over s of W[s])) elementwise, the splits added in index
+// C = rne16(epi(alpha * sum over s of W[s])) elementwise, the splits added in index
 // order in fp32 (so the result does not depend on scheduling).  W holds
 // `splits` slices of M x N fp32 one after another, C is M x N fp16, both
 // with row pitch N: the flattened index e addresses the same element in
@@ -47,7 +47,7 @@ hipError_t static_scratch(void **ptr)
 // moved per output element.
 template <bool VEC4>
 __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float *__restrict__ W, half_t *__restrict__ C,
-                                                            int64_t mn, int splits, int relu)
+                                                            int64_t mn, int splits, float alpha, int relu)
 {
     const int64_t stride = (int64_t)gridDim.x * 256;
     if constexpr (VEC4) {
@@ -61,6 +61,10 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float *__restr
                 acc[2] += v[2];
                 acc[3] += v[3];
             }
+            acc[0] *= alpha;
+            acc[1] *= alpha;
+            acc[2] *= alpha;
+            acc[3] *= alpha;
             if (relu) {
                 acc[0] = __builtin_fmaxf(acc[0], 0.0f);
                 acc[1] = __builtin_fmaxf(acc[1], 0.0f);
@@ -75,6 +79,7 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float *__restr
             float acc = W[e];
             for (int s = 1; s < splits; ++s)
                 acc += W[s * mn + e];
+            acc *= alpha;
             if (relu)
                 acc = __builtin_fmaxf(acc, 0.0f);
             C[e] = (half_t)acc;
@@ -82,8 +87,8 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float *__restr
     }
 }
 
-hipError_t launch_reduce(const float *W, _Float16 *C, int64_t M, int64_t N, int splits, int relu, bool vec4,
-                         hipStream_t s)
+hipError_t launch_reduce(const float *W, _Float16 *C, int64_t M, int64_t N, int splits, float alpha, int relu,
+                         bool vec4, hipStream_t s)
 {
     const int64_t mn = M * N;
     const int64_t items = vec4 ? mn / 4 : mn;
@@ -91,10 +96,10 @@ hipError_t launch_reduce(const float *W, _Float16 *C, int64_t M, int64_t N, int 
     const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((items + 255) / 256, 256 * 16));
     if (vec4)
         hipLaunchKernelGGL(splitk_reduce_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, s, W, C, mn, splits,
-                           relu);
+                           alpha, relu);
     else
         hipLaunchKernelGGL(splitk_reduce_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, s, W, C, mn,
-                           splits, relu);
+                           splits, alpha, relu);
     return hipGetLastError();
 }
 

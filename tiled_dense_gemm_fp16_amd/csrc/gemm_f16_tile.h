@@ -896,6 +896,7 @@ gemm_f16_kernel(KernelArgs args)
         half_t *c_base = args.C + (int64_t)m0 * N;
         const __amdgpu_buffer_rsrc_t c_rsrc = make_rsrc(c_base, (uint32_t)c_rows * (uint32_t)N * 2u);
         const bool relu = args.relu != 0;
+        const float alpha = args.alpha;
 #pragma unroll
         for (int i = 0; i < T::TM; ++i)
 #pragma unroll
@@ -905,7 +906,7 @@ gemm_f16_kernel(KernelArgs args)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const int r = wm0 + 32 * i + 8 * (v / 4) + 4 * (lane >> 5) + (v % 4);
-                    float x = acc[i][j][v];
+                    float x = acc[i][j][v] * alpha;
                     if (relu)
                         x = __builtin_fmaxf(x, 0.0f);
                     const half_t h = (half_t)x;
@@ -952,15 +953,17 @@ gemm_f16_kernel(KernelArgs args)
         return;
     }
 
-    // ---- epilogue: optional ReLU, RNE to fp16, store ----
+    // ---- epilogue: scale, optional ReLU, RNE to fp16, store ----
     half_t *c_base = args.C + (int64_t)m0 * N;
     const __amdgpu_buffer_rsrc_t c_rsrc = make_rsrc(c_base, (uint32_t)c_rows * (uint32_t)N * 2u);
     const bool relu = args.relu != 0;
+    const float alpha = args.alpha;
     const int vec_c = args.vec_c;
-    // The four values of block (i, j), group g, as fp16 after the epilogue.
+    // The four values of block (i, j), group g, as fp16 after the epilogue
+    // (alpha = 1 leaves the sums unchanged: x * 1 is exact).
     auto out4 = [&](int i, int j, int g, half_t &h0, half_t &h1, half_t &h2, half_t &h3) {
-        float v0 = acc[i][j][4 * g + 0], v1 = acc[i][j][4 * g + 1];
-        float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
+        float v0 = acc[i][j][4 * g + 0] * alpha, v1 = acc[i][j][4 * g + 1] * alpha;
+        float v2 = acc[i][j][4 * g + 2] * alpha, v3 = acc[i][j][4 * g + 3] * alpha;
         if (relu) {
             v0 = __builtin_fmaxf(v0, 0.0f);
             v1 = __builtin_fmaxf(v1, 0.0f);
