@@ -283,7 +283,8 @@ typedef struct gemm_f16_plan {
     int32_t vec_c;         /* binary16 elements per store of C */
     int64_t tiles_m;       /* ceil(M / bM) */
     int64_t tiles_n;       /* ceil(N / bN) */
-    int64_t grid;          /* workgroups launched (tiles_m * tiles_n * splits) */
+    int64_t grid;          /* workgroups launched: tiles_m * tiles_n * splits, or for a
+                              persistent configuration min(tiles_m * tiles_n, 256 CUs) */
     int64_t k_tiles;       /* K-loop trip count of one workgroup: ceil(k_split / bK) */
     int64_t lds_bytes;     /* LDS per workgroup */
     double flops;          /* 2 M N K: the algorithmic work of the call */

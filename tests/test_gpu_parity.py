@@ -396,3 +396,42 @@ def test_scaled_score_block_shape():
     torch.cuda.synchronize()
     res = oracle.compare(u16(got), oracle.gemm(u16(a), u16(b), scale=oracle.as_binary32(alpha)))
     assert res["pass"], res
+
+
+def persistent_config():
+    names = [g.config_name(c) for c in range(g.num_configs())]
+    return [c for c, n in enumerate(names) if n.endswith("_persistent")]
+
+
+@pytest.mark.parametrize("ta,tb", [(False, False), (False, True), (True, False), (True, True)])
+def test_persistent_loop_many_tiles(ta, tb):
+    """The persistent tile loop with more tiles than CUs (17 x 18 = 306
+    tiles of 256 x 256 on 256 workgroups, so some run two tiles), ragged M
+    and N and a K tail (K = 200: four slices, the last 8 deep), against the
+    oracle; with ReLU and a scale too."""
+    M, N, K = 4304, 4400, 200
+    a, b, a_st, b_st = stored_operands(M, N, K, ta, tb, 70 + 2 * ta + tb)
+    ad, bd = a_st.to(DEV), b_st.to(DEV)
+    for c in persistent_config():
+        p = g.plan(M, N, K, ad.data_ptr(), bd.data_ptr(), 1 << 20, config=c, trans_a=ta, trans_b=tb)
+        assert p["grid"] == 256 and p["tiles_m"] * p["tiles_n"] == 306
+        for epilogue, alpha in (("none", 1.0), ("relu", 0.375)):
+            print(f"[persistent] ta={int(ta)} tb={int(tb)} config={c} epi={epilogue} alpha={alpha}", flush=True)
+            ref = oracle.gemm(u16(a), u16(b), relu=(epilogue == "relu"), scale=alpha)
+            got = g.gemm(ad, bd, epilogue=epilogue, config=c, trans_a=ta, trans_b=tb, alpha=alpha, splits=1)
+            torch.cuda.synchronize()
+            res = oracle.compare(u16(got), ref)
+            assert res["pass"], (ta, tb, c, epilogue, res)
+
+
+def test_persistent_loop_matches_one_tile_kernel():
+    """Same tile, same MFMA order: the persistent loop and the one-tile
+    kernel give identical bits on the 8192^3 workload."""
+    w = workloads.WORKLOADS["gemm_8192"]
+    a, b = workloads.make_inputs(w)
+    ad, bd = a.to(DEV), b.to(DEV)
+    one = g.gemm(ad, bd, config=g.plan(8192, 8192, 8192, 1 << 20, 1 << 20, 1 << 20)["config"], splits=1)
+    for c in persistent_config():
+        loop = g.gemm(ad, bd, config=c, splits=1)
+        torch.cuda.synchronize()
+        assert torch.equal(one, loop)

@@ -30,6 +30,7 @@ const ConfigDesc kConfigs[kNumConfigs] = {
     {"256x256x64_s2_direct_m16", 256, 256, 64, 2, 4, true, 8, 8, kAllLayouts, 1},
     {"256x256x64_s2_direct_m16_a4", 256, 256, 64, 2, 4, true, 2, 8, kNN | kNT, 1},
     {"256x256x32_s4_direct_m16", 256, 256, 32, 4, 4, true, 8, 8, kAllLayouts, 1},
+    {"256x256x64_s2_direct_m16_persistent", 256, 256, 64, 2, 4, true, 8, 8, kAllLayouts, 1, true},
 };
 
 // Sparse configurations (2:4 A): fields as above; every one takes A as
@@ -104,6 +105,7 @@ double config_efficiency(int c)
     case 8: return 1.06;    // 256x256x64 direct, 4 waves, 16x16x32 MFMAs
     case 9: return 0.95;    // the same with 4-byte loads of A (A rows 4-byte aligned)
     case 10: return 1.05;   // 256x256x32 direct, 4 stages, 16x16x32 MFMAs
+    case 11: return 1.07;   // 256x256x64 16x16x32 tile, persistent over the tiles
     case 5: return 1.00;    // 256x256x64 direct, 8 waves
     case 0: return 0.97;    // 256x256x64 direct, 4 waves
     case 1: return 0.90;    // 256x128x64 direct
@@ -114,6 +116,17 @@ double config_efficiency(int c)
     case 4: return 0.25;    // 64x64x64 register-staged, any alignment
     default: return 0.0;
     }
+}
+
+// Shape conditions beyond layout and alignment: the persistent tile loop
+// needs an even number (>= 2) of k slices, no split, and 8-byte stores of C
+// (vc >= 4: N % 4 == 0 and C 8-byte aligned).
+bool shape_fits(int c, int64_t K, int vc, int splits)
+{
+    if (!kConfigs[c].persistent)
+        return true;
+    const int64_t nk = ceil_div(K, kConfigs[c].block_k);
+    return nk >= 2 && nk % 2 == 0 && vc >= 4 && splits <= 1;
 }
 
 bool config_fits(int c, int va, int vb, bool ta, bool tb)
@@ -179,7 +192,8 @@ void fill_plan(int c, int64_t M, int64_t N, int64_t K, int va, int vb, int vc, b
     p->vec_c = vc;
     p->tiles_m = ceil_div(M, d.block_m);
     p->tiles_n = ceil_div(N, d.block_n);
-    p->grid = p->tiles_m * p->tiles_n * sp.splits;
+    p->grid = d.persistent ? std::min<int64_t>(p->tiles_m * p->tiles_n, kComputeUnits)
+                           : p->tiles_m * p->tiles_n * sp.splits;
     p->k_tiles = ceil_div(sp.splits > 1 ? sp.k_split : K, d.block_k);
     p->lds_bytes = gemm_f16_stage_bytes(d.block_m, d.block_n, d.block_k, d.stages);
     p->flops = 2.0 * (double)M * (double)N * (double)K;
@@ -295,16 +309,23 @@ Split model_split(int c, int64_t M, int64_t N, int64_t K, int requested, double 
     return best;
 }
 
+// The one-workgroup-per-tile configuration that computes the same tile as
+// persistent configuration c (for shapes the persistent loop does not take).
+int one_tile_twin(int c) { return kConfigs[c].persistent ? 8 : c; }
+
 // Configuration (and split) with the lowest modelled time.
-int choose_config(int64_t M, int64_t N, int64_t K, int va, int vb, bool ta, bool tb, int requested, Split *split)
+int choose_config(int64_t M, int64_t N, int64_t K, int va, int vb, int vc, bool ta, bool tb, int requested,
+                  Split *split)
 {
     int best = -1;
     double best_t = 0.0;
     for (int c = 0; c < kNumConfigs; ++c) {
         if (!config_fits(c, va, vb, ta, tb) || config_efficiency(c) <= 0.0)
             continue;
+        if (kConfigs[c].persistent && (requested > 1 || !shape_fits(c, K, vc, 1)))
+            continue;
         double t;
-        const Split sp = model_split(c, M, N, K, requested, &t);
+        const Split sp = model_split(c, M, N, K, kConfigs[c].persistent ? 1 : requested, &t);
         if (best < 0 || t < best_t * 0.999) {
             best = c;
             best_t = t;
@@ -346,12 +367,15 @@ gemm_f16_status_t make_plan(int64_t M, int64_t N, int64_t K, const void *A, bool
                 sp = {1, K};
             }
         } else {
-            c = choose_config(M, N, K, va, vb, ta, tb, splits, &sp);
+            c = choose_config(M, N, K, va, vb, vc, ta, tb, splits, &sp);
         }
+        // a table entry may name the persistent loop for a nearby shape it does not take
+        if (c >= 0 && !shape_fits(c, K, vc, sp.splits))
+            c = one_tile_twin(c);
     } else if (config_fits(c, va, vb, ta, tb)) {
-        sp = model_split(c, M, N, K, splits, nullptr);
+        sp = model_split(c, M, N, K, kConfigs[c].persistent ? 1 : splits, nullptr);
     }
-    if (c < 0 || !config_fits(c, va, vb, ta, tb))
+    if (c < 0 || !config_fits(c, va, vb, ta, tb) || !shape_fits(c, K, vc, sp.splits))
         return GEMM_F16_ERROR_INVALID_VALUE;
     if (sp.splits > 1 && !split_addressable(kConfigs[c], N))
         return GEMM_F16_ERROR_UNSUPPORTED_SIZE;

@@ -38,9 +38,10 @@ struct ConfigDesc {
     int min_vec_b;        // ... of B loads
     int layouts;          // layouts compiled, bit 2 trans_a + trans_b: 1 = A . B only, 15 = all four
     int occupancy;        // workgroups resident per CU (LDS and register limits)
+    bool persistent;      // one resident workgroup per CU loops over the tiles
 };
 
-constexpr int kNumConfigs = 11;
+constexpr int kNumConfigs = 12;
 extern const ConfigDesc kConfigs[kNumConfigs];
 
 // Launch configuration `config` with `grid` workgroups on `s`.

@@ -82,6 +82,10 @@
 #ifndef GEMM_F16_M16_VMEM_EVERY
 #define GEMM_F16_M16_VMEM_EVERY 2
 #endif
+// parts the 16x16x32 tile's loads of a slice are issued in (one per k step)
+#ifndef GEMM_F16_M16_SPREAD
+#define GEMM_F16_M16_SPREAD 2
+#endif
 
 namespace gemm_f16_impl {
 
@@ -320,6 +324,7 @@ struct Operand {
     const half_t *X;       // the stored matrix
     int ld;                // its row pitch (elements)
     int mn0;               // first m (A) or n (B) of the workgroup's tile
+    int mn_total;          // M (A) or N (B)
     int K;                 // end of the workgroup's k range
     int kbase;             // start of the workgroup's k range (split-K), a multiple of BK
     __amdgpu_buffer_rsrc_t panel;   // ROWS_K: the workgroup's BMN rows
@@ -333,18 +338,15 @@ struct Operand {
     int ldsv[VEC_DIV];
     typename VecT<V>::type reg[VEC_DIV];
 
-    __device__ __forceinline__ void init(const half_t *x, int ld_, int mn0_, int mn_total, int k_begin, int k_end,
+    __device__ __forceinline__ void init(const half_t *x, int ld_, int mn0_, int mn_total_, int k_begin, int k_end,
                                          int tid, int wave, int lane)
     {
         X = x;
         ld = ld_;
-        mn0 = mn0_;
         K = k_end;
         kbase = k_begin;
-        if constexpr (ROWS_K) {
-            const int rows = min(BMN, mn_total - mn0);
-            panel = make_rsrc(X + (int64_t)mn0 * ld, (uint32_t)rows * (uint32_t)ld * 2u);
-        }
+        mn_total = mn_total_;
+        set_tile(mn0_);
         if constexpr (DIRECT) {
             const int byte = wave * WAVE_BYTES + lane * WB;
             const int r = byte / (ROW * 2);
@@ -352,7 +354,9 @@ struct Operand {
             const int sub = (byte % 16) / 2;                // element inside it (4-byte pieces)
             const int c = (pos ^ swz(r)) * 8 + sub;
             kcol0 = c;
-            off0 = ((uint32_t)r * (uint32_t)ld + (uint32_t)(ROWS_K ? c : mn0 + c)) * 2u;
+            // (an mn-rows operand's tile origin mn0 is in its slice's base
+            // address, so these offsets do not depend on the tile)
+            off0 = ((uint32_t)r * (uint32_t)ld + (uint32_t)c) * 2u;
             step = (uint32_t)ROW_STEP * (uint32_t)ld * 2u;
             if constexpr (ALT_COLUMN) {
                 // row r + ROW_STEP flips one bit of the row's XOR: the chunk moves
@@ -379,6 +383,19 @@ struct Operand {
         }
     }
 
+    // Point the operand at the tile whose m (A) or n (B) range starts at
+    // mn0_: the k-rows operand's panel of at most BMN rows (rows past the
+    // matrix read as zero); an mn-rows operand keeps mn0 for its slices'
+    // base address.
+    __device__ __forceinline__ void set_tile(int mn0_)
+    {
+        mn0 = mn0_;
+        if constexpr (ROWS_K) {
+            const int rows = min(BMN, mn_total - mn0);
+            panel = make_rsrc(X + (int64_t)mn0 * ld, (uint32_t)rows * (uint32_t)ld * 2u);
+        }
+    }
+
     // Start the loads of k slice kt of the workgroup's range: into LDS at dst
     // (direct) or into the registers (staged).  kt past the last slice is
     // allowed and reads zeros.  Direct loads may be issued in `nparts` parts
@@ -391,6 +408,13 @@ struct Operand {
         if constexpr (ROWS_K) {
             rs = panel;
             shift = (uint32_t)k0 * 2u;
+        } else if constexpr (DIRECT) {
+            // the slice's rows from column mn0 on: rows past K read as zero;
+            // uniform by construction, readfirstlane keeps it in SGPRs
+            const int rows = __builtin_amdgcn_readfirstlane(max(0, min(BK, K - k0)));
+            const int m = __builtin_amdgcn_readfirstlane(mn0);
+            rs = make_rsrc(X + (int64_t)k0 * ld + m,
+                           rows > 0 ? (uint32_t)rows * (uint32_t)ld * 2u - (uint32_t)m * 2u : 0u);
         } else {
             // uniform by construction; readfirstlane keeps the descriptor in SGPRs
             const int rows = __builtin_amdgcn_readfirstlane(max(0, min(BK, K - k0)));
@@ -1059,6 +1083,249 @@ gemm_f16_kernel(KernelArgs args)
     }
 }
 
+// ---- persistent tile loop -------------------------------------------------------
+// The 256x256x64 tile of 16x16x32 MFMAs (4 waves of 128x128, two LDS stages)
+// run by one resident workgroup per CU over a sequence of output tiles.
+// Against one workgroup per tile it removes, per tile after a workgroup's
+// first: the launch of a new workgroup, the pipeline fill (the next tile's
+// first k slice is loaded while the current tile's last slice is
+// multiplied) and the accumulator clearing (a tile's first MFMAs take a zero
+// accumulator input).  The result leaves straight from the accumulators as
+// 8-byte stores of four consecutive columns, so that the LDS stages stay
+// free for the next tile's slices; those stores drain while the next tile's
+// first slice is multiplied.
+// Tile order: workgroups are handed to the 8 XCDs round-robin; XCD x owns a
+// contiguous range of the grouped tile order (as in tile_coords) and its
+// workgroups take that range's tiles in turn, so in every round the tiles
+// running on one XCD are neighbours, as with one workgroup per tile.
+// Requirements (checked by the planner): an even number of k slices (at
+// least 2), no split, N % 4 == 0 and C 8-byte aligned.
+// PLAIN: alpha 1 and no ReLU (the store path converts and stores only).
+template <int VA, bool A_ROWS_K, bool B_ROWS_K, bool PLAIN>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+gemm_f16_persistent_kernel(KernelArgs args)
+{
+    constexpr int BM = 256, BN = 256, BK = 64, WM = 2, WN = 2, STAGES = 2, PARTS = 2;
+    using T = Tile<BM, BN, BK, WM, WN, STAGES, true, VA, 8, A_ROWS_K, B_ROWS_K, false, true>;
+    static_assert(T::KSTEP == 32 && BK / T::KSTEP == 2, "two 32-deep k steps per slice");
+    __shared__ __attribute__((aligned(1024))) half_t lds[T::LDS_BYTES / 2];
+    half_t *const As = lds;                                  // two A stages
+    half_t *const Bs = lds + STAGES * T::A_STAGE;            // two B stages
+
+    const int M = args.M, N = args.N, K = args.K;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm0 = (wave / WN) * T::WTM;
+    const int wn0 = (wave % WN) * T::WTN;
+    const int nk = (K + BK - 1) / BK;
+
+    // this workgroup's tiles: positions local, local + wgs, ... of its XCD's range
+    constexpr int kXcds = 8;
+    const int P = (int)gridDim.x;
+    const int tiles = args.tiles_m * args.tiles_n;
+    const int xcd = (int)blockIdx.x % kXcds, local = (int)blockIdx.x / kXcds;
+    const int wgs = P / kXcds + (xcd < P % kXcds ? 1 : 0);
+    const int per = tiles / kXcds, rem = tiles % kXcds;
+    const int first = xcd * per + min(xcd, rem);
+    const int count = per + (xcd < rem ? 1 : 0);
+    auto coords = [&](int id, int &m0_, int &n0_) {
+        const int width = args.group_m * args.tiles_n;
+        const int group = id / width;
+        const int first_m = group * args.group_m;
+        const int gm = min(args.tiles_m - first_m, args.group_m);
+        const int in_group = id - group * width;
+        m0_ = (first_m + in_group % gm) * BM;
+        n0_ = (in_group / gm) * BN;
+    };
+    int tl = local;
+    if (tl >= count)
+        return;
+    int m0, n0;
+    coords(first + tl, m0, n0);
+
+    typename T::OpA opa;
+    typename T::OpB opb;
+    opa.init(args.A, A_ROWS_K ? K : M, m0, M, 0, K, tid, wave, lane);
+    opb.init(args.B, B_ROWS_K ? K : N, n0, N, 0, K, tid, wave, lane);
+
+    float4v acc[T::TM][T::TN];
+    struct Frags {
+        half8 x[T::TN];
+        half8 y[T::TM];
+    };
+    Frags f0, f1;
+    auto load_frags = [&](Frags &f, const half_t *as, const half_t *bs, int ks) {
+#pragma unroll
+        for (int i = 0; i < T::TM; ++i)
+            f.y[i] = opa.frag16(as, wm0 + 16 * i, ks, lane);
+#pragma unroll
+        for (int j = 0; j < T::TN; ++j)
+            f.x[j] = opb.frag16(bs, wn0 + 16 * j, ks, lane);
+    };
+    // ZERO: the tile's first k step, on a zero accumulator input
+    auto mma = [&](const Frags &f, auto zero_c) {
+#pragma unroll
+        for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+            for (int jj = 0; jj < T::TN; ++jj) {
+#if GEMM_F16_SNAKE
+                const int j = (i & 1) ? T::TN - 1 - jj : jj;
+#else
+                const int j = jj;
+#endif
+                if constexpr (decltype(zero_c)::value)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(f.x[j], f.y[i], float4v{}, 0, 0, 0);
+                else
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(f.x[j], f.y[i], acc[i][j], 0, 0, 0);
+            }
+    };
+    using Zero = std::integral_constant<bool, true>;
+    using Accumulate = std::integral_constant<bool, false>;
+    // k-step placement as in the one-tile kernel's 16x16x32 tile
+    constexpr int kMfmaPerStep = T::TM * T::TN;
+    constexpr int kReadsPerStep = (A_ROWS_K ? 1 : 2) * T::TM + (B_ROWS_K ? 1 : 2) * T::TN;
+    constexpr int kReadsPerMfma = GEMM_F16_M16_READS_PER_MFMA;
+    constexpr int kReadEvery = GEMM_F16_M16_READ_EVERY;
+    constexpr int kVmemEvery = GEMM_F16_M16_VMEM_EVERY;
+    static_assert(kMfmaPerStep / kReadEvery * kReadsPerMfma >= kReadsPerStep, "every read has a slot");
+    constexpr int PART_LOADS = (T::OpA::LOADS + T::OpB::LOADS) / PARTS;
+    auto interleave = [&](int n_vmem) {
+#pragma unroll
+        for (int i = 0; i < kMfmaPerStep; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // one MFMA
+#pragma unroll
+            for (int r = 0; r < kReadsPerMfma; ++r)
+                if (i % kReadEvery == 0 && (i / kReadEvery) * kReadsPerMfma + r < kReadsPerStep)
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+            if (i % kVmemEvery == 0 && i / kVmemEvery < n_vmem)
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);      // one global load
+        }
+    };
+    auto issue = [&](int kt, half_t *dst_a, half_t *dst_b, int part) __attribute__((always_inline)) {
+        opa.issue(kt, dst_a, wave, part, PARTS);
+        opb.issue(kt, dst_b, wave, part, PARTS);
+    };
+    // every wave's loads of the stage about to be read have landed (two
+    // stages: all of them), its reads of the stage about to be refilled are
+    // done, then the workgroup barrier
+    auto slice_ready = [&]() {
+        wait_vm_lgkm0<0>();
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // One k slice read from stage (rd_a, rd_b) while slice `req` of the
+    // operands' current tile is requested into (wr_a, wr_b), half with each
+    // k step.  FIRST: the tile's first slice (no earlier k step pending; its
+    // first step starts the accumulators from zero); otherwise f1 holds the
+    // previous slice's last step.
+    auto step = [&](auto first_c, const half_t *__restrict__ rd_a, const half_t *__restrict__ rd_b,
+                    half_t *__restrict__ wr_a, half_t *__restrict__ wr_b, int req) __attribute__((always_inline)) {
+        constexpr bool FIRST = decltype(first_c)::value;
+        issue(req, wr_a, wr_b, 0);
+        load_frags(f0, rd_a, rd_b, 0);
+        if constexpr (!FIRST)
+            mma(f1, Accumulate{});
+        interleave(PART_LOADS);
+        __builtin_amdgcn_sched_barrier(0);
+        issue(req, wr_a, wr_b, 1);
+        load_frags(f1, rd_a, rd_b, 1);
+        if constexpr (FIRST)
+            mma(f0, Zero{});
+        else
+            mma(f0, Accumulate{});
+        interleave(PART_LOADS);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    const bool relu = args.relu != 0;
+    const float alpha = args.alpha;
+    const uint32_t row_pitch = (uint32_t)N * 2u;
+    // Lane l holds, in block (i, j), columns 16 j + 4 (l / 16) .. +3 of row
+    // 16 i + l % 16 of its wave's sub-tile.  Each store's offset is a row
+    // part (range-checked against the tile's c_rows rows) plus a column part
+    // that carries the out-of-range bit for columns past N (N % 4 == 0: four
+    // columns are all inside or all outside).
+    auto store_tile = [&](int tm0, int tn0) {
+        const int c_rows = min(BM, M - tm0);
+        const __amdgpu_buffer_rsrc_t c_rsrc =
+            make_rsrc(args.C + (int64_t)tm0 * N, (uint32_t)c_rows * row_pitch);
+        uint32_t col[T::TN];
+#pragma unroll
+        for (int j = 0; j < T::TN; ++j) {
+            const int n = tn0 + wn0 + 16 * j + 4 * (lane >> 4);
+            col[j] = ((uint32_t)n * 2u) | oob_unless(n < N);
+        }
+#pragma unroll
+        for (int i = 0; i < T::TM; ++i) {
+            const uint32_t row = (uint32_t)(wm0 + 16 * i + (lane & 15)) * row_pitch;
+#pragma unroll
+            for (int j = 0; j < T::TN; ++j) {
+                float v0 = acc[i][j][0], v1 = acc[i][j][1], v2 = acc[i][j][2], v3 = acc[i][j][3];
+                if constexpr (!PLAIN) {
+                    v0 *= alpha;
+                    v1 *= alpha;
+                    v2 *= alpha;
+                    v3 *= alpha;
+                    if (relu) {
+                        v0 = __builtin_fmaxf(v0, 0.0f);
+                        v1 = __builtin_fmaxf(v1, 0.0f);
+                        v2 = __builtin_fmaxf(v2, 0.0f);
+                        v3 = __builtin_fmaxf(v3, 0.0f);
+                    }
+                }
+                // element conversions kept as scalars (see the one-tile epilogue)
+                const half_t h0 = (half_t)v0, h1 = (half_t)v1, h2 = (half_t)v2, h3 = (half_t)v3;
+                const half4 h = {h0, h1, h2, h3};
+                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(int2v, h), c_rsrc, row + col[j], 0, 0);
+            }
+        }
+    };
+    (void)relu;
+    (void)alpha;
+
+    half_t *const A0 = As, *const A1 = As + T::A_STAGE;
+    half_t *const B0 = Bs, *const B1 = Bs + T::B_STAGE;
+    // the first tile's slice 0 into stage 0 (every later tile's slice 0 is
+    // requested by its predecessor's last slice)
+    issue(0, A0, B0, 0);
+    issue(0, A0, B0, 1);
+    while (true) {
+        const int tl_next = tl + wgs;
+        const bool more = tl_next < count;
+        int m0n = m0, n0n = n0;
+        if (more)
+            coords(first + tl_next, m0n, n0n);
+        // slice 0 (stage 0), requesting slice 1 into stage 1
+        slice_ready();
+        step(Zero{}, A0, B0, A1, B1, 1);
+        // slices 1 .. nk-1 in pairs (nk even): stage 1 then stage 0
+        for (int kt = 1; kt < nk; kt += 2) {
+            int req = kt + 1;
+            if (req == nk && more) {
+                // the tile's last slice requests the next tile's first one
+                opa.set_tile(m0n);
+                opb.set_tile(n0n);
+                req = 0;
+            }
+            slice_ready();
+            step(Accumulate{}, A1, B1, A0, B0, req);
+            if (kt + 1 < nk) {
+                slice_ready();
+                step(Accumulate{}, A0, B0, A1, B1, kt + 2);
+            }
+        }
+        mma(f1, Accumulate{});       // the tile's last k step
+        store_tile(m0, n0);
+        if (!more)
+            break;
+        tl = tl_next;
+        m0 = m0n;
+        n0 = n0n;
+    }
+    wait_vmcnt<0>();   // the last request's zero-filling loads land before the workgroup retires
+}
+
 // ---- launchers ----------------------------------------------------------------
 
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool DIRECT, int VA, int VB, bool AR, bool BR,
@@ -1078,6 +1345,19 @@ static hipError_t launch_one(const KernelArgs &a, int64_t grid, hipStream_t stre
     }
     hipLaunchKernelGGL((gemm_f16_kernel<BM, BN, BK, WM, WN, STAGES, DIRECT, VA, VB, AR, BR, SPREAD, SPARSE, M16>),
                        dim3((unsigned)grid), dim3(64 * WM * WN), 0, stream, a);
+    return hipGetLastError();
+}
+
+// the persistent tile loop: `grid` resident workgroups (at most one per CU)
+template <int VA, bool AR, bool BR>
+static hipError_t launch_persistent(const KernelArgs &a, int64_t grid, hipStream_t stream)
+{
+    if (a.alpha == 1.0f && a.relu == 0)
+        hipLaunchKernelGGL((gemm_f16_persistent_kernel<VA, AR, BR, true>), dim3((unsigned)grid), dim3(256), 0,
+                           stream, a);
+    else
+        hipLaunchKernelGGL((gemm_f16_persistent_kernel<VA, AR, BR, false>), dim3((unsigned)grid), dim3(256), 0,
+                           stream, a);
     return hipGetLastError();
 }
 
@@ -1138,8 +1418,9 @@ hipError_t launch_transposed(int config, const KernelArgs &a, int va, int vb, in
     case 4: return launch_staged_8or1<64, 64, 64, 2, 2, 2, AR, BR>(a, va, vb, grid, s);
     case 5: return launch_one<256, 256, 64, 2, 4, 2, true, 8, 8, AR, BR, 2>(a, grid, s);
     case 6: return launch_staged_wide<256, 256, 64, 2, 4, 2, AR, BR>(a, va, vb, grid, s);
-    case 8: return launch_one<256, 256, 64, 2, 2, 2, true, 8, 8, AR, BR, 2, false, true>(a, grid, s);
+    case 8: return launch_one<256, 256, 64, 2, 2, 2, true, 8, 8, AR, BR, GEMM_F16_M16_SPREAD, false, true>(a, grid, s);
     case 10: return launch_one<256, 256, 32, 2, 2, 4, true, 8, 8, AR, BR, 1, false, true>(a, grid, s);
+    case 11: return launch_persistent<8, AR, BR>(a, grid, s);
     case 9:
         // A stored M x K with 4-byte direct loads: B given N x K (NT) only
         if constexpr (AR)
