@@ -741,7 +741,7 @@ gemm_f16_status_t gemm_f16_sp(int64_t M, int64_t N, int64_t K, const void *vals,
     a.group_m = GEMM_F16_GROUP_M;
     a.relu = epilogue == GEMM_F16_EPILOGUE_RELU ? 1 : 0;
     a.alpha = 1.0f;
-    a.vec_c = 1;
+    a.vec_c = (N % 8 == 0 && (uintptr_t)C % 16 == 0) ? 8 : 1;   // 8: the LDS-staged epilogue
     a.k_split = (int)K;
     a.W = nullptr;
     a.meta = (const uint16_t *)meta;

@@ -550,8 +550,6 @@ struct Tile {
     static constexpr int B_STAGE = OpB::STAGE;
     static constexpr int LDS_BYTES = STAGES * (A_STAGE + B_STAGE) * 2;
     static_assert(LDS_BYTES <= 163840, "LDS budget");
-    static constexpr int META_LOADS = SPARSE ? TM * (BK / 32) : 0;   // position words per lane per tile
-    static constexpr int LOADS_PER_TILE = OpA::LOADS + OpB::LOADS + META_LOADS;
 };
 
 // SPREAD (direct kernels): the loads of the tile requested during a step are
@@ -565,8 +563,12 @@ struct Tile {
 // fills the matrix-core registers: with one epilogue path the accumulator
 // does not have to be held in vector registers across a branch, where it
 // overflows them and spills to scratch.
+// WIDE_META (sparse, K % 64 == 0): the four position words of a 64-deep
+// slice of each fragment row arrive with one 8-byte load instead of two
+// 2-byte loads per k step.
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool DIRECT, int VA, int VB, bool A_ROWS_K,
-          bool B_ROWS_K, int SPREAD = 1, bool SPARSE = false, bool M16 = false, bool STAGED_ONLY = false>
+          bool B_ROWS_K, int SPREAD = 1, bool SPARSE = false, bool M16 = false, bool STAGED_ONLY = false,
+          bool WIDE_META = false>
 __global__ void __launch_bounds__(64 * WM * WN)
 __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4)))
 gemm_f16_kernel(KernelArgs args)
@@ -610,7 +612,14 @@ gemm_f16_kernel(KernelArgs args)
     // tile cover its words too) into slot kt % STAGES.
     constexpr int NSTEP = BK / T::KSTEP;
     constexpr int MSLOTS = SPARSE ? STAGES : 1;
-    uint32_t meta[MSLOTS][T::TM][SPARSE ? NSTEP : 1];
+    static_assert(!WIDE_META || (SPARSE && NSTEP == 2), "wide position loads: two 32-deep steps per slice");
+    // vector memory loads of one tile per lane: the operands' and sparse A's
+    // position words (one per fragment row, or one per row and k step)
+    constexpr int kMetaLoads = SPARSE ? (WIDE_META ? T::TM : T::TM * NSTEP) : 0;
+    constexpr int kLoadsPerTile = T::OpA::LOADS + T::OpB::LOADS + kMetaLoads;
+    uint32_t meta[MSLOTS][T::TM][SPARSE && !WIDE_META ? NSTEP : 1];
+    int2v metaw[WIDE_META ? MSLOTS : 1][WIDE_META ? T::TM : 1];
+    const uint32_t mshift = 16u * (uint32_t)(lane >> 5);   // wide: the lane's word in each dword
     const int kwords = K / 16;
     const __amdgpu_buffer_rsrc_t meta_rsrc =
         make_rsrc(SPARSE ? args.meta + (int64_t)m0 * kwords : args.meta,
@@ -619,10 +628,20 @@ gemm_f16_kernel(KernelArgs args)
     if constexpr (SPARSE) {
 #pragma unroll
         for (int i = 0; i < T::TM; ++i)
-            meta_off[i] = ((uint32_t)(wm0 + 32 * i + (lane & 31)) * (uint32_t)kwords + (uint32_t)(lane >> 5)) * 2u;
+            meta_off[i] = ((uint32_t)(wm0 + 32 * i + (lane & 31)) * (uint32_t)kwords +
+                           (WIDE_META ? 0u : (uint32_t)(lane >> 5))) * 2u;
     }
     auto issue_meta = [&](int kt, int slot) {
-        if constexpr (SPARSE) {
+        if constexpr (WIDE_META) {
+            // words k0/16 .. +3 of the row: 8 bytes, 8-byte aligned (K % 64 == 0);
+            // a slice past K reads zeros
+            const int w = (k_begin + kt * BK) / 16;
+            const uint32_t mask = oob_unless(w < kwords);
+#pragma unroll
+            for (int i = 0; i < T::TM; ++i)
+                metaw[slot][i] = __builtin_bit_cast(
+                    int2v, __builtin_amdgcn_raw_buffer_load_b64(meta_rsrc, (meta_off[i] + (uint32_t)w * 2u) | mask, 0, 0));
+        } else if constexpr (SPARSE) {
 #pragma unroll
             for (int ks = 0; ks < NSTEP; ++ks) {
                 const int w = (k_begin + kt * BK) / 16 + 2 * ks;
@@ -691,7 +710,13 @@ gemm_f16_kernel(KernelArgs args)
                 f.x[j] = opb.frag(bs, wn0 + 32 * j, ks, lane);
             }
         }
-        if constexpr (SPARSE) {
+        if constexpr (WIDE_META) {
+            // step ks uses word 2 ks + lane / 32: the low 16 bits of dword ks
+            // shifted by the lane's half (the instruction reads the low half)
+#pragma unroll
+            for (int i = 0; i < T::TM; ++i)
+                f.idx[i] = (uint32_t)metaw[mslot][i][ks] >> mshift;
+        } else if constexpr (SPARSE) {
 #pragma unroll
             for (int i = 0; i < T::TM; ++i)
                 f.idx[i] = meta[mslot][i][ks];
@@ -777,7 +802,7 @@ gemm_f16_kernel(KernelArgs args)
     // reads wait for those loads or writes.
     constexpr bool SPREAD_LOADS = DIRECT && SPREAD > 1;
     constexpr int PARTS = SPREAD_LOADS ? SPREAD : 1;
-    static_assert(PARTS <= NS && T::LOADS_PER_TILE % PARTS == 0, "whole parts, one per k step at most");
+    static_assert(PARTS <= NS && (T::OpA::LOADS + T::OpB::LOADS) % PARTS == 0, "whole parts, one per k step at most");
     // rd_slot / wr_slot: the stage indices of (rd_a, rd_b) and (wr_a, wr_b),
     // which are also the register slots of sparse A's position words
     auto step = [&](auto cur_c, const half_t *__restrict__ rd_a, const half_t *__restrict__ rd_b,
@@ -810,8 +835,8 @@ gemm_f16_kernel(KernelArgs args)
             if (pending)
                 mma(f0);
         }
-        constexpr int PART_LOADS = T::LOADS_PER_TILE / PARTS;
-        interleave(DIRECT ? PART_LOADS : 0, DIRECT ? 0 : T::LOADS_PER_TILE);
+        constexpr int PART_LOADS = kLoadsPerTile / PARTS;
+        interleave(DIRECT ? PART_LOADS : 0, DIRECT ? 0 : kLoadsPerTile);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int ks = 1; ks < NS; ++ks) {
@@ -834,7 +859,7 @@ gemm_f16_kernel(KernelArgs args)
     auto tile_ready = [&](int kt) {
         if constexpr (DIRECT) {
             if (kt + STAGES - 2 < nk)
-                wait_vm_lgkm0<(STAGES - 2) * T::LOADS_PER_TILE>();
+                wait_vm_lgkm0<(STAGES - 2) * kLoadsPerTile>();
             else
                 wait_vm_lgkm0<0>();
         } else {
@@ -912,6 +937,55 @@ gemm_f16_kernel(KernelArgs args)
     auto col_of = [&](int j, int g) {
         return M16 ? wn0 + 16 * j + 4 * (lane >> 4) : wn0 + 32 * j + 8 * g + 4 * (lane >> 5);
     };
+    if constexpr (SPARSE && STAGED_ONLY) {
+        // C = A . B was computed untransposed: lane l of block (i, j) holds
+        // column wn0 + 32 j + l % 32, rows wm0 + 32 i + 8 g + 4 (l / 32) + r
+        // in accumulator 4 g + r.  N % 8 == 0 and C 16-byte aligned: the fp16
+        // tile is staged through the (now idle) LDS, [BM][BN] with each
+        // row's 16-byte chunks XOR-ed by 4 when row bit 2 is set (the two
+        // half-waves of a write, rows 4 apart, then land in disjoint banks),
+        // and leaves as 16-byte pieces of whole rows.
+        static_assert(BM * BN * 2 <= T::LDS_BYTES, "the output tile fits in the LDS stages");
+        half_t *c_base = args.C + (int64_t)m0 * N;
+        const __amdgpu_buffer_rsrc_t c_rsrc = make_rsrc(c_base, (uint32_t)c_rows * (uint32_t)N * 2u);
+        const bool relu = args.relu != 0;
+        const float alpha = args.alpha;
+        auto swz = [](int row) { return ((row >> 2) & 1) * 4; };
+        half_t *ct = lds;
+        wait_vmcnt<0>();
+        wait_lgkm0();
+        __builtin_amdgcn_s_barrier();                       // every wave is done with the stages
+#pragma unroll
+        for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+            for (int j = 0; j < T::TN; ++j) {
+                const int c = wn0 + 32 * j + (lane & 31);
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int r = wm0 + 32 * i + 8 * (v / 4) + 4 * (lane >> 5) + (v % 4);
+                    float x = acc[i][j][v] * alpha;
+                    if (relu)
+                        x = __builtin_fmaxf(x, 0.0f);
+                    ct[r * BN + (((c >> 3) ^ swz(r)) << 3) + (c & 7)] = (half_t)x;
+                }
+            }
+        wait_lgkm0();
+        __builtin_amdgcn_s_barrier();
+        constexpr int CHUNKS_PER_ROW = BN / 8;
+        constexpr int PER_THREAD = BM * CHUNKS_PER_ROW / T::kThreads;
+        static_assert(BM * CHUNKS_PER_ROW % T::kThreads == 0, "output chunks split evenly");
+#pragma unroll
+        for (int q = 0; q < PER_THREAD; ++q) {
+            const int id = tid + q * T::kThreads;
+            const int r = id / CHUNKS_PER_ROW;
+            const int c8 = id % CHUNKS_PER_ROW;
+            const int4v v = *reinterpret_cast<const int4v *>(ct + r * BN + ((c8 ^ swz(r)) << 3));
+            const int n = n0 + 8 * c8;
+            const uint32_t off = ((uint32_t)r * (uint32_t)N + (uint32_t)n) * 2u;
+            __builtin_amdgcn_raw_buffer_store_b128(v, c_rsrc, off | oob_unless(n < N), 0, 0);
+        }
+        return;
+    }
     if constexpr (SPARSE) {
         // C = A . B was computed untransposed: lane l of block (i, j) holds
         // column wn0 + 32 j + l % 32, rows wm0 + 32 i + 8 g + 4 (l / 32) + r
@@ -1332,6 +1406,25 @@ template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool DIRECT, int V
           int SPREAD = 1, bool SPARSE = false, bool M16 = false>
 static hipError_t launch_one(const KernelArgs &a, int64_t grid, hipStream_t stream)
 {
+    if constexpr (SPARSE) {
+        // wide position loads when K % 64 == 0; the LDS-staged epilogue when
+        // N % 8 == 0 and C is 16-byte aligned
+        const bool wide = a.K % 64 == 0, staged = a.vec_c == 8;
+#define GEMM_F16_SP(ST, WIDE)                                                                                     \
+        hipLaunchKernelGGL(                                                                                      \
+            (gemm_f16_kernel<BM, BN, BK, WM, WN, STAGES, DIRECT, VA, VB, AR, BR, SPREAD, SPARSE, M16, ST, WIDE>), \
+            dim3((unsigned)grid), dim3(64 * WM * WN), 0, stream, a)
+        if (staged && wide)
+            GEMM_F16_SP(true, true);
+        else if (staged)
+            GEMM_F16_SP(true, false);
+        else if (wide)
+            GEMM_F16_SP(false, true);
+        else
+            GEMM_F16_SP(false, false);
+#undef GEMM_F16_SP
+        return hipGetLastError();
+    }
     // one wave per SIMD holding a 128x128 accumulator (256 registers): the
     // common unsplit, 16-byte-aligned case runs the staged-epilogue build
     constexpr bool FULL_ACC = !SPARSE && WM * WN == 4 && BM * BN == 256 * 256;
