@@ -104,8 +104,8 @@ double config_efficiency(int c)
     switch (c) {
     case 8: return 1.06;    // 256x256x64 direct, 4 waves, 16x16x32 MFMAs
     case 9: return 0.95;    // the same with 4-byte loads of A (A rows 4-byte aligned)
-    case 10: return 1.05;   // 256x256x32 direct, 4 stages, 16x16x32 MFMAs
-    case 11: return 1.07;   // 256x256x64 16x16x32 tile, persistent over the tiles
+    case 10: return 0.99;   // 256x256x32 direct, 4 stages, 16x16x32 MFMAs (ahead only for A given K x M)
+    case 11: return 1.05;   // 256x256x64 16x16x32 tile, persistent over the tiles (within 1 % of 8)
     case 5: return 1.00;    // 256x256x64 direct, 8 waves
     case 0: return 0.97;    // 256x256x64 direct, 4 waves
     case 1: return 0.90;    // 256x128x64 direct
@@ -258,7 +258,7 @@ const TunedEntry *tuned_entry(int64_t M, int64_t N, int64_t K, bool ta, bool tb,
 // through HBM (written 4 bytes, read 4 bytes per split and element) and a
 // second launch.
 constexpr double kCuFlops = 5.0e12;        // fp16 flop/s of one CU at efficiency 1 (about 1290 TF/s chip-wide)
-constexpr double kWgFixedTiles = 3.0;      // per-workgroup overhead in k-tile times
+constexpr double kWgFixedTiles = 3.0;      // per-workgroup overhead in times of a 64-deep k tile
 constexpr double kStreamBytes = 4.5e12;    // bytes/s of a streaming kernel
 constexpr double kLaunchSeconds = 3e-6;    // one more kernel on the stream
 constexpr int64_t kAutoWorkspaceMax = (int64_t)256 << 20;
@@ -271,7 +271,7 @@ double model_seconds(int c, int64_t M, int64_t N, int64_t K, const Split &sp)
     const double sharing = std::min((double)d.occupancy, ceil(units / kComputeUnits));
     const double kt = (double)ceil_div(sp.splits > 1 ? sp.k_split : K, d.block_k);
     const double t_kt = 2.0 * d.block_m * d.block_n * d.block_k * sharing / (kCuFlops * config_efficiency(c));
-    double t = rounds * (kt + kWgFixedTiles) * t_kt;
+    double t = rounds * (kt + kWgFixedTiles * 64.0 / d.block_k) * t_kt;
     if (sp.splits > 1)
         t += kLaunchSeconds + (8.0 * sp.splits + 2.0) * (double)M * (double)N / kStreamBytes;
     return t;
@@ -776,7 +776,11 @@ int64_t gemm_f16_stage_bytes(int64_t block_m, int64_t block_n, int64_t block_k, 
 
 const char *gemm_f16_status_string(gemm_f16_status_t status)
 {
-    switch (status) {
+    // read as an integer: C callers may pass any int, which need not be a
+    // value of the enumeration
+    int code;
+    memcpy(&code, &status, sizeof(code));
+    switch (code) {
     case GEMM_F16_SUCCESS: return "success";
     case GEMM_F16_ERROR_INVALID_VALUE: return "invalid value";
     case GEMM_F16_ERROR_MISALIGNED: return "pointer not aligned";

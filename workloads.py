@@ -14,7 +14,7 @@ rounded to binary16 by ``.to(torch.float16)``):
 * ``mlp``       -- activations A ~ N(0, 1), weights B ~ N(0, 1/sqrt(K)).
 
 The pages benchmark FP16 GEMM at unstated sizes; these five shapes (plus the
-one-GPU shard of the largest) stand in for them.  For the largest shapes the
+one-GPU shard of the largest, 8192 x 3584 x 8192) stand in for them.  For the largest shapes the
 oracle checks a 4096 x 4096 block at seeded random rows R and columns S:
 ``randperm(M)[:4096]`` then ``randperm(N)[:4096]`` from a generator seeded
 with ``seed + 1000``.
@@ -56,6 +56,9 @@ WORKLOADS = {
     "gemm_8192": Workload("gemm_8192", 8192, 8192, 8192, "mlp", 4, sampled=True),
     "gemm_mlp_8192x28672x8192": Workload("gemm_mlp_8192x28672x8192", 8192, 28672, 8192, "mlp", 4,
                                          sampled=True),
+    # one GPU's column block of the MLP projection when it is split over 8 GPUs along N
+    "gemm_mlp_shard_8192x3584x8192": Workload("gemm_mlp_shard_8192x3584x8192", 8192, 3584, 8192, "mlp", 4,
+                                              sampled=True),
 }
 
 SAMPLE = 4096
