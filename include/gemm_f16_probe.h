@@ -49,6 +49,27 @@ extern "C" {
 int gemm_f16_probe_mfma(int mode, int iters, int64_t blocks, const void *operands, void *out,
                         void *stream, double *flops);
 
+/*
+ * Lane-layout probe: one wave of 64 lanes runs one matrix instruction with a
+ * zero accumulator on operands given per lane, and writes every lane's
+ * accumulators, so that tests can check the operand and result layouts the
+ * GEMM kernels are written against.
+ *   instr : GEMM_F16_PROBE_LAYOUT_* below.
+ *   src0  : 64 x 8 binary16, lane l's first operand (for the sparse
+ *           instruction: its 8 kept values).
+ *   src1  : lane l's second operand, 64 x 8 binary16 (64 x 16 for the sparse
+ *           instruction).
+ *   index : 64 int32, lane l's position word (sparse instruction only; may
+ *           be NULL otherwise).
+ *   out   : 64 x 16 floats (32x32 results) or 64 x 4 (16x16), lane-major.
+ * Returns 0 on success, 1 for bad arguments, 2 if the launch failed.
+ */
+#define GEMM_F16_PROBE_LAYOUT_32X32X16 0         /* v_mfma_f32_32x32x16_f16 */
+#define GEMM_F16_PROBE_LAYOUT_16X16X32 1         /* v_mfma_f32_16x16x32_f16 */
+#define GEMM_F16_PROBE_LAYOUT_SMFMAC_32X32X32 2  /* v_smfmac_f32_32x32x32_f16 */
+int gemm_f16_probe_mfma_layout(int instr, const void *src0, const void *src1, const void *index, void *out,
+                               void *stream);
+
 #ifdef __cplusplus
 }
 #endif

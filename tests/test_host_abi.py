@@ -46,7 +46,7 @@ def test_probe_library_exports_its_header():
     text = open(os.path.join(ROOT, "include", "gemm_f16_probe.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = sorted(set(re.findall(r"\b(gemm_f16_probe\w*)\s*\(", text)))
-    assert names == ["gemm_f16_probe_mfma"]
+    assert names == ["gemm_f16_probe_mfma", "gemm_f16_probe_mfma_layout"]
     lib = ctypes.CDLL(g.PROBE_LIB_PATH)
     for name in names:
         assert hasattr(lib, name)
@@ -54,6 +54,8 @@ def test_probe_library_exports_its_header():
     # argument checks happen before any launch
     assert g.probe_lib().gemm_f16_probe_mfma(7, 1, 1, None, FAKE, None, None) == 1
     assert g.probe_lib().gemm_f16_probe_mfma(0, 1, 0, None, FAKE, None, None) == 1
+    assert g.probe_lib().gemm_f16_probe_mfma_layout(3, FAKE, FAKE, FAKE, FAKE, None) == 1
+    assert g.probe_lib().gemm_f16_probe_mfma_layout(2, FAKE, FAKE, None, FAKE, None) == 1
 
 
 def test_status_strings():

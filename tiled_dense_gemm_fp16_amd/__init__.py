@@ -329,10 +329,12 @@ def gemm_sp(vals, meta, b, epilogue: str = "none", out=None, config: int = CONFI
 # ---- measurement probe (libgemm_f16_probe.so, include/gemm_f16_probe.h) ----
 
 PROBE_CONSTANT, PROBE_RANDOM_FIXED, PROBE_RANDOM_CHANGING = 0, 1, 2
+PROBE_LAYOUT_32X32X16, PROBE_LAYOUT_16X16X32, PROBE_LAYOUT_SMFMAC_32X32X32 = 0, 1, 2
 PROBE_MFMA16 = 3          # added to a kind: the 16x16x32 instruction
 PROBE_OPERAND_VECTORS = 1024
 PROBE_SIGNATURES = {
     "gemm_f16_probe_mfma": ([_int, _int, _i64, _vp, _vp, _vp, ctypes.POINTER(ctypes.c_double)], _int),
+    "gemm_f16_probe_mfma_layout": ([_int, _vp, _vp, _vp, _vp, _vp], _int),
 }
 _probe = None
 

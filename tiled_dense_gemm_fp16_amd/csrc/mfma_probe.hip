@@ -190,3 +190,64 @@ extern "C" int gemm_f16_probe_mfma(int mode, int iters, int64_t blocks, const vo
         *flops = (double)blocks * 4.0 /* waves */ * (double)iters * 32.0 /* MFMAs */ * 32768.0;
     return 0;
 }
+
+// ---- lane-layout probe ---------------------------------------------------------
+// One wave runs one MFMA on operands the caller lays out per lane and writes
+// back every lane's accumulators, so that a test can check the lane layouts
+// the GEMM kernels rely on (and that subnormal binary16 inputs are kept).
+namespace {
+
+typedef _Float16 half16v __attribute__((ext_vector_type(16)));
+
+template <int INSTR>
+__global__ void __launch_bounds__(64) mfma_layout_kernel(const half8 *__restrict__ src0,
+                                                         const _Float16 *__restrict__ src1,
+                                                         const int *__restrict__ index, float *__restrict__ out)
+{
+    const int lane = threadIdx.x;
+    const half8 a = src0[lane];
+    if constexpr (INSTR == GEMM_F16_PROBE_LAYOUT_32X32X16) {
+        const half8 b = reinterpret_cast<const half8 *>(src1)[lane];
+        const float16v d = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, float16v{}, 0, 0, 0);
+        for (int e = 0; e < 16; ++e)
+            out[lane * 16 + e] = d[e];
+    } else if constexpr (INSTR == GEMM_F16_PROBE_LAYOUT_16X16X32) {
+        const half8 b = reinterpret_cast<const half8 *>(src1)[lane];
+        const float4v d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, float4v{}, 0, 0, 0);
+        for (int e = 0; e < 4; ++e)
+            out[lane * 4 + e] = d[e];
+    } else {
+        const half16v b = reinterpret_cast<const half16v *>(src1)[lane];
+        const float16v d = __builtin_amdgcn_smfmac_f32_32x32x32_f16(a, b, float16v{}, index[lane], 0, 0);
+        for (int e = 0; e < 16; ++e)
+            out[lane * 16 + e] = d[e];
+    }
+}
+
+}  // namespace
+
+extern "C" int gemm_f16_probe_mfma_layout(int instr, const void *src0, const void *src1, const void *index,
+                                          void *out, void *stream)
+{
+    if (!src0 || !src1 || !out || (instr == GEMM_F16_PROBE_LAYOUT_SMFMAC_32X32X32 && !index))
+        return 1;
+    hipStream_t s = (hipStream_t)stream;
+    const half8 *a = (const half8 *)src0;
+    const _Float16 *b = (const _Float16 *)src1;
+    const int *idx = (const int *)index;
+    float *o = (float *)out;
+    switch (instr) {
+    case GEMM_F16_PROBE_LAYOUT_32X32X16:
+        hipLaunchKernelGGL(mfma_layout_kernel<GEMM_F16_PROBE_LAYOUT_32X32X16>, dim3(1), dim3(64), 0, s, a, b, idx, o);
+        break;
+    case GEMM_F16_PROBE_LAYOUT_16X16X32:
+        hipLaunchKernelGGL(mfma_layout_kernel<GEMM_F16_PROBE_LAYOUT_16X16X32>, dim3(1), dim3(64), 0, s, a, b, idx, o);
+        break;
+    case GEMM_F16_PROBE_LAYOUT_SMFMAC_32X32X32:
+        hipLaunchKernelGGL(mfma_layout_kernel<GEMM_F16_PROBE_LAYOUT_SMFMAC_32X32X32>, dim3(1), dim3(64), 0, s, a, b,
+                           idx, o);
+        break;
+    default: return 1;
+    }
+    return hipGetLastError() == hipSuccess ? 0 : 2;
+}
