@@ -165,7 +165,8 @@ gemm_f16_status_t gemm_f16_trans(int64_t M, int64_t N, int64_t K,
  *                     count is rounded down so that no split is empty and
  *                     every split spans whole K tiles (gemm_f16_plan_split
  *                     reports the count used; 1 means one kernel and no
- *                     workspace).
+ *                     workspace).  The persistent configuration takes no
+ *                     split: a count above 1 with it is INVALID_VALUE.
  *   workspace       : a caller-owned device buffer of workspace_bytes
  *                     bytes, 16-byte aligned, overlapping none of A, B, C,
  *                     and at least the plan's workspace_bytes long.  NULL

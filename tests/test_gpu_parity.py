@@ -63,7 +63,12 @@ def test_every_config_aligned_shapes(shape):
     M, N, K = shape
     a, b = workloads.draw(M, N, K, "uniform", M + N + K)
     cfgs = configs_for(M, N, K)
-    assert len(cfgs) == g.num_configs()
+    # every tile configuration takes an aligned shape; the persistent loop
+    # only an even number (at least two) of 64-deep k tiles
+    k_tiles = -(-K // 64)
+    want = [c for c in range(g.num_configs())
+            if "persistent" not in g.config_name(c) or (k_tiles >= 2 and k_tiles % 2 == 0)]
+    assert cfgs == want
     for c in cfgs:
         check(a, b, config=c, label=f"config {g.config_name(c)}")
 
@@ -169,7 +174,8 @@ def test_empty_k_every_config():
     a = torch.empty(M, 0, dtype=torch.float16, device=DEV)
     b = torch.empty(0, N, dtype=torch.float16, device=DEV)
     cfgs = configs_for(M, N, 0)
-    assert len(cfgs) == g.num_configs()
+    # the persistent loop takes no empty K (its planner runs the one-tile twin)
+    assert cfgs == [c for c in range(g.num_configs()) if "persistent" not in g.config_name(c)]
     for cfg in cfgs:
         for epi in ("none", "relu"):
             print(f"[parity] empty K config={cfg} epi={epi}", flush=True)

@@ -29,8 +29,12 @@ def u16(t: torch.Tensor) -> np.ndarray:
 
 
 def configs_for(M, N, K, ta=False, tb=False):
+    """Every configuration with a split form (all but the persistent loop)
+    that accepts this shape."""
     out = []
     for c in range(g.num_configs()):
+        if "persistent" in g.config_name(c):
+            continue
         try:
             g.plan(M, N, K, FAKE, FAKE, FAKE, config=c, trans_a=ta, trans_b=tb)
             out.append(c)

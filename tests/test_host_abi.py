@@ -437,3 +437,15 @@ def test_sparse_argument_checks_before_any_launch():
     for c in range(g.sp_num_configs()):
         q = g.plan_sp(300, 264, 1008, FAKE, FAKE, FAKE, FAKE, config=c)
         assert q["config"] == c and q["grid"] == q["tiles_m"] * q["tiles_n"]
+
+
+def test_persistent_config_takes_no_split():
+    """The persistent tile loop has no split form: an explicit count above 1
+    is refused, SPLITS_AUTO and 1 plan one kernel of at most 256 workgroups."""
+    c = [i for i in range(g.num_configs()) if g.config_name(i).endswith("_persistent")]
+    assert len(c) == 1
+    for sp in (None, 1):
+        p = g.plan(4096, 4096, 4096, FAKE, FAKE, FAKE, config=c[0], **({} if sp is None else {"splits": sp}))
+        assert p["splits"] == 1 and p["workspace_bytes"] == 0 and p["grid"] == 256
+    with pytest.raises(g.GemmError):
+        g.plan(4096, 4096, 4096, FAKE, FAKE, FAKE, config=c[0], splits=2)

@@ -31,6 +31,9 @@ const ConfigDesc kConfigs[kNumConfigs] = {
     {"256x256x64_s2_direct_m16_a4", 256, 256, 64, 2, 4, true, 2, 8, kNN | kNT, 1},
     {"256x256x32_s4_direct_m16", 256, 256, 32, 4, 4, true, 8, 8, kAllLayouts, 1},
     {"256x256x64_s2_direct_m16_persistent", 256, 256, 64, 2, 4, true, 8, 8, kAllLayouts, 1, true},
+    {"64x64x64_s4_direct", 64, 64, 64, 4, 4, true, 8, 8, kAllLayouts, 2},
+    {"128x128x64_s4_direct_m16", 128, 128, 64, 4, 4, true, 8, 8, kAllLayouts, 1},
+    {"128x64x64_s4_direct", 128, 64, 64, 4, 4, true, 8, 8, kAllLayouts, 1},
 };
 
 // Sparse configurations (2:4 A): fields as above; every one takes A as
@@ -106,6 +109,9 @@ double config_efficiency(int c)
     case 9: return 0.95;    // the same with 4-byte loads of A (A rows 4-byte aligned)
     case 10: return 0.99;   // 256x256x32 direct, 4 stages, 16x16x32 MFMAs (ahead only for A given K x M)
     case 11: return 1.05;   // 256x256x64 16x16x32 tile, persistent over the tiles (within 1 % of 8)
+    case 12: return 0.30;   // 64x64x64 direct, 4 stages (latency-bound; many small tiles)
+    case 13: return 0.82;   // 128x128x64 direct, 4 stages, 16x16x32 MFMAs
+    case 14: return 0.60;   // 128x64x64 direct, 4 stages
     case 5: return 1.00;    // 256x256x64 direct, 8 waves
     case 0: return 0.97;    // 256x256x64 direct, 4 waves
     case 1: return 0.90;    // 256x128x64 direct
@@ -373,6 +379,8 @@ gemm_f16_status_t make_plan(int64_t M, int64_t N, int64_t K, const void *A, bool
         if (c >= 0 && !shape_fits(c, K, vc, sp.splits))
             c = one_tile_twin(c);
     } else if (config_fits(c, va, vb, ta, tb)) {
+        if (kConfigs[c].persistent && splits > 1)
+            return GEMM_F16_ERROR_INVALID_VALUE;   // the persistent loop has no split form
         sp = model_split(c, M, N, K, kConfigs[c].persistent ? 1 : splits, nullptr);
     }
     if (c < 0 || !config_fits(c, va, vb, ta, tb) || !shape_fits(c, K, vc, sp.splits))

@@ -41,7 +41,7 @@ struct ConfigDesc {
     bool persistent;      // one resident workgroup per CU loops over the tiles
 };
 
-constexpr int kNumConfigs = 12;
+constexpr int kNumConfigs = 15;
 extern const ConfigDesc kConfigs[kNumConfigs];
 
 // Launch configuration `config` with `grid` workgroups on `s`.

@@ -20,6 +20,9 @@ hipError_t launch_nn(int config, const KernelArgs &a, int va, int vb, int64_t gr
     case 9: return launch_one<256, 256, 64, 2, 2, 2, true, 2, 8, AR, BR, 2, false, true>(a, grid, s);
     case 10: return launch_one<256, 256, 32, 2, 2, 4, true, 8, 8, AR, BR, 1, false, true>(a, grid, s);
     case 11: return launch_persistent<8, AR, BR>(a, grid, s);
+    case 12: return launch_one<64, 64, 64, 2, 2, 4, true, 8, 8, AR, BR, 1>(a, grid, s);
+    case 13: return launch_one<128, 128, 64, 2, 2, 4, true, 8, 8, AR, BR, 1, false, true>(a, grid, s);
+    case 14: return launch_one<128, 64, 64, 2, 2, 4, true, 8, 8, AR, BR, 1>(a, grid, s);
     default: return hipErrorInvalidValue;
     }
 }

@@ -754,9 +754,13 @@ gemm_f16_kernel(KernelArgs args)
     // MFMAs, at the rate set by the placement switches above.
     // the 8-wave register-staged tile takes one read per MFMA (+2-3 % on the
     // 3000x5000x4100 workload it serves; the 4-wave staged 128x128 tile lost 5 %)
-    constexpr int kReadsPerMfma = M16 ? GEMM_F16_M16_READS_PER_MFMA
+    // (a small 16x16x32 wave tile has fewer MFMAs than reads per step: one
+    // MFMA then carries as many reads as it takes)
+    constexpr bool kM16Fits = kMfmaPerStep / GEMM_F16_M16_READ_EVERY * GEMM_F16_M16_READS_PER_MFMA >= kReadsPerStep;
+    constexpr int kReadsPerMfma = M16 ? (kM16Fits ? GEMM_F16_M16_READS_PER_MFMA
+                                                  : (kReadsPerStep + kMfmaPerStep - 1) / kMfmaPerStep)
                                       : (!DIRECT && T::kWaves == 8) ? 1 : GEMM_F16_READS_PER_MFMA;
-    constexpr int kReadEvery = M16 ? GEMM_F16_M16_READ_EVERY : GEMM_F16_READ_EVERY;
+    constexpr int kReadEvery = M16 ? (kM16Fits ? GEMM_F16_M16_READ_EVERY : 1) : GEMM_F16_READ_EVERY;
     static_assert(!M16 || kMfmaPerStep / kReadEvery * kReadsPerMfma >= kReadsPerStep, "every read has a slot");
     constexpr int kVmemEvery = M16 ? GEMM_F16_M16_VMEM_EVERY : GEMM_F16_VMEM_EVERY;
     auto interleave = [&](int n_vmem, int n_dswrite) {
@@ -1514,6 +1518,9 @@ hipError_t launch_transposed(int config, const KernelArgs &a, int va, int vb, in
     case 8: return launch_one<256, 256, 64, 2, 2, 2, true, 8, 8, AR, BR, GEMM_F16_M16_SPREAD, false, true>(a, grid, s);
     case 10: return launch_one<256, 256, 32, 2, 2, 4, true, 8, 8, AR, BR, 1, false, true>(a, grid, s);
     case 11: return launch_persistent<8, AR, BR>(a, grid, s);
+    case 12: return launch_one<64, 64, 64, 2, 2, 4, true, 8, 8, AR, BR, 1>(a, grid, s);
+    case 13: return launch_one<128, 128, 64, 2, 2, 4, true, 8, 8, AR, BR, 1, false, true>(a, grid, s);
+    case 14: return launch_one<128, 64, 64, 2, 2, 4, true, 8, 8, AR, BR, 1>(a, grid, s);
     case 9:
         // A stored M x K with 4-byte direct loads: B given N x K (NT) only
         if constexpr (AR)

@@ -5,9 +5,9 @@ autotuner, freezing the result per machine and power limit, and re-running
 the search on new hardware ("TileLang：比 Triton 低一层的 tile 语言",
 section "工程上的几个注意点"; "5分钟上手TileLang：GPU内核开发指南", section
 "避坑与调参").  This script is that search for this library: on a GPU it
-times every configuration that accepts each shape of a grid (three sizes per
-dimension, four layouts, aligned and misaligned pitches), unsplit and with
-K split 2 to 16 ways, and writes ``csrc/gemm_f16_tuned.inc``, a table the
+times every configuration that accepts each shape of a grid (four layouts,
+aligned and misaligned pitches), unsplit and, where the unsplit grid leaves
+CUs idle, with K split 2 to 16 ways, and writes ``csrc/gemm_f16_tuned.inc``, a table the
 host planner consults before its analytic model: per shape the fastest
 configuration and split count, and the fastest configuration unsplit (what
 a call without a workspace runs).  Measurements are logged by configuration
@@ -30,8 +30,15 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 OUT = os.path.join(HERE, "csrc", "gemm_f16_tuned.inc")
 
-SIZES_MN = [512, 2048, 8192]
-SIZES_K = [512, 2048, 8192]
+# shape grid per alignment class: aligned pitches (every configuration runs)
+# at 2x steps in M and N and 4x steps in K; the misaligned classes, which
+# only the register-staged configurations serve, on a coarser grid
+GRIDS = {
+    1: ([256, 512, 1024, 2048, 4096, 8192], [256, 1024, 4096, 8192]),
+    0: ([512, 2048, 8192], [512, 2048, 8192]),
+    2: ([512, 2048, 8192], [512, 2048, 8192]),
+}
+SPLIT_BELOW_TILES = 512       # K splits are timed only for grids under two workgroups per CU
 LAYOUTS = [(False, False), (False, True), (True, False), (True, True)]
 SPLITS = [1, 2, 4, 8, 16]
 WORKSPACE_MAX = 256 << 20     # the planner's limit for automatic splits
@@ -85,7 +92,7 @@ def _time(fn, flops, target_s=0.03):
     return flops / (ms * 1e-3) / 1e12
 
 
-def sweep(sizes_mn, sizes_k, layouts, log, classes=(1, 0, 2)):
+def sweep(layouts, log, classes=(1, 0, 2)):
     import torch
 
     import tiled_dense_gemm_fp16_amd as g
@@ -93,6 +100,7 @@ def sweep(sizes_mn, sizes_k, layouts, log, classes=(1, 0, 2)):
     rows = []
     ws = torch.empty(WORKSPACE_MAX // 4, dtype=torch.float32, device="cuda")   # every split's workspace
     for aligned in classes:
+        sizes_mn, sizes_k = GRIDS[aligned]
         for M in sizes_mn:
             for N in sizes_mn:
                 for K in sizes_k:
@@ -114,6 +122,10 @@ def sweep(sizes_mn, sizes_k, layouts, log, classes=(1, 0, 2)):
                                     p = g.plan(m, n, k, a.data_ptr(), b.data_ptr(), c.data_ptr(), config=cfg,
                                                trans_a=ta, trans_b=tb, splits=sp)
                                 except g.GemmError:
+                                    break
+                                if sp == 1:
+                                    unsplit_grid = p["grid"]
+                                elif unsplit_grid >= SPLIT_BELOW_TILES:
                                     break
                                 # a split must keep two k tiles and use a new count
                                 if sp > 1 and (p["splits"] != sp or p["k_tiles"] < 2
@@ -222,7 +234,7 @@ def main() -> int:
     codes = {"nn": (False, False), "nt": (False, True), "tn": (True, False), "tt": (True, True)}
     layouts = [codes[x] for x in args.layouts.split(",")]
     log = open(args.log, "w") if args.log else sys.stdout
-    rows = sweep(SIZES_MN, SIZES_K, layouts, log, tuple(int(x) for x in args.classes.split(",")))
+    rows = sweep(layouts, log, tuple(int(x) for x in args.classes.split(",")))
     dev = torch.cuda.get_device_properties(0)
     note = (f"swept {datetime.date.today().isoformat()} on {dev.name} "
             f"({getattr(dev, 'gcnArchName', '?')}, {dev.multi_processor_count} CUs)")
