@@ -449,3 +449,17 @@ def test_persistent_config_takes_no_split():
         assert p["splits"] == 1 and p["workspace_bytes"] == 0 and p["grid"] == 256
     with pytest.raises(g.GemmError):
         g.plan(4096, 4096, 4096, FAKE, FAKE, FAKE, config=c[0], splits=2)
+
+
+def test_library_binds_to_torchs_hip_runtime():
+    """Loaded through the binding, even before torch is imported, the library
+    uses the HIP runtime torch loaded: the process maps one libamdhip64."""
+    import subprocess
+    import sys
+    code = ("import tiled_dense_gemm_fp16_amd as g; g.lib(); g.probe_lib(); import torch; "
+            "maps = open('/proc/self/maps').read(); "
+            "print(len({l.split()[-1] for l in maps.splitlines() if 'libamdhip64' in l}))")
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300,
+                         cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    assert out.returncode == 0, out.stderr[-2000:]
+    assert out.stdout.strip().splitlines()[-1] == "1"

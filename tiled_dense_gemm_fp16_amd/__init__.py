@@ -81,10 +81,20 @@ class GemmError(RuntimeError):
         super().__init__(f"{what}: status {status} ({status_string(status)})")
 
 
+def _load_hip_runtime_first():
+    """torch ships its own copy of the HIP runtime (same soname as the
+    system's).  Loading it before the library makes the library bind to that
+    copy; loaded the other way round the process holds two runtimes, and the
+    library's, which does not own torch's streams and allocations, reports no
+    device."""
+    import torch  # noqa: F401
+
+
 def lib() -> ctypes.CDLL:
     """Load libgemm_f16.so (built in-tree by ``__graft_entry__.build()``)."""
     global _lib
     if _lib is None:
+        _load_hip_runtime_first()
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build the HIP library first "
                                "(python -c 'import __graft_entry__ as g; g.build()')")
@@ -342,6 +352,7 @@ _probe = None
 def probe_lib() -> ctypes.CDLL:
     global _probe
     if _probe is None:
+        _load_hip_runtime_first()
         if not os.path.exists(PROBE_LIB_PATH):
             raise RuntimeError(f"{PROBE_LIB_PATH} is missing: build the HIP library first")
         h = ctypes.CDLL(PROBE_LIB_PATH)
