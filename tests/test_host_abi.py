@@ -292,7 +292,7 @@ def test_workspace_free_entry_points_never_split():
     """gemm_f16, gemm_f16_ex and gemm_f16_trans take no workspace: their
     plans run one kernel over all of K even where gemm_f16_split would
     split (table hits and model choices alike)."""
-    for M, N, K in [(1024, 1024, 8192), (512, 512, 8192), (96, 96, 30000), (24, 24, 1 << 20), (512, 512, 2048)]:
+    for M, N, K in [(1024, 1024, 8192), (512, 512, 8192), (96, 96, 30000), (24, 24, 1 << 20), (512, 512, 4096)]:
         for ta, tb in [(False, False), (False, True), (True, False), (True, True)]:
             auto = g.plan(M, N, K, FAKE, FAKE, FAKE, trans_a=ta, trans_b=tb)
             assert auto["splits"] == 1 and auto["workspace_bytes"] == 0 and auto["k_split"] == K
