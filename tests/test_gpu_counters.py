@@ -33,7 +33,7 @@ for name in {names}:
     print("ran", name, flush=True)
 """
 
-NAMES = ["256x256x64_s2_direct", "256x256x64_s2_direct_m16", "256x256x64_s2_direct_m16_persistent"]
+NAMES = ["256x128x64_s3_direct_m16", "256x256x64_s2_direct_m16", "256x256x64_s2_direct_m16_persistent"]
 
 
 def test_mfma_op_counter_matches_2mnk():

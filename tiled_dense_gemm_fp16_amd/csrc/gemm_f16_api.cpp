@@ -19,7 +19,7 @@ namespace gemm_f16_impl {
 // (512 per lane per SIMD, VGPRs + AGPRs as the compiler reports them).
 constexpr int kNN = 1, kNT = 2, kAllLayouts = 15;   // masks over bit 2 trans_a + trans_b
 const ConfigDesc kConfigs[kNumConfigs] = {
-    {"256x256x64_s2_direct", 256, 256, 64, 2, 4, true, 8, 8, kAllLayouts, 1},
+    {"256x128x64_s3_direct_m16", 256, 128, 64, 3, 4, true, 8, 8, kAllLayouts, 1},
     {"256x128x64_s3_direct", 256, 128, 64, 3, 4, true, 8, 8, kAllLayouts, 1},
     {"128x128x64_s3_direct", 128, 128, 64, 3, 4, true, 8, 8, kAllLayouts, 1},
     {"128x128x32_s2_staged", 128, 128, 32, 2, 4, false, 1, 1, kAllLayouts, 2},
@@ -112,8 +112,9 @@ double config_efficiency(int c)
     case 12: return 0.30;   // 64x64x64 direct, 4 stages (latency-bound; many small tiles)
     case 13: return 0.82;   // 128x128x64 direct, 4 stages, 16x16x32 MFMAs
     case 14: return 0.60;   // 128x64x64 direct, 4 stages
+
     case 5: return 1.00;    // 256x256x64 direct, 8 waves
-    case 0: return 0.97;    // 256x256x64 direct, 4 waves
+    case 0: return 0.94;    // 256x128x64 direct, 3 stages, 16x16x32 MFMAs
     case 1: return 0.90;    // 256x128x64 direct
     case 6: return 0.85;    // 256x256x64 register-staged, 8 waves (vectors of 4 or 8)
     case 2: return 0.76;    // 128x128x64 direct

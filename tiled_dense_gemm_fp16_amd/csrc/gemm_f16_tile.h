@@ -1508,7 +1508,7 @@ hipError_t launch_transposed(int config, const KernelArgs &a, int va, int vb, in
                                     hipStream_t s)
 {
     switch (config) {
-    case 0: return launch_one<256, 256, 64, 2, 2, 2, true, 8, 8, AR, BR, 4>(a, grid, s);
+    case 0: return launch_one<256, 128, 64, 2, 2, 3, true, 8, 8, AR, BR, 1, false, true>(a, grid, s);
     case 1: return launch_one<256, 128, 64, 2, 2, 3, true, 8, 8, AR, BR, 4>(a, grid, s);
     case 2: return launch_one<128, 128, 64, 2, 2, 3, true, 8, 8, AR, BR, 4>(a, grid, s);
     case 3: return launch_staged_8or1<128, 128, 32, 2, 2, 2, AR, BR>(a, va, vb, grid, s);

@@ -169,24 +169,42 @@ def sweep(layouts, log, classes=(1, 0, 2)):
     return rows
 
 
-def choose(r, names):
+def narrow_configs(g):
+    """Names of the configurations whose loads stay narrower than 16 bytes on
+    16-byte-aligned operands (the fallbacks for misaligned pitches)."""
+    out = set()
+    for c in range(g.num_configs()):
+        try:
+            p = g.plan(4096, 4096, 4096, 1 << 20, 1 << 20, 1 << 20, config=c)
+        except g.GemmError:
+            continue
+        if p["vec_a"] < 8 or p["vec_b"] < 8:
+            out.add(g.config_name(c))
+    return out
+
+
+def choose(r, names, narrow=()):
     """(config, splits, TFLOP/s) of the fastest run and (config, TFLOP/s) of
     the fastest unsplit run of one sweep record, over the configurations in
     ``names`` (the library's current list); None if none of them ran.  Keys
-    re-timed in interleaved rounds take their re-timed medians."""
+    re-timed in interleaved rounds take their re-timed medians.  On aligned
+    shapes the ``narrow`` fallbacks are not chosen (a win there is a near-tie
+    with their 16-byte twin)."""
     index = {n: i for i, n in enumerate(names)}
-    vals = {k: v for k, v in {**r["tflops"], **(r.get("retimed") or {})}.items() if k.split(":")[0] in index}
+    skip = set(narrow) if r["aligned"] == 1 else set()
+    vals = {k: v for k, v in {**r["tflops"], **(r.get("retimed") or {})}.items()
+            if k.split(":")[0] in index and k.split(":")[0] not in skip}
     if not vals:
         return None
     retimed = {k: v for k, v in (r.get("retimed") or {}).items() if k in vals}
     best = max(retimed or vals, key=(retimed or vals).get)
     unsplit = {k: v for k, v in vals.items() if k.endswith(":1")}
-    best1 = max(unsplit, key=unsplit.get)
+    best1 = best if best.endswith(":1") else max(unsplit, key=unsplit.get)
     name, sp = best.split(":")
     return (index[name], int(sp), vals[best]), (index[best1.split(":")[0]], unsplit[best1])
 
 
-def write_table(rows, path, note, names):
+def write_table(rows, path, note, names, narrow=()):
     lines = [
         "// gemm_f16_tuned.inc -- measured configuration table, written by",
         "// tiled_dense_gemm_fp16_amd/tune.py; do not edit by hand.",
@@ -196,7 +214,7 @@ def write_table(rows, path, note, names):
         "// best configuration, K splits, its TFLOP/s, best configuration unsplit, its TFLOP/s",
     ]
     for r in rows:
-        picked = choose(r, names)
+        picked = choose(r, names, narrow)
         if picked is None:
             continue
         (cfg, sp, tf), (cfg1, tf1) = picked
@@ -223,7 +241,7 @@ def main() -> int:
     names = [g.config_name(c) for c in range(g.num_configs())]
     if args.from_log:
         rows = [json.loads(line) for path in args.from_log for line in open(path) if line.strip()]
-        write_table(rows, args.out, f"combined from {len(args.from_log)} sweep log(s)", names)
+        write_table(rows, args.out, f"combined from {len(args.from_log)} sweep log(s)", names, narrow_configs(g))
         print(f"wrote {args.out} ({len(rows)} shapes)", flush=True)
         return 0
     import torch
@@ -238,7 +256,7 @@ def main() -> int:
     dev = torch.cuda.get_device_properties(0)
     note = (f"swept {datetime.date.today().isoformat()} on {dev.name} "
             f"({getattr(dev, 'gcnArchName', '?')}, {dev.multi_processor_count} CUs)")
-    write_table(rows, args.out, note, names)
+    write_table(rows, args.out, note, names, narrow_configs(g))
     print(f"wrote {args.out} ({len(rows)} shapes)", flush=True)
     return 0
 
