@@ -234,10 +234,14 @@ gemm_f16_status_t gemm_f16_split_static(int64_t M, int64_t N, int64_t K,
  * library's format, matched to gfx950's v_smfmac_f32_32x32x32_f16:
  *   vals : M x K/2 binary16, row-major: in every aligned group of 4
  *          consecutive k of a row, the 2 kept values in position order.
- *   meta : M x K/16 uint16, row-major: word w of a row covers k = 16w ..
- *          16w+15; bits 2s+1..2s give the position (0..3) inside group
- *          4w + s/2 of kept value s (s = 0..7), i.e. vals[i][8w + s] sits at
- *          k = 16w + 4 (s/2) + position.
+ *   meta : M K/16 uint16 words.  Word w of row i covers k = 16w .. 16w+15;
+ *          bits 2s+1..2s give the position (0..3) inside group 4w + s/2 of
+ *          kept value s (s = 0..7), i.e. vals[i][8w + s] sits at
+ *          k = 16w + 4 (s/2) + position.  The words are stored by 64-deep
+ *          k slices, so that a slice's words of consecutive rows are
+ *          contiguous: with kw = K/16 and F = kw / 4 whole slices, word w of
+ *          row i is at index (w/4 * M + i) * 4 + w % 4 when w/4 < F, and at
+ *          F * M * 4 + i * (kw % 4) + w % 4 in the partial last slice.
  * K must be a multiple of 16.
  */
 
@@ -314,8 +318,8 @@ gemm_f16_status_t gemm_f16_plan_trans(int64_t M, int64_t N, int64_t K,
                                       const void *C, int config, gemm_f16_plan_t *plan);
 
 /* As gemm_f16_plan, for gemm_f16_sp (config indexes the sparse list; flops
- * counts the products of kept values, M N K; lds_bytes the compressed A and
- * the B stages). */
+ * counts the products of kept values, M N K; lds_bytes the compressed A, the
+ * B and the position-word stages). */
 gemm_f16_status_t gemm_f16_plan_sp(int64_t M, int64_t N, int64_t K, const void *vals, const void *meta,
                                    const void *B, int trans_b, const void *C, int config,
                                    gemm_f16_plan_t *plan);

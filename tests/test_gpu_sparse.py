@@ -14,6 +14,7 @@ import torch
 import oracle
 import tiled_dense_gemm_fp16_amd as g
 import workloads
+from sp_layout import meta_flat, meta_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -43,7 +44,7 @@ def test_compress_bit_exact(shape, ties):
     torch.cuda.synchronize()
     v_ref, m_ref = oracle.sp_compress(u16(a))
     assert np.array_equal(u16(vals), v_ref)
-    assert np.array_equal(u16(meta), m_ref)
+    assert np.array_equal(meta_rows(u16(meta), M, K), m_ref)
 
 
 def test_compress_unaligned_source():
@@ -56,7 +57,7 @@ def test_compress_unaligned_source():
     vals, meta = g.sp_compress(ad)
     torch.cuda.synchronize()
     v_ref, m_ref = oracle.sp_compress(u16(a))
-    assert np.array_equal(u16(vals), v_ref) and np.array_equal(u16(meta), m_ref)
+    assert np.array_equal(u16(vals), v_ref) and np.array_equal(meta_rows(u16(meta), M, K), m_ref)
 
 
 def check_sp(M, N, K, seed, config=g.CONFIG_AUTO, epilogue="none", trans_b=False):
@@ -99,7 +100,7 @@ def test_sparse_auto_and_relu(epilogue):
 
 def test_sparse_zero_k_and_empty():
     vals = torch.empty((70, 0), dtype=torch.float16, device=DEV)
-    meta = torch.empty((70, 0), dtype=torch.int16, device=DEV)
+    meta = torch.empty((0,), dtype=torch.int16, device=DEV)
     b = torch.empty((0, 96), dtype=torch.float16, device=DEV)
     c = torch.full((70, 96), 3.0, dtype=torch.float16, device=DEV)
     g.gemm_sp(vals, meta, b, out=c)
@@ -141,4 +142,20 @@ def test_sparse_large_sampled():
     got = u16(c)[np.ix_(rows, cols)]
     res = oracle.compare(got, ref)
     print(f"[sparse] 4096^3 sampled: {res}", flush=True)
+    assert res["pass"], res
+
+
+@pytest.mark.parametrize("shape", [(300, 264, 1008), (130, 72, 4096), (257, 520, 80)])
+def test_oracle_operands_through_the_library(shape):
+    """The oracle's own compression, put into the library's storage order,
+    multiplied by the library: the stored order the kernels read is the one
+    the header documents (whole and partial 64-deep slices)."""
+    M, N, K = shape
+    a, b = draw(M, N, K, 31 + M)
+    v_ref, m_ref = oracle.sp_compress(u16(a))
+    vals = torch.from_numpy(v_ref.view(np.int16).copy()).view(torch.float16).to(DEV)
+    meta = torch.from_numpy(meta_flat(m_ref).view(np.int16)).to(DEV)
+    c = g.gemm_sp(vals, meta, b.to(DEV))
+    torch.cuda.synchronize()
+    res = oracle.compare(u16(c), oracle.gemm_sp(v_ref, m_ref, u16(b)))
     assert res["pass"], res

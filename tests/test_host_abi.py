@@ -463,3 +463,19 @@ def test_library_binds_to_torchs_hip_runtime():
                          cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
     assert out.returncode == 0, out.stderr[-2000:]
     assert out.stdout.strip().splitlines()[-1] == "1"
+
+
+def test_sparse_position_word_order():
+    """The documented storage order of the position words is a permutation
+    of the M K/16 words that keeps each 64-deep slice's words of
+    consecutive rows contiguous."""
+    import numpy as np
+    from sp_layout import meta_flat, meta_index, meta_rows
+    for M, K in [(1, 16), (5, 64), (7, 80), (33, 1008), (64, 4096), (3, 48)]:
+        idx = meta_index(M, K)
+        assert np.array_equal(np.sort(idx.reshape(-1)), np.arange(M * K // 16))
+        for s in range(K // 64):
+            block = idx[:, 4 * s:4 * s + 4].reshape(-1)
+            assert np.array_equal(block, np.arange(block[0], block[0] + 4 * M))
+        rows = np.arange(M * K // 16, dtype=np.uint16).reshape(M, K // 16)
+        assert np.array_equal(meta_rows(meta_flat(rows), M, K), rows)

@@ -289,13 +289,14 @@ def _check_gpu_2d(t, name, dtype):
 
 def sp_compress(a, stream=None):
     """(vals, meta) for a (M x K float16 GPU tensor, K % 16 == 0): vals is
-    M x K/2 float16, meta M x K/16 int16 (the uint16 words' bits)."""
+    M x K/2 float16, meta the M K/16 uint16 position words (as int16 bits) in
+    the slice-major order include/gemm_f16.h gives, a 1-D tensor."""
     import torch
 
     _check_gpu_2d(a, "a", torch.float16)
     M, K = a.shape
     vals = torch.empty((M, K // 2), dtype=torch.float16, device=a.device)
-    meta = torch.empty((M, K // 16), dtype=torch.int16, device=a.device)
+    meta = torch.empty((M * (K // 16),), dtype=torch.int16, device=a.device)
     if stream is None:
         stream = torch.cuda.current_stream(a.device)
     with torch.cuda.device(a.device):
@@ -315,11 +316,13 @@ def gemm_sp(vals, meta, b, epilogue: str = "none", out=None, config: int = CONFI
     if epilogue not in _EPILOGUES:
         raise ValueError(f"epilogue must be one of {sorted(_EPILOGUES)}, got {epilogue!r}")
     _check_gpu_2d(vals, "vals", torch.float16)
-    _check_gpu_2d(meta, "meta", torch.int16)
+    if (not isinstance(meta, torch.Tensor) or meta.dtype != torch.int16 or meta.dim() != 1 or not meta.is_cuda
+            or not meta.is_contiguous()):
+        raise ValueError("meta must be a 1-D contiguous int16 GPU tensor (as sp_compress returns)")
     _check_gpu_2d(b, "b", torch.float16)
     M, K = vals.shape[0], 2 * vals.shape[1]
     kb, N = (b.shape[1], b.shape[0]) if trans_b else (b.shape[0], b.shape[1])
-    if tuple(meta.shape) != (M, K // 16) or kb != K:
+    if meta.numel() != M * (K // 16) or kb != K:
         raise ValueError(f"shape mismatch: vals {tuple(vals.shape)}, meta {tuple(meta.shape)}, b {tuple(b.shape)}")
     if out is None:
         out = torch.empty((M, N), dtype=torch.float16, device=b.device)

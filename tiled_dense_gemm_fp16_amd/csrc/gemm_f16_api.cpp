@@ -557,9 +557,10 @@ gemm_f16_status_t make_plan_sp(int64_t M, int64_t N, int64_t K, int config, gemm
     p->tiles_n = ceil_div(N, d.block_n);
     p->grid = p->tiles_m * p->tiles_n;
     p->k_tiles = ceil_div(K, d.block_k);
-    // LDS: the compressed A tile (bK/2 columns) and the B tile per stage
+    // LDS: the compressed A tile (bK/2 columns), the B tile and A's position
+    // words (two dwords per row of a 64-deep slice) per stage
     p->lds_bytes = gemm_f16_stage_bytes(d.block_m, 0, d.block_k / 2, d.stages) +
-                   gemm_f16_stage_bytes(0, d.block_n, d.block_k, d.stages);
+                   gemm_f16_stage_bytes(0, d.block_n, d.block_k, d.stages) + (int64_t)d.stages * 8 * d.block_m;
     p->flops = (double)M * (double)N * (double)K;   // 2 M N (K/2): products of kept values
     p->min_bytes = (double)M * K + (double)M * K / 8 + 2.0 * ((double)K * N + (double)M * N);
     p->splits = 1;

@@ -9,11 +9,12 @@ namespace gemm_f16_impl {
 // each group of 4 it keeps the 2 entries of largest magnitude (compared as
 // binary16 bit patterns without the sign; ties: lower position), writes
 // them in position order to vals (M x K/2) and their positions, 2 bits per
-// kept value, to one word of meta (M x K/16).  VEC: A and vals 16-byte
-// aligned (16-byte loads and stores).
+// kept value, to one word of meta, stored slice-major (sp_meta_index).  VEC:
+// A and vals 16-byte aligned (16-byte loads and stores).
 template <bool VEC>
 __global__ void __launch_bounds__(256) sp_compress_kernel(const half_t *__restrict__ A, half_t *__restrict__ vals,
-                                                          unsigned short *__restrict__ meta, int64_t words)
+                                                          unsigned short *__restrict__ meta, int64_t words,
+                                                          int64_t M, int64_t kw)
 {
     const int64_t stride = (int64_t)gridDim.x * 256;
     for (int64_t w = (int64_t)blockIdx.x * 256 + threadIdx.x; w < words; w += stride) {
@@ -67,7 +68,7 @@ __global__ void __launch_bounds__(256) sp_compress_kernel(const half_t *__restri
             for (int e = 0; e < 8; ++e)
                 v[e] = kept[e];
         }
-        meta[w] = (unsigned short)word;
+        meta[sp_meta_index(w / kw, w % kw, M, kw)] = (unsigned short)word;
     }
 }
 
@@ -78,10 +79,10 @@ hipError_t launch_sp_compress(const _Float16 *A, _Float16 *vals, uint16_t *meta,
     const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((words + 255) / 256, 256 * 16));
     if (vec)
         hipLaunchKernelGGL(sp_compress_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, s, A, vals,
-                           (unsigned short *)meta, words);
+                           (unsigned short *)meta, words, M, K / 16);
     else
         hipLaunchKernelGGL(sp_compress_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, s, A, vals,
-                           (unsigned short *)meta, words);
+                           (unsigned short *)meta, words, M, K / 16);
     return hipGetLastError();
 }
 

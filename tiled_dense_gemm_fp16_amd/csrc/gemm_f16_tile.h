@@ -189,6 +189,18 @@ __device__ __forceinline__ int swz_b16(int row)
     return 4 * (row & 3) ^ 2 * ((row >> 3) & 1);
 }
 
+// ---- sparse A's position words ----------------------------------------------
+// Word g of row r (k = 16 g .. 16 g + 15; kw = K / 16 words per row) is
+// stored slice-major, so that the words of one 64-deep k slice of a block of
+// rows are contiguous: slice s = g / 4 of the kw / 4 whole slices holds the
+// M rows' 4 words each, [s][r][g % 4]; the kw % 4 words of a last, partial
+// slice follow, [r][g % 4].
+__host__ __device__ inline int64_t sp_meta_index(int64_t r, int64_t g, int64_t M, int64_t kw)
+{
+    const int64_t full = kw / 4, s = g / 4;
+    return s < full ? (s * M + r) * 4 + g % 4 : full * M * 4 + r * (kw % 4) + g % 4;
+}
+
 // ---- tile index remap -----------------------------------------------------
 // Workgroups are handed to the 8 XCDs round-robin (id % 8).  Give XCD x a
 // contiguous block of logical tile ids so its L2 sees neighbouring tiles, then
@@ -548,7 +560,10 @@ struct Tile {
     using OpB = Operand<B_ROWS_K, BN, BK, kThreads, DIRECT, VB, M16>;
     static constexpr int A_STAGE = OpA::STAGE;
     static constexpr int B_STAGE = OpB::STAGE;
-    static constexpr int LDS_BYTES = STAGES * (A_STAGE + B_STAGE) * 2;
+    // sparse A's position words of a 64-deep slice, per stage: two dwords
+    // per tile row, stored dword-major ([2][BM])
+    static constexpr int META_STAGE = SPARSE ? 2 * BM * 4 : 0;
+    static constexpr int LDS_BYTES = STAGES * ((A_STAGE + B_STAGE) * 2 + META_STAGE);
     static_assert(LDS_BYTES <= 163840, "LDS budget");
 };
 
@@ -564,8 +579,11 @@ struct Tile {
 // does not have to be held in vector registers across a branch, where it
 // overflows them and spills to scratch.
 // WIDE_META (sparse, K % 64 == 0): the four position words of a 64-deep
-// slice of each fragment row arrive with one 8-byte load instead of two
-// 2-byte loads per k step.
+// slice of every tile row travel to LDS with the slice's operands (4-byte
+// direct loads, two per row), and each fragment reads its words from there,
+// instead of 2-byte loads into registers per row and k step.  Loads into
+// registers would make the compiler wait for them with a count that also
+// covers later tiles' loads, draining the prefetch ring every slice.
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool DIRECT, int VA, int VB, bool A_ROWS_K,
           bool B_ROWS_K, int SPREAD = 1, bool SPARSE = false, bool M16 = false, bool STAGED_ONLY = false,
           bool WIDE_META = false>
@@ -577,6 +595,8 @@ gemm_f16_kernel(KernelArgs args)
     __shared__ __attribute__((aligned(1024))) half_t lds[T::LDS_BYTES / 2];
     half_t *const As = lds;                                  // STAGES A stages
     half_t *const Bs = lds + STAGES * T::A_STAGE;            // STAGES B stages
+    // sparse: STAGES position-word stages after the operand stages
+    uint32_t *const Ms = reinterpret_cast<uint32_t *>(lds + STAGES * (T::A_STAGE + T::B_STAGE));
 
     const int M = args.M, N = args.N, K = args.K;
     int tm, tn, split;
@@ -615,41 +635,55 @@ gemm_f16_kernel(KernelArgs args)
     static_assert(!WIDE_META || (SPARSE && NSTEP == 2), "wide position loads: two 32-deep steps per slice");
     // vector memory loads of one tile per lane: the operands' and sparse A's
     // position words (one per fragment row, or one per row and k step)
-    constexpr int kMetaLoads = SPARSE ? (WIDE_META ? T::TM : T::TM * NSTEP) : 0;
+    // wide: each thread moves META_DMA of the stage's 2 BM position dwords
+    constexpr int META_DMA = WIDE_META ? 2 * BM / T::kThreads : 1;
+    static_assert(!WIDE_META || (2 * BM) % T::kThreads == 0, "whole position loads per thread");
+    constexpr int kMetaLoads = SPARSE ? (WIDE_META ? META_DMA : T::TM * NSTEP) : 0;
     constexpr int kLoadsPerTile = T::OpA::LOADS + T::OpB::LOADS + kMetaLoads;
     uint32_t meta[MSLOTS][T::TM][SPARSE && !WIDE_META ? NSTEP : 1];
-    int2v metaw[WIDE_META ? MSLOTS : 1][WIDE_META ? T::TM : 1];
     const uint32_t mshift = 16u * (uint32_t)(lane >> 5);   // wide: the lane's word in each dword
+    static_assert(!SPARSE || BK == 64, "position words are stored by 64-deep slices");
     const int kwords = K / 16;
-    const __amdgpu_buffer_rsrc_t meta_rsrc =
-        make_rsrc(SPARSE ? args.meta + (int64_t)m0 * kwords : args.meta,
-                  SPARSE ? (uint32_t)min(BM, M - m0) * (uint32_t)kwords * 2u : 0u);
-    uint32_t meta_off[T::TM];
-    if constexpr (SPARSE) {
-#pragma unroll
-        for (int i = 0; i < T::TM; ++i)
-            meta_off[i] = ((uint32_t)(wm0 + 32 * i + (lane & 31)) * (uint32_t)kwords +
-                           (WIDE_META ? 0u : (uint32_t)(lane >> 5))) * 2u;
-    }
+    // the descriptor of slice s's words for this tile's rows (sp_meta_index):
+    // rows of `stride` words from `base`; rows past M, and slices past K,
+    // read zeros
+    auto meta_slice = [&](int s, int &stride) __attribute__((always_inline)) {
+        const int full = kwords / 4;
+        const uint32_t rows = (uint32_t)min(BM, M - m0);
+        if (s < full) {
+            stride = 4;
+            return make_rsrc(args.meta + ((int64_t)s * M + m0) * 4, rows * 8u);
+        }
+        stride = kwords % 4;
+        return make_rsrc(args.meta + (int64_t)full * M * 4 + (int64_t)m0 * stride,
+                         s == full ? rows * (uint32_t)stride * 2u : 0u);
+    };
     auto issue_meta = [&](int kt, int slot) {
         if constexpr (WIDE_META) {
-            // words k0/16 .. +3 of the row: 8 bytes, 8-byte aligned (K % 64 == 0);
-            // a slice past K reads zeros
-            const int w = (k_begin + kt * BK) / 16;
-            const uint32_t mask = oob_unless(w < kwords);
+            // the slice's words of the tile's rows are 8 BM contiguous bytes:
+            // thread load i moves dword q = (i waves + wave) 64 + lane of them
+            // to LDS dword q of the slot (row q / 2, words 2 (q % 2), +1)
+            int stride;
+            const __amdgpu_buffer_rsrc_t rs = meta_slice((k_begin + kt * BK) / 64, stride);
 #pragma unroll
-            for (int i = 0; i < T::TM; ++i)
-                metaw[slot][i] = __builtin_bit_cast(
-                    int2v, __builtin_amdgcn_raw_buffer_load_b64(meta_rsrc, (meta_off[i] + (uint32_t)w * 2u) | mask, 0, 0));
+            for (int i = 0; i < META_DMA; ++i) {
+                const int q0 = (i * T::kWaves + wave) * 64;
+                LDS_AS void *d = (LDS_AS void *)(Ms + slot * 2 * BM + q0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d, 4, (uint32_t)(q0 + lane) * 4u, 0, 0, 0);
+            }
         } else if constexpr (SPARSE) {
+            // word 2 ks + lane / 32 of the slice for each fragment row; past
+            // the row's words (a partial last slice) reads zero
+            int stride;
+            const __amdgpu_buffer_rsrc_t rs = meta_slice((k_begin + kt * BK) / 64, stride);
 #pragma unroll
             for (int ks = 0; ks < NSTEP; ++ks) {
-                const int w = (k_begin + kt * BK) / 16 + 2 * ks;
-                const uint32_t mask = oob_unless(w + (lane >> 5) < kwords);
+                const int j = 2 * ks + (lane >> 5);
+                const uint32_t mask = oob_unless(j < stride);
 #pragma unroll
                 for (int i = 0; i < T::TM; ++i)
                     meta[slot][i][ks] = (uint32_t)(unsigned short)__builtin_amdgcn_raw_buffer_load_b16(
-                        meta_rsrc, (meta_off[i] + (uint32_t)w * 2u) | mask, 0, 0);
+                        rs, ((uint32_t)((wm0 + 32 * i + (lane & 31)) * stride + j) * 2u) | mask, 0, 0);
             }
         } else {
             (void)kt;
@@ -711,11 +745,12 @@ gemm_f16_kernel(KernelArgs args)
             }
         }
         if constexpr (WIDE_META) {
-            // step ks uses word 2 ks + lane / 32: the low 16 bits of dword ks
-            // shifted by the lane's half (the instruction reads the low half)
+            // step ks uses word 2 ks + lane / 32 of the row: dword ks of the
+            // row shifted by the lane's half (the instruction reads the low half)
+            const uint32_t *ms = Ms + mslot * 2 * BM + 2 * (wm0 + (lane & 31)) + ks;
 #pragma unroll
             for (int i = 0; i < T::TM; ++i)
-                f.idx[i] = (uint32_t)metaw[mslot][i][ks] >> mshift;
+                f.idx[i] = ms[64 * i] >> mshift;
         } else if constexpr (SPARSE) {
 #pragma unroll
             for (int i = 0; i < T::TM; ++i)
@@ -749,7 +784,7 @@ gemm_f16_kernel(KernelArgs args)
     // LDS writes), so the matrix core keeps busy while those are in flight.
     constexpr int kMfmaPerStep = T::TM * T::TN;
     constexpr int kReadsPerStep = M16 ? (A_ROWS_K ? 1 : 2) * T::TM + (B_ROWS_K ? 1 : 2) * T::TN
-                                      : T::TM + (SPARSE ? 4 : 2) * T::TN;
+                                      : T::TM + (SPARSE ? 4 : 2) * T::TN + (WIDE_META ? T::TM : 0);
     // The next step's fragment reads are requested during the current step's
     // MFMAs, at the rate set by the placement switches above.
     // the 8-wave register-staged tile takes one read per MFMA (+2-3 % on the
