@@ -171,13 +171,15 @@ def traffic_from(directory: str, workload: str, config_name: str) -> int:
         return statistics.median(vals)
 
     def busy_fraction(kernel):
-        """Median over dispatches of the matrix cores' busy share, if the SQ pass is there."""
+        """Medians over dispatches of the matrix cores' busy share and of the
+        GPU's active cycles per XCD (GRBM_GUI_ACTIVE reads the sum over the 8
+        XCDs), if the SQ pass is there."""
         import csv
         import collections
 
         paths = glob.glob(os.path.join(directory, "sq", "**", "*counter_collection.csv"), recursive=True)
         if not paths:
-            return None
+            return None, None
         per = collections.defaultdict(lambda: collections.defaultdict(float))
         with open(paths[0]) as f:
             for r in csv.DictReader(f):
@@ -185,7 +187,8 @@ def traffic_from(directory: str, workload: str, config_name: str) -> int:
                     per[int(r["Dispatch_Id"])][r["Counter_Name"]] += float(r["Counter_Value"])
         fr = [d["SQ_VALU_MFMA_BUSY_CYCLES"] / (4.0 * d["SQ_BUSY_CU_CYCLES"]) for d in per.values()
               if d.get("SQ_BUSY_CU_CYCLES")]
-        return statistics.median(fr) if fr else None
+        cyc = [d["GRBM_GUI_ACTIVE"] / 8.0 for d in per.values() if d.get("GRBM_GUI_ACTIVE")]
+        return (statistics.median(fr) if fr else None), (statistics.median(cyc) if cyc else None)
 
     copy_fetch = one("copy_fetch", "FETCH_SIZE", "copyBuffer")
     copy_write = one("copy_write", "WRITE_SIZE", "copyBuffer")
@@ -197,9 +200,11 @@ def traffic_from(directory: str, workload: str, config_name: str) -> int:
            "fetch_bytes_per_launch": fetch, "write_bytes_per_launch": write,
            "fetch_calibration": f_fetch, "write_calibration": f_write,
            "copy_fetch_kib": copy_fetch, "copy_write_kib": copy_write}
-    busy = busy_fraction("gemm_f16_kernel")
+    busy, cycles = busy_fraction("gemm_f16_kernel")
     if busy is not None:
         rec["mfma_busy_frac"] = busy
+    if cycles is not None:
+        rec["gpu_cycles_per_launch"] = cycles
     with open(traffic_file(workload), "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec), flush=True)
@@ -348,6 +353,16 @@ def main() -> int:
                        "elements": spot["n"], "n_fail": spot.get("n_fail"), "pass": spot["pass"],
                        "max_ulp_err": spot["max_ulp_err"], "max_abs_err": spot.get("max_abs_err")},
     }
+    rec = measured_counters(workload_name, config_name)
+    if rec is not None and "gpu_cycles_per_launch" in rec:
+        # the shader clock this run sustained: the kernel's GPU cycles (from
+        # the committed counter record of the same kernel source) over its
+        # live mean duration; and the matrix cores' busy share at that clock
+        out["roofline"]["counters"] = {
+            "source": os.path.relpath(traffic_file(workload_name), ROOT),
+            "gpu_cycles_per_launch": rec["gpu_cycles_per_launch"],
+            "sclk_ghz": round(rec["gpu_cycles_per_launch"] / (float(launch_ms.mean()) * 1e-3) / 1e9, 3),
+            "mfma_busy_frac": round(rec.get("mfma_busy_frac", float("nan")), 4)}
     if not args.no_ceiling:
         # the matrix cores' sustained rate on register operands alone, for the
         # kernel's MFMA instruction, with constant and with changing random bits

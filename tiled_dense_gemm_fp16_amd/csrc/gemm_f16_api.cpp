@@ -508,15 +508,17 @@ gemm_f16_status_t validate_sp(int64_t M, int64_t N, int64_t K, const void *vals,
     return GEMM_F16_SUCCESS;
 }
 
-// Relative per-workgroup throughput of the sparse tiles (ranking only; 8192^3
-// and 4096^3 on MI355X): the 4-wave 256x256 tile shares each B fragment
-// between 4 A fragments, and the sparse MFMA leaves the kernel bound by
-// B's movement through LDS.  0: kept for tests and sweeps only.
+// Relative per-workgroup throughput of the sparse tiles (ranking only;
+// measured at 8192^3 and 4096^3 on MI355X, A's position words stored by
+// slices): the sparse MFMA does a 64-deep slice in half the dense time, so
+// the tile is bound by issuing its loads, which the spread tile issues half
+// per k step (0.564 ms at 8192^3 against 0.624 with all at the step start).
 double sp_config_efficiency(int c)
 {
     switch (c) {
+    case 3: return 1.10;   // 256x256x64, 4 waves, loads spread over the two k steps
+    case 0: return 1.09;   // 256x256x64, 8 waves
     case 2: return 1.00;   // 256x256x64, 4 waves
-    case 0: return 0.68;   // 256x256x64, 8 waves
     case 1: return 0.60;   // 128x128x64, 4 waves
     default: return 0.0;
     }
