@@ -145,7 +145,7 @@ def test_sparse_large_sampled():
     assert res["pass"], res
 
 
-@pytest.mark.parametrize("shape", [(300, 264, 1008), (130, 72, 4096), (257, 520, 80)])
+@pytest.mark.parametrize("shape", [(300, 264, 1008), (130, 72, 4096), (257, 520, 80), (257, 136, 1024)])
 def test_oracle_operands_through_the_library(shape):
     """The oracle's own compression, put into the library's storage order,
     multiplied by the library: the stored order the kernels read is the one
