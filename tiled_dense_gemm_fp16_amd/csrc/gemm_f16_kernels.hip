@@ -72,7 +72,7 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float *__restr
                 acc[3] = __builtin_fmaxf(acc[3], 0.0f);
             }
             const half_t h0 = (half_t)acc[0], h1 = (half_t)acc[1], h2 = (half_t)acc[2], h3 = (half_t)acc[3];
-            reinterpret_cast<half4 *>(C)[q] = half4{h0, h1, h2, h3};
+            __builtin_nontemporal_store(half4{h0, h1, h2, h3}, reinterpret_cast<half4 *>(C) + q);   // C streams out
         }
     } else {
         for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < mn; e += stride) {
@@ -82,7 +82,7 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float *__restr
             acc *= alpha;
             if (relu)
                 acc = __builtin_fmaxf(acc, 0.0f);
-            C[e] = (half_t)acc;
+            __builtin_nontemporal_store((half_t)acc, C + e);
         }
     }
 }

@@ -100,6 +100,14 @@ typedef int int4v __attribute__((ext_vector_type(4)));
 typedef int int2v __attribute__((ext_vector_type(2)));
 
 #define LDS_AS __attribute__((address_space(3)))
+// Cache policy of the stores of C: non-temporal (the NT bit, 2).  C is
+// written once and not read back by the kernel; streamed, it no longer
+// displaces the operands' lines in the L2s and the Infinity Cache, whose
+// re-reads feed the other tiles (8192^3: +4 %, 1411 -> 1472 TFLOP/s
+// interleaved; the operands' loads with the NT bit lost 10-35 %).
+#ifndef GEMM_F16_C_CPOL
+#define GEMM_F16_C_CPOL 2
+#endif
 
 // Descriptor word 3 for gfx9-family raw buffers (untyped, 32-bit dwords).
 constexpr int kBufferFlags = 0x00020000;
@@ -1021,7 +1029,7 @@ gemm_f16_kernel(KernelArgs args)
             const int4v v = *reinterpret_cast<const int4v *>(ct + r * BN + ((c8 ^ swz(r)) << 3));
             const int n = n0 + 8 * c8;
             const uint32_t off = ((uint32_t)r * (uint32_t)N + (uint32_t)n) * 2u;
-            __builtin_amdgcn_raw_buffer_store_b128(v, c_rsrc, off | oob_unless(n < N), 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(v, c_rsrc, off | oob_unless(n < N), 0, GEMM_F16_C_CPOL);
         }
         return;
     }
@@ -1048,7 +1056,8 @@ gemm_f16_kernel(KernelArgs args)
                         x = __builtin_fmaxf(x, 0.0f);
                     const half_t h = (half_t)x;
                     const uint32_t off = ((uint32_t)r * (uint32_t)N + (uint32_t)n) * 2u;
-                    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(short, h), c_rsrc, off | col_mask, 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(short, h), c_rsrc, off | col_mask, 0,
+                                                          GEMM_F16_C_CPOL);
                 }
             }
         return;
@@ -1163,7 +1172,7 @@ gemm_f16_kernel(KernelArgs args)
                 v = int4v{v[2], v[3], v[0], v[1]};
             const int n = n0 + 8 * c;
             const uint32_t off = ((uint32_t)r * (uint32_t)N + (uint32_t)n) * 2u;
-            __builtin_amdgcn_raw_buffer_store_b128(v, c_rsrc, off | oob_unless(n < N), 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(v, c_rsrc, off | oob_unless(n < N), 0, GEMM_F16_C_CPOL);
         }
         return;
     }
@@ -1182,14 +1191,15 @@ gemm_f16_kernel(KernelArgs args)
                     // N % 4 == 0: the four columns are all inside or all outside
                     half4 h = {h0, h1, h2, h3};
                     __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(int2v, h), c_rsrc,
-                                                          off | oob_unless(n < N), 0, 0);
+                                                          off | oob_unless(n < N), 0, GEMM_F16_C_CPOL);
                 } else {
                     const short hs[4] = {__builtin_bit_cast(short, h0), __builtin_bit_cast(short, h1),
                                          __builtin_bit_cast(short, h2), __builtin_bit_cast(short, h3)};
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
                         __builtin_amdgcn_raw_buffer_store_b16(hs[e], c_rsrc,
-                                                              (off + 2u * e) | oob_unless(n + e < N), 0, 0);
+                                                              (off + 2u * e) | oob_unless(n + e < N), 0,
+                                                              GEMM_F16_C_CPOL);
                 }
             }
         }
@@ -1390,7 +1400,8 @@ gemm_f16_persistent_kernel(KernelArgs args)
                 // element conversions kept as scalars (see the one-tile epilogue)
                 const half_t h0 = (half_t)v0, h1 = (half_t)v1, h2 = (half_t)v2, h3 = (half_t)v3;
                 const half4 h = {h0, h1, h2, h3};
-                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(int2v, h), c_rsrc, row + col[j], 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(int2v, h), c_rsrc, row + col[j], 0,
+                                                      GEMM_F16_C_CPOL);
             }
         }
     };
