@@ -581,11 +581,12 @@ struct Tile {
 // ahead of their MFMAs at once (measured: 4 parts +3 % for 256x256 tiles
 // with 4 waves and +6-8 % for 128x128; 2 parts +0-3 % with 8 waves, where 4
 // parts leave the last loads too little time).  1: all at the start.
-// STAGED_ONLY: compiled with the LDS-staged fp16 epilogue alone (no split-K
-// partials, N % 8 == 0 and C 16-byte aligned), for tiles whose accumulator
-// fills the matrix-core registers: with one epilogue path the accumulator
-// does not have to be held in vector registers across a branch, where it
-// overflows them and spills to scratch.
+// EPI_ONLY: 1 compiles the LDS-staged fp16 epilogue alone (no split-K
+// partials, N % 8 == 0 and C 16-byte aligned), 2 the split-K partial stores
+// alone, 3 the direct fp16 stores alone (8- or 2-byte pieces), 0 every path.  For tiles whose accumulator fills the matrix-core
+// registers: with one epilogue path the accumulator does not have to be held
+// in vector registers across a branch, where it overflows them and spills to
+// scratch.
 // WIDE_META (sparse, K % 64 == 0): the four position words of a 64-deep
 // slice of every tile row travel to LDS with the slice's operands (4-byte
 // direct loads, two per row), and each fragment reads its words from there,
@@ -593,12 +594,13 @@ struct Tile {
 // registers would make the compiler wait for them with a count that also
 // covers later tiles' loads, draining the prefetch ring every slice.
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool DIRECT, int VA, int VB, bool A_ROWS_K,
-          bool B_ROWS_K, int SPREAD = 1, bool SPARSE = false, bool M16 = false, bool STAGED_ONLY = false,
+          bool B_ROWS_K, int SPREAD = 1, bool SPARSE = false, bool M16 = false, int EPI_ONLY = 0,
           bool WIDE_META = false>
 __global__ void __launch_bounds__(64 * WM * WN)
 __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4)))
 gemm_f16_kernel(KernelArgs args)
 {
+    constexpr bool STAGED_ONLY = EPI_ONLY == 1, SPLIT_ONLY = EPI_ONLY == 2, DIRECT_ONLY = EPI_ONLY == 3;
     using T = Tile<BM, BN, BK, WM, WN, STAGES, DIRECT, VA, VB, A_ROWS_K, B_ROWS_K, SPARSE, M16>;
     __shared__ __attribute__((aligned(1024))) half_t lds[T::LDS_BYTES / 2];
     half_t *const As = lds;                                  // STAGES A stages
@@ -958,7 +960,7 @@ gemm_f16_kernel(KernelArgs args)
     }
     // the last tile's last step: set (nk NS - 1) & 1 (set 1, zero, when nk = 0)
     if constexpr (NS % 2 == 0) {
-        if (STAGED_ONLY || nk > 0)
+        if (EPI_ONLY != 0 || nk > 0)
             mma(f1);
     } else {
         // nk odd: the last tile (nk - 1, even) ended in f0
@@ -969,7 +971,7 @@ gemm_f16_kernel(KernelArgs args)
 #pragma unroll
         for (int i = 0; i < T::TM; ++i)
             f1.y[i] = odd ? f0.y[i] : f1.y[i];
-        if (STAGED_ONLY || nk > 0)
+        if (EPI_ONLY != 0 || nk > 0)
             mma(f1);
     }
     wait_vmcnt<0>();   // the tail's zero-filling loads must land before the workgroup retires
@@ -1062,7 +1064,7 @@ gemm_f16_kernel(KernelArgs args)
             }
         return;
     }
-    if (!STAGED_ONLY && args.W) {
+    if (SPLIT_ONLY || (!STAGED_ONLY && !DIRECT_ONLY && args.W)) {
         // split-K: the fp32 partial sums of this split go to its slice of the
         // workspace (row pitch N); the reduction applies the epilogue.  When
         // N % 4 == 0 a lane's four consecutive columns leave as one 16-byte
@@ -1124,7 +1126,7 @@ gemm_f16_kernel(KernelArgs args)
         h3 = (half_t)v3;
     };
     static_assert(BM * BN * 2 <= T::LDS_BYTES, "the output tile fits in the LDS stages");
-    if (STAGED_ONLY || vec_c == 8) {
+    if (STAGED_ONLY || (!DIRECT_ONLY && vec_c == 8)) {
         // N % 8 == 0 and C 16-byte aligned: stage the fp16 tile through the
         // (now idle) LDS and write it as 16-byte pieces of consecutive
         // columns, so that every row of the tile leaves as whole cache lines.
@@ -1475,20 +1477,32 @@ static hipError_t launch_one(const KernelArgs &a, int64_t grid, hipStream_t stre
 #undef GEMM_F16_SP
         return hipGetLastError();
     }
-    // one wave per SIMD holding a 128x128 accumulator (256 registers): the
-    // common unsplit, 16-byte-aligned case runs the staged-epilogue build
+    // one wave per SIMD holding a 128x128 accumulator (256 registers): each
+    // epilogue path has a build of its own (with every path, the build would
+    // spill around its epilogue): the staged fp16 stores for the common
+    // unsplit, 16-byte-aligned case, the split-K partials, the direct stores
     constexpr bool FULL_ACC = !SPARSE && WM * WN == 4 && BM * BN == 256 * 256;
     if constexpr (FULL_ACC) {
         if (a.W == nullptr && a.vec_c == 8) {
             hipLaunchKernelGGL(
-                (gemm_f16_kernel<BM, BN, BK, WM, WN, STAGES, DIRECT, VA, VB, AR, BR, SPREAD, SPARSE, M16, true>),
+                (gemm_f16_kernel<BM, BN, BK, WM, WN, STAGES, DIRECT, VA, VB, AR, BR, SPREAD, SPARSE, M16, 1>),
                 dim3((unsigned)grid), dim3(64 * WM * WN), 0, stream, a);
             return hipGetLastError();
         }
+        if (a.W != nullptr)
+            hipLaunchKernelGGL(
+                (gemm_f16_kernel<BM, BN, BK, WM, WN, STAGES, DIRECT, VA, VB, AR, BR, SPREAD, SPARSE, M16, 2>),
+                dim3((unsigned)grid), dim3(64 * WM * WN), 0, stream, a);
+        else
+            hipLaunchKernelGGL(
+                (gemm_f16_kernel<BM, BN, BK, WM, WN, STAGES, DIRECT, VA, VB, AR, BR, SPREAD, SPARSE, M16, 3>),
+                dim3((unsigned)grid), dim3(64 * WM * WN), 0, stream, a);
+        return hipGetLastError();
+    } else {
+        hipLaunchKernelGGL((gemm_f16_kernel<BM, BN, BK, WM, WN, STAGES, DIRECT, VA, VB, AR, BR, SPREAD, SPARSE, M16>),
+                           dim3((unsigned)grid), dim3(64 * WM * WN), 0, stream, a);
+        return hipGetLastError();
     }
-    hipLaunchKernelGGL((gemm_f16_kernel<BM, BN, BK, WM, WN, STAGES, DIRECT, VA, VB, AR, BR, SPREAD, SPARSE, M16>),
-                       dim3((unsigned)grid), dim3(64 * WM * WN), 0, stream, a);
-    return hipGetLastError();
 }
 
 // the persistent tile loop: `grid` resident workgroups (at most one per CU)
