@@ -283,8 +283,11 @@ typedef struct gemm_f16_plan {
     int32_t stages;        /* LDS ring-buffer stages */
     int32_t threads;       /* threads per workgroup */
     int32_t direct_lds;    /* 1: operands go global -> LDS without registers */
-    int32_t vec_a;         /* binary16 elements per global load of A */
-    int32_t vec_b;         /* binary16 elements per global load of B */
+    int32_t vec_a;         /* alignment of A's rows the kernel relies on, in binary16
+                              elements: the width of its global loads (register-staged),
+                              or 8 / 2 for 16-byte / 4-byte aligned rows (direct_lds,
+                              whose loads always move 16-byte chunks) */
+    int32_t vec_b;         /* the same for B */
     int32_t vec_c;         /* binary16 elements per store of C */
     int64_t tiles_m;       /* ceil(M / bM) */
     int64_t tiles_n;       /* ceil(N / bN) */

@@ -87,45 +87,105 @@ def test_ragged_shapes(shape, epilogue):
         check(a, b, epilogue, config=c, label=f"config {g.config_name(c)}")
 
 
-# A's rows only 4-byte aligned (K = 2, 4 or 6 mod 8) while B's rows allow
-# 16-byte loads (N % 8 == 0): the configuration that moves A with 4-byte
-# direct loads; K tails end inside a 16-byte chunk.
-A4 = "256x256x64_s2_direct_m16_a4"
-A4_SHAPES = [(300, 264, 130), (520, 392, 198), (257, 520, 66), (64, 64, 2), (511, 264, 4100)]
+# ---- rows only 4-byte aligned: the direct configurations for such rows ----
+# Their loads move 16-byte chunks at 4-byte alignment.  Where K % 8 != 0 the
+# chunk at the end of a k-row (A given M x K, B given N x K) runs into the
+# next row's first elements, which the kernel zeroes in LDS; an mn-row's
+# chunk past M or N only reaches outputs that are never stored.
+U_NAMES = ("256x256x64_s2_direct_m16_u", "128x128x64_s4_direct_m16_u", "64x64x64_s4_direct_u")
+# every pitch even; K % 8 in {2, 4, 6}; M and N pitches off 16-byte alignment in some
+U_SHAPES = [(300, 264, 130), (520, 392, 198), (258, 522, 66), (64, 64, 2), (510, 268, 4100), (130, 134, 132)]
+ALL_LAYOUTS = [(False, False), (False, True), (True, False), (True, True)]
 
 
-def a4_config():
-    return [c for c in range(g.num_configs()) if g.config_name(c) == A4][0]
+def u_configs():
+    cfgs = [c for c in range(g.num_configs()) if g.config_name(c) in U_NAMES]
+    assert len(cfgs) == len(U_NAMES)
+    return cfgs
 
 
-@pytest.mark.parametrize("shape", A4_SHAPES)
-@pytest.mark.parametrize("epilogue", ["none", "relu"])
-def test_a_rows_4byte_direct_loads(shape, epilogue):
+@pytest.mark.parametrize("ta,tb", ALL_LAYOUTS)
+@pytest.mark.parametrize("shape", U_SHAPES)
+def test_rows_4byte_aligned_direct_configs(ta, tb, shape):
     M, N, K = shape
-    c = a4_config()
-    p = g.plan(M, N, K, 1 << 20, 1 << 20, 1 << 20, config=c)
-    assert p["vec_a"] == 2 and p["vec_b"] == 8 and p["direct_lds"] == 1
-    a, b = workloads.draw(M, N, K, "uniform", 3 * M + N + K)
-    check(a, b, epilogue, config=c, label="A 4-byte direct")
+    a_st, b_st = stored(M, N, K, ta, tb, 11 * M + 3 * N + K)
+    a_dev, b_dev = a_st.to(DEV), b_st.to(DEV)
+    for epi in ("none", "relu"):
+        ref = oracle.gemm(u16(a_st), u16(b_st), relu=(epi == "relu"), trans_a=ta, trans_b=tb)
+        for c in u_configs():
+            p = g.plan(M, N, K, a_dev.data_ptr(), b_dev.data_ptr(), 1 << 20, config=c, trans_a=ta, trans_b=tb)
+            assert (p["direct_lds"], p["vec_a"], p["vec_b"]) == (1, 2, 2)
+            print(f"[parity] 4-byte rows ta={ta} tb={tb} {M}x{N}x{K} epi={epi} {g.config_name(c)}", flush=True)
+            out = g.gemm(a_dev, b_dev, epilogue=epi, config=c, trans_a=ta, trans_b=tb)
+            torch.cuda.synchronize()
+            res = oracle.compare(u16(out), ref)
+            assert res["pass"], (ta, tb, shape, epi, g.config_name(c), res)
 
 
-def test_a_rows_4byte_direct_loads_nt_offset_pointer():
+def compare_with_specials(got, ref):
+    """NaN and infinity where the oracle has them (same sign); every finite
+    reference element within the usual bound."""
+    gv, rv = oracle.decode(got), oracle.decode(ref)
+    assert np.array_equal(np.isnan(gv), np.isnan(rv))
+    assert np.array_equal(np.isposinf(gv), np.isposinf(rv)) and np.array_equal(np.isneginf(gv), np.isneginf(rv))
+    fin = np.isfinite(rv)
+    res = oracle.compare(got[fin], ref[fin])
+    assert res["pass"], res
+    return int(np.count_nonzero(~fin))
+
+
+@pytest.mark.parametrize("K", [130, 132, 134])
+@pytest.mark.parametrize("ta,tb", [(False, False), (False, True), (True, True)])
+def test_rows_4byte_aligned_tail_chunk_is_cleared(K, ta, tb):
+    """Infinities and a NaN among the first k of some rows of each k-rows
+    operand: the chunk that ends the previous row at K reads them, and the
+    previous row's outputs must still equal the oracle's (finite)."""
+    M, N = 300, 264
+    a, b = workloads.draw(M, N, K, "uniform", 7 * K + 2 * ta + tb)
+    a, b = a.clone(), b.clone()
+    vals = (float("inf"), float("-inf"), float("nan"), float("inf"))
+    if not ta:
+        # A given M x K: rows 1, 77, 255, 257 start with a special; B's first
+        # rows kept away from zero and subnormals (infinity times them is
+        # then infinity, whatever the order of the sum)
+        b[:4] = torch.where(b[:4].abs() < 1 / 16, torch.full_like(b[:4], 0.5), b[:4])
+        for r, k, v in zip((1, 77, 255, 257), range(4), vals):
+            a[r, k] = v
+    if tb:
+        # B given N x K: columns 1, 130, 257, 263 of the product likewise
+        a[:, :4] = torch.where(a[:, :4].abs() < 1 / 16, torch.full_like(a[:, :4], 0.5), a[:, :4])
+        for n, k, v in zip((1, 130, 257, 263), range(4), vals):
+            b[k, n] = v
+    a_st = a.t().contiguous() if ta else a
+    b_st = b.t().contiguous() if tb else b
+    ref = oracle.gemm(u16(a_st), u16(b_st), trans_a=ta, trans_b=tb)
+    a_dev, b_dev = a_st.to(DEV), b_st.to(DEV)
+    for c in u_configs():
+        print(f"[parity] tail chunk with specials ta={ta} tb={tb} K={K} {g.config_name(c)}", flush=True)
+        out = g.gemm(a_dev, b_dev, config=c, trans_a=ta, trans_b=tb)
+        torch.cuda.synchronize()
+        n_special = compare_with_specials(u16(out), ref)
+        assert n_special > 0
+
+
+def test_rows_4byte_aligned_nt_offset_pointer():
     """B given N x K with a 16-byte aligned pitch, A's pointer only 4-byte
     aligned (a view two elements into a buffer)."""
     M, N, K = 300, 264, 136
-    c = a4_config()
     a, b = workloads.draw(M, N, K, "uniform", 1234)
     buf = torch.zeros(M * K + 8, dtype=torch.float16, device=DEV)
     a_dev = buf[2:2 + M * K].view(M, K)
     a_dev.copy_(a.to(DEV))
     bt = b.t().contiguous().to(DEV)
-    p = g.plan(M, N, K, a_dev.data_ptr(), bt.data_ptr(), 1 << 20, config=c, trans_b=True)
-    assert p["vec_a"] == 2 and p["direct_lds"] == 1
-    print(f"[parity] A 4-byte direct, NT, A pointer offset by 4 bytes, {M}x{N}x{K}", flush=True)
-    out = g.gemm(a_dev, bt, config=c, trans_b=True)
-    torch.cuda.synchronize()
-    res = oracle.compare(u16(out), oracle.gemm(u16(a), u16(b)))
-    assert res["pass"], res
+    ref = oracle.gemm(u16(a), u16(b))
+    for c in u_configs():
+        p = g.plan(M, N, K, a_dev.data_ptr(), bt.data_ptr(), 1 << 20, config=c, trans_b=True)
+        assert p["vec_a"] == 2 and p["direct_lds"] == 1
+        print(f"[parity] 4-byte rows, NT, A pointer offset by 4 bytes, {M}x{N}x{K} {g.config_name(c)}", flush=True)
+        out = g.gemm(a_dev, bt, config=c, trans_b=True)
+        torch.cuda.synchronize()
+        res = oracle.compare(u16(out), ref)
+        assert res["pass"], res
 
 
 def test_misaligned_pointers():

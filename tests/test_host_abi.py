@@ -115,18 +115,19 @@ def test_plan_geometry_and_vector_widths():
     assert p["tiles_m"] == -(-3000 // p["block_m"]) and p["tiles_n"] == -(-5000 // p["block_n"])
     assert p["grid"] == p["tiles_m"] * p["tiles_n"]
     assert p["k_tiles"] == -(-4100 // p["block_k"])
-    # K = 4100: A's rows only 8-byte aligned; B's allow 16-byte loads, so A
-    # moves straight to LDS in 4-byte pieces (measured: +11 % over 8-byte
-    # register-staged vectors on this shape)
-    assert p["vec_a"] == 2 and p["direct_lds"] == 1
-    assert p["vec_b"] == 8 and p["vec_c"] == 8          # N = 5000: 16-byte stores of C
+    # K = 4100: A's rows only 8-byte aligned, so the direct configuration
+    # for 4-byte rows runs (16-byte loads at 8-byte alignment)
+    assert p["vec_a"] == 2 and p["vec_b"] == 2 and p["direct_lds"] == 1
+    assert p["vec_c"] == 8                              # N = 5000: 16-byte stores of C
     assert p["flops"] == 2.0 * 3000 * 5000 * 4100
     assert p["min_bytes"] == 2.0 * (3000 * 4100 + 4100 * 5000 + 3000 * 5000)
     # odd pitches and 2-byte-aligned pointers
     p = g.plan(33, 17, 9, FAKE + 2, FAKE + 6, FAKE + 2)
     assert (p["vec_a"], p["vec_b"], p["vec_c"]) == (1, 1, 1)
     p = g.plan(64, 64, 64, FAKE + 4, FAKE + 8, FAKE)
-    assert (p["vec_a"], p["vec_b"], p["vec_c"]) == (2, 4, 8)
+    # a direct configuration reports the rows' alignment it needs (4 bytes),
+    # a register-staged one its vector widths
+    assert (p["vec_a"], p["vec_b"], p["vec_c"]) == ((2, 2, 8) if p["direct_lds"] else (2, 4, 8))
     p = g.plan(64, 60, 64, FAKE, FAKE, FAKE + 8)
     assert p["vec_c"] == 4
     # large aligned problems take a direct-to-LDS configuration
@@ -164,10 +165,14 @@ def test_transposed_layout_planning():
     # vector widths follow the pitch of each matrix as stored
     p = g.plan(64, 48, 40, FAKE, FAKE, FAKE, trans_a=True)            # A stored 40 x 64: pitch M = 64
     assert (p["vec_a"], p["trans_a"], p["trans_b"]) == (8, 1, 0)
-    p = g.plan(66, 48, 40, FAKE, FAKE, FAKE, trans_a=True)            # pitch 66: single elements
+    p = g.plan(66, 48, 40, FAKE, FAKE, FAKE, trans_a=True)            # pitch 66: 4-byte rows
+    assert p["vec_a"] == (2 if p["direct_lds"] else 1)
+    p = g.plan(65, 48, 40, FAKE, FAKE, FAKE, trans_a=True)            # pitch 65: single elements
     assert p["vec_a"] == 1 and p["direct_lds"] == 0
     p = g.plan(64, 48, 36, FAKE, FAKE, FAKE, trans_b=True)            # B stored 48 x 36: pitch K = 36
-    assert p["vec_b"] == 1 and p["trans_b"] == 1
+    assert p["vec_b"] in (1, 2) and p["trans_b"] == 1
+    p = g.plan(64, 48, 35, FAKE, FAKE, FAKE, trans_b=True)            # pitch 35: single elements
+    assert p["vec_b"] == 1 and p["direct_lds"] == 0
     p = g.plan(8192, 8192, 8192, FAKE, FAKE, FAKE, trans_a=True, trans_b=True)
     assert p["direct_lds"] == 1
     # only some configurations are compiled for transposed layouts; the others refuse
@@ -224,23 +229,35 @@ def test_python_wrapper_argument_checks():
         g.gemm(a.float(), a)
 
 
-def test_only_a_misaligned_takes_four_byte_direct_loads():
-    """A stored M x K whose rows or pointer are only 4-byte aligned, B's
-    16-byte aligned: A moves straight to LDS in 4-byte pieces.  An odd K, or
-    A given K x M, never takes that path."""
-    a4 = "256x256x64_s2_direct_m16_a4"
-    for kw in ({}, {"trans_b": True}):
-        p = g.plan(8192, 8192, 8192, FAKE + 4, FAKE, FAKE, **kw)          # A's pointer 4-byte aligned
-        assert g.config_name(p["config"]) == a4 and (p["vec_a"], p["vec_b"], p["direct_lds"]) == (2, 8, 1), kw
-    p = g.plan(8192, 8192, 8194, FAKE, FAKE, FAKE)                        # A's rows 4-byte aligned
-    assert g.config_name(p["config"]) == a4 and p["vec_a"] == 2
+U_NAMES = {"256x256x64_s2_direct_m16_u", "128x128x64_s4_direct_m16_u", "64x64x64_s4_direct_u"}
+
+
+def test_rows_4byte_aligned_take_direct_configs():
+    """Operands whose rows (or pointers) are only 4-byte aligned run the
+    direct configurations for such rows (16-byte loads at 4-byte alignment)
+    in every layout; rows only 2-byte aligned (an odd pitch or pointer) run
+    register-staged ones."""
+    index = {g.config_name(c): c for c in range(g.num_configs())}
+    assert U_NAMES <= set(index)
+    for ta in (False, True):
+        for tb in (False, True):
+            kw = {"trans_a": ta, "trans_b": tb}
+            p = g.plan(8192, 8192, 8192, FAKE + 4, FAKE, FAKE, **kw)        # A's pointer 4-byte aligned
+            assert g.config_name(p["config"]) in U_NAMES and (p["vec_a"], p["vec_b"], p["direct_lds"]) == (2, 2, 1), kw
+            p = g.plan(8196, 8196, 8196, FAKE, FAKE, FAKE, **kw)            # every pitch 8-byte aligned
+            assert g.config_name(p["config"]) in U_NAMES, kw
     p = g.plan(8192, 8192, 8193, FAKE, FAKE, FAKE)                        # odd K: 2-byte rows
-    assert g.config_name(p["config"]) != a4 and p["vec_a"] == 1
-    p = g.plan(8192, 8192, 8192, FAKE + 4, FAKE, FAKE, trans_a=True)      # A given K x M
-    assert g.config_name(p["config"]) != a4
-    with pytest.raises(g.GemmError):                                       # B's rows must allow 16 bytes
-        g.plan(8192, 8196, 8194, FAKE, FAKE, FAKE, config=[c for c in range(g.num_configs())
-                                                            if g.config_name(c) == a4][0])
+    assert p["direct_lds"] == 0 and p["vec_a"] == 1
+    p = g.plan(8192, 8192, 8192, FAKE + 2, FAKE, FAKE)                    # A's pointer 2-byte aligned
+    assert p["direct_lds"] == 0
+    for name in U_NAMES:
+        g.plan(8192, 8196, 8194, FAKE, FAKE, FAKE, config=index[name])
+        for kw in ({"trans_b": True}, {"trans_a": True}):
+            g.plan(8194, 8196, 8198, FAKE, FAKE, FAKE, config=index[name], **kw)
+        with pytest.raises(g.GemmError):
+            g.plan(8192, 8192, 8193, FAKE, FAKE, FAKE, config=index[name])
+        with pytest.raises(g.GemmError):
+            g.plan(8192, 8192, 8192, FAKE, FAKE + 2, FAKE, config=index[name])
 
 
 TUNED = os.path.join(ROOT, "tiled_dense_gemm_fp16_amd", "csrc", "gemm_f16_tuned.inc")
@@ -270,8 +287,8 @@ def test_tuned_table_drives_the_automatic_choice():
         key = (lm, ln, lk, ta, tb, aligned)
         assert key not in seen
         seen.add(key)
-        # class 1: aligned pitches; 0: every pitch off by 4 elements; 2: only K (A's pitch)
-        pm, pn, pk = {1: (0, 0, 0), 0: (4, 4, 4), 2: (0, 0, 4)}[aligned]
+        # class 1: aligned pitches; 2: every pitch off by 4 elements; 0: every pitch odd
+        pm, pn, pk = {1: (0, 0, 0), 2: (4, 4, 4), 0: (1, 1, 1)}[aligned]
         M, N, K = (1 << lm) + pm, (1 << ln) + pn, (1 << lk) + pk
         kw = dict(trans_a=bool(ta), trans_b=bool(tb))
         p = g.plan(M, N, K, FAKE, FAKE, FAKE, **kw)
@@ -281,7 +298,7 @@ def test_tuned_table_drives_the_automatic_choice():
         want = g.plan(M, N, K, FAKE, FAKE, FAKE, config=cfg, splits=splits, **kw)
         assert q["splits"] == want["splits"] and q["k_split"] == want["k_split"], key
         assert (p["vec_a"] == 8 and p["vec_b"] == 8) == (aligned == 1)
-        assert aligned != 2 or (not ta and not tb and p["vec_b"] == 8)
+        assert aligned != 0 or min(p["vec_a"], p["vec_b"]) == 1
     # far from every swept shape the analytic model decides (no table hit):
     # a deep K under a one-tile output is split when a workspace may be used
     p = g.plan(24, 24, 1 << 20, FAKE, FAKE, FAKE, splits=g.SPLITS_AUTO)

@@ -28,12 +28,14 @@ const ConfigDesc kConfigs[kNumConfigs] = {
     {"256x256x64_s2_staged_w8", 256, 256, 64, 2, 8, false, 4, 4, kAllLayouts, 1},
     {"256x128x64_s2_staged", 256, 128, 64, 2, 4, false, 4, 4, kNN, 1},
     {"256x256x64_s2_direct_m16", 256, 256, 64, 2, 4, true, 8, 8, kAllLayouts, 1},
-    {"256x256x64_s2_direct_m16_a4", 256, 256, 64, 2, 4, true, 2, 8, kNN | kNT, 1},
+    {"256x256x64_s2_direct_m16_u", 256, 256, 64, 2, 4, true, 2, 2, kAllLayouts, 1},
     {"256x256x32_s4_direct_m16", 256, 256, 32, 4, 4, true, 8, 8, kAllLayouts, 1},
     {"256x256x64_s2_direct_m16_persistent", 256, 256, 64, 2, 4, true, 8, 8, kAllLayouts, 1, true},
     {"64x64x64_s4_direct", 64, 64, 64, 4, 4, true, 8, 8, kAllLayouts, 2},
     {"128x128x64_s4_direct_m16", 128, 128, 64, 4, 4, true, 8, 8, kAllLayouts, 1},
     {"128x64x64_s4_direct", 128, 64, 64, 4, 4, true, 8, 8, kAllLayouts, 1},
+    {"128x128x64_s4_direct_m16_u", 128, 128, 64, 4, 4, true, 2, 2, kAllLayouts, 1},
+    {"64x64x64_s4_direct_u", 64, 64, 64, 4, 4, true, 2, 2, kAllLayouts, 2},
 };
 
 // Sparse configurations (2:4 A): fields as above; every one takes A as
@@ -106,12 +108,14 @@ double config_efficiency(int c)
 {
     switch (c) {
     case 8: return 1.06;    // 256x256x64 direct, 4 waves, 16x16x32 MFMAs
-    case 9: return 0.95;    // the same with 4-byte loads of A (A rows 4-byte aligned)
+    case 9: return 1.02;    // the same for rows only 4-byte aligned
     case 10: return 0.99;   // 256x256x32 direct, 4 stages, 16x16x32 MFMAs (ahead only for A given K x M)
     case 11: return 1.05;   // 256x256x64 16x16x32 tile, persistent over the tiles (within 1 % of 8)
     case 12: return 0.30;   // 64x64x64 direct, 4 stages (latency-bound; many small tiles)
     case 13: return 0.82;   // 128x128x64 direct, 4 stages, 16x16x32 MFMAs
     case 14: return 0.60;   // 128x64x64 direct, 4 stages
+    case 15: return 0.80;   // 13 for rows only 4-byte aligned
+    case 16: return 0.29;   // 12 for rows only 4-byte aligned
 
     case 5: return 1.00;    // 256x256x64 direct, 8 waves
     case 0: return 0.94;    // 256x128x64 direct, 3 stages, 16x16x32 MFMAs
@@ -220,8 +224,8 @@ void fill_plan(int c, int64_t M, int64_t N, int64_t K, int va, int vb, int vc, b
 struct TunedEntry {
     int lm, ln, lk;        // log2 of the swept M, N, K
     int trans_a, trans_b;
-    int aligned;           // 1: pitches allowed 16-byte loads of both operands; 2: of B only,
-                           // A's rows 4-byte aligned (A . B and A . B^T); 0: otherwise
+    int aligned;           // rows of both operands 16-byte aligned (1), both at least 4-byte
+                           // aligned (2), otherwise (0)
     int config;
     int splits;
     double tflops;
@@ -356,10 +360,10 @@ gemm_f16_status_t make_plan(int64_t M, int64_t N, int64_t K, const void *A, bool
     int c = config;
     Split sp = {1, K};
     if (c == GEMM_F16_CONFIG_AUTO) {
-        // alignment class of the table: both operands 16-byte (1), only B (2,
-        // A stored M x K with 4-byte rows), neither (0); a class-2 shape with
-        // no class-2 entry near it takes the class-0 entries
-        const int cls = (va == 8 && vb == 8) ? 1 : (!ta && va >= 2 && vb == 8) ? 2 : 0;
+        // alignment class of the table: both operands' rows 16-byte aligned
+        // (1), both at least 4-byte aligned (2), otherwise (0); a class-2
+        // shape with no class-2 entry near it takes the class-0 entries
+        const int cls = (va == 8 && vb == 8) ? 1 : (va >= 2 && vb >= 2) ? 2 : 0;
         const TunedEntry *e = tuned_entry(M, N, K, ta, tb, cls, va, vb);
         if (!e && cls == 2)
             e = tuned_entry(M, N, K, ta, tb, 0, va, vb);

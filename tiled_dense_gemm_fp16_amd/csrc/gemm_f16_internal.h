@@ -34,14 +34,15 @@ struct ConfigDesc {
     int stages;
     int waves;            // wave64s per workgroup (4: one per SIMD, 8: two)
     bool direct;          // operands move global -> LDS with buffer_load ... lds
-    int min_vec;          // smallest vector width (elements) of A loads it accepts
-    int min_vec_b;        // ... of B loads
+    int min_vec;          // alignment of A's rows it needs, in elements: direct kernels (always
+                          // 16-byte loads) 8 or 2, register-staged ones their narrowest vector
+    int min_vec_b;        // ... of B's rows
     int layouts;          // layouts compiled, bit 2 trans_a + trans_b: 1 = A . B only, 15 = all four
     int occupancy;        // workgroups resident per CU (LDS and register limits)
     bool persistent;      // one resident workgroup per CU loops over the tiles
 };
 
-constexpr int kNumConfigs = 15;
+constexpr int kNumConfigs = 17;
 extern const ConfigDesc kConfigs[kNumConfigs];
 
 // Launch configuration `config` with `grid` workgroups on `s`.

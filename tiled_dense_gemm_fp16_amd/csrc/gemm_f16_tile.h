@@ -283,7 +283,9 @@ __device__ __forceinline__ void lds_store(half_t *p, typename VecT<V>::type v)
 // transposed as N x K.  The LDS tile is [BMN][BK] and an MFMA fragment (8 k
 // of one m or n per lane) is one 16-byte read.  The workgroup's BMN rows form
 // one buffer descriptor (rows past the matrix read as 0); columns past K are
-// masked, since they would read the next row.
+// masked, since they would read the next row (16-byte chunks wholly past K
+// by their offsets; with rows only 4-byte aligned, the part past K of the
+// chunk that straddles the row end is zeroed in LDS by fix_tail).
 //
 // Otherwise the stored rows run along m or n -- A given transposed as K x M,
 // or B given as K x N.  The LDS tile is [BK][BMN] (as in memory) and a
@@ -303,16 +305,20 @@ struct Operand {
     static constexpr int CHUNKS = ROW / 8;                   // 16-byte chunks per row
     static constexpr int WAVES = THREADS / 64;
     static_assert(CHUNKS >= 2 && (CHUNKS & (CHUNKS - 1)) == 0, "rows of a power-of-two number of chunks");
-    // direct: each lane moves WB bytes per load, so one wave instruction
-    // fills 64 WB bytes of LDS, lane l at byte WB l.  16-byte chunks, or
-    // 4-byte pieces (V = 2) for a k-rows operand whose rows are only 4-byte
-    // aligned; the LDS layout is the same either way.
-    static constexpr int WB = DIRECT ? 2 * V : 16;
+    // direct: each lane moves one 16-byte chunk per load, so one wave
+    // instruction fills 1 KiB of LDS, lane l at byte 16 l.  V is the
+    // alignment of the stored rows in halves: 8 (16-byte rows) or 2 (rows
+    // only 4-byte aligned).  The memory path serves 16-byte loads at any
+    // 4-byte alignment (measured: with such rows 8-12 % faster than four
+    // times as many 4-byte loads).  A k-rows operand's row of 4-byte
+    // alignment ends inside a chunk when K % 8 != 0: that chunk's part past
+    // K holds the next row's first elements until fix_tail zeroes it.
+    static constexpr int WB = 16;
     static constexpr int WAVE_BYTES = 64 * WB;
     static constexpr int DMA = STAGE * 2 / (THREADS * WB);   // loads per thread per stage
     static_assert(!DIRECT || STAGE * 2 % (THREADS * WB) == 0, "whole block-wide loads");
-    static_assert(!DIRECT || V == 8 || (V == 2 && ROWS_K && CHUNKS == 8),
-                  "direct loads move 16-byte chunks, or 4-byte pieces of 128-byte k rows");
+    static_assert(!DIRECT || V == 8 || V == 2, "direct rows 16-byte or 4-byte aligned");
+    static constexpr bool KTAIL = DIRECT && ROWS_K && V < 8;
     static_assert(!DIRECT || ROW * 2 <= WAVE_BYTES, "a row fits in one wave instruction");
     static constexpr int ROWS_PER_LOAD = DIRECT ? WAVE_BYTES / (ROW * 2) : 1;
     // consecutive direct loads of a thread are ROW_STEP rows apart, a multiple
@@ -371,8 +377,7 @@ struct Operand {
             const int byte = wave * WAVE_BYTES + lane * WB;
             const int r = byte / (ROW * 2);
             const int pos = (byte % (ROW * 2)) / 16;        // 16-byte chunk of the LDS row
-            const int sub = (byte % 16) / 2;                // element inside it (4-byte pieces)
-            const int c = (pos ^ swz(r)) * 8 + sub;
+            const int c = (pos ^ swz(r)) * 8;
             kcol0 = c;
             // (an mn-rows operand's tile origin mn0 is in its slice's base
             // address, so these offsets do not depend on the tile)
@@ -380,7 +385,7 @@ struct Operand {
             step = (uint32_t)ROW_STEP * (uint32_t)ld * 2u;
             if constexpr (ALT_COLUMN) {
                 // row r + ROW_STEP flips one bit of the row's XOR: the chunk moves
-                const int c_odd = (pos ^ swz(r + ROW_STEP)) * 8 + sub;
+                const int c_odd = (pos ^ swz(r + ROW_STEP)) * 8;
                 alt = (uint32_t)((c_odd - c) * 2);
                 kcol1 = c_odd;
             } else {
@@ -445,9 +450,10 @@ struct Operand {
             // the slice's k position is a scalar offset (k-rows operand) or
             // the slice's own buffer range (mn-rows operand).  The row part
             // stays in the range-checked vector offset, so rows past the
-            // matrix read as zero; k columns past K (K % V == 0: a load is
-            // wholly inside or wholly past the row end) get the out-of-range
-            // bit OR-ed in.
+            // matrix read as zero; chunks that start at or past K get the
+            // out-of-range bit OR-ed in.  (An mn-rows chunk that runs past
+            // the matrix edge brings the next row's first elements into
+            // columns past M or N, whose outputs are never stored.)
             const uint32_t soff = (uint32_t)__builtin_amdgcn_readfirstlane((int)shift);
             const uint32_t mask0 = ROWS_K ? oob_unless(k0 + kcol0 < K) : 0u;
             const uint32_t mask1 = ROWS_K ? oob_unless(k0 + kcol1 < K) : 0u;
@@ -458,10 +464,7 @@ struct Operand {
                 const bool odd = ALT_COLUMN && (i & 1);
                 const uint32_t off = ROWS_K ? (voff[i] | (odd ? mask1 : mask0)) : voff[i];
                 LDS_AS void *d = (LDS_AS void *)(dst + (wave + WAVES * i) * (WAVE_BYTES / 2));
-                if constexpr (WB == 16)
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d, 16, off, soff, 0, 0);
-                else
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d, 4, off, soff, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d, 16, off, soff, 0, 0);
             }
         } else {
             (void)dst;
@@ -472,6 +475,35 @@ struct Operand {
                 const uint32_t mask = ROWS_K ? oob_unless(k0 + kcolv[i] < K) : 0u;
                 reg[i] = buf_load<V>(rs, (offv[i] + shift) | mask);
             }
+        }
+    }
+
+    // KTAIL: once this thread's loads of k slice kt (at dst) have landed,
+    // zero the halves at or past K of each chunk it loaded that straddles
+    // the row end.  K is even (4-byte rows) and a chunk starts at an even
+    // column, so a straddling chunk keeps 2, 4 or 6 halves and whole dwords
+    // are cleared.  Rows past the matrix already read as zero.
+    __device__ __forceinline__ void fix_tail(int kt, half_t *dst, int wave, int lane) const
+    {
+        if constexpr (KTAIL) {
+            const int k0 = kbase + kt * BK;
+            const int v0 = K - (k0 + kcol0), v1 = K - (k0 + kcol1);
+#pragma unroll
+            for (int i = 0; i < DMA; ++i) {
+                const int v = (ALT_COLUMN && (i & 1)) ? v1 : v0;   // halves of the chunk before K
+                if (v > 0 && v < 8) {
+                    uint32_t *p = reinterpret_cast<uint32_t *>(dst + (wave + WAVES * i) * (WAVE_BYTES / 2) + lane * 8);
+#pragma unroll
+                    for (int d = 0; d < 4; ++d)
+                        if (2 * d >= v)
+                            p[d] = 0u;
+                }
+            }
+        } else {
+            (void)kt;
+            (void)dst;
+            (void)wave;
+            (void)lane;
         }
     }
 
@@ -902,16 +934,30 @@ gemm_f16_kernel(KernelArgs args)
         }
         // set (CUR + NS - 1) & 1 now holds step NS-1 of this tile, multiplied by the next call
     };
-    // Wait until tile kt is in LDS for every wave: this wave's loads (direct)
-    // or LDS writes (staged) of it have completed, and so have its reads of
-    // the stage about to be refilled; then the workgroup barrier.
-    auto tile_ready = [&](int kt) {
+    // Wait until tile kt (in stage `stage`) is in LDS for every wave: this
+    // wave's loads (direct) or LDS writes (staged) of it have completed, and
+    // so have its reads of the stage about to be refilled; then the
+    // workgroup barrier.  Rows only 4-byte aligned: in the range's last
+    // tile each thread first clears the halves past K of the chunks it
+    // loaded that straddle a row end.
+    auto tile_ready = [&](int kt, int stage) {
         if constexpr (DIRECT) {
             if (kt + STAGES - 2 < nk)
                 wait_vm_lgkm0<(STAGES - 2) * kLoadsPerTile>();
             else
                 wait_vm_lgkm0<0>();
+            if constexpr (T::OpA::KTAIL || T::OpB::KTAIL) {
+                if (kt == nk - 1) {
+                    // (the last tile waited for every load; the clobber keeps
+                    // the compiler from moving the clears above that wait)
+                    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+                    opa.fix_tail(kt, As + stage * T::A_STAGE, wave, lane);
+                    opb.fix_tail(kt, Bs + stage * T::B_STAGE, wave, lane);
+                    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                }
+            }
         } else {
+            (void)stage;
             (void)kt;
             wait_lgkm0();
         }
@@ -934,7 +980,7 @@ gemm_f16_kernel(KernelArgs args)
     // the stage written during step kt is (kt + W_OFF) % STAGES
     constexpr int W_OFF = DIRECT ? LOOKAHEAD : 1;
     if (nk > 0) {
-        tile_ready(0);
+        tile_ready(0, 0);
         step(std::integral_constant<int, 0>{}, As, Bs, As + (W_OFF % STAGES) * T::A_STAGE,
              Bs + (W_OFF % STAGES) * T::B_STAGE, LOOKAHEAD, false, 0, W_OFF % STAGES);
     }
@@ -947,7 +993,7 @@ gemm_f16_kernel(KernelArgs args)
             const int s = (1 + u) % STAGES;                 // stage holding tile kt
             const int w = (s + W_OFF) % STAGES;
             if (kt < nk) {
-                tile_ready(kt);
+                tile_ready(kt, s);
                 // kt0 = 1 + STAGES j: with NS odd and STAGES even, kt's parity is (1 + u)'s
                 if (((1 + u) * NS) & 1)
                     step(std::integral_constant<int, 1>{}, As + s * T::A_STAGE, Bs + s * T::B_STAGE,
@@ -1581,12 +1627,10 @@ hipError_t launch_transposed(int config, const KernelArgs &a, int va, int vb, in
     case 12: return launch_one<64, 64, 64, 2, 2, 4, true, 8, 8, AR, BR, 1>(a, grid, s);
     case 13: return launch_one<128, 128, 64, 2, 2, 4, true, 8, 8, AR, BR, 1, false, true>(a, grid, s);
     case 14: return launch_one<128, 64, 64, 2, 2, 4, true, 8, 8, AR, BR, 1>(a, grid, s);
-    case 9:
-        // A stored M x K with 4-byte direct loads: B given N x K (NT) only
-        if constexpr (AR)
-            return launch_one<256, 256, 64, 2, 2, 2, true, 2, 8, AR, BR, 2, false, true>(a, grid, s);
-        else
-            return hipErrorInvalidValue;
+    // rows only 4-byte aligned: 9 = 8, 15 = 13, 16 = 12
+    case 9: return launch_one<256, 256, 64, 2, 2, 2, true, 2, 2, AR, BR, GEMM_F16_M16_SPREAD, false, true>(a, grid, s);
+    case 15: return launch_one<128, 128, 64, 2, 2, 4, true, 2, 2, AR, BR, 1, false, true>(a, grid, s);
+    case 16: return launch_one<64, 64, 64, 2, 2, 4, true, 2, 2, AR, BR, 1>(a, grid, s);
     default: return hipErrorInvalidValue;
     }
 }

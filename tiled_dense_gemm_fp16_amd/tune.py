@@ -31,8 +31,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 OUT = os.path.join(HERE, "csrc", "gemm_f16_tuned.inc")
 
 # shape grid per alignment class: aligned pitches (every configuration runs)
-# at 2x steps in M and N and 4x steps in K; the misaligned classes, which
-# only the register-staged configurations serve, on a coarser grid
+# at 2x steps in M and N and 4x steps in K; the misaligned classes (rows
+# 4-byte aligned: the direct configurations for such rows and the
+# register-staged ones; rows 2-byte aligned: register-staged only) on a
+# coarser grid
 GRIDS = {
     1: ([256, 512, 1024, 2048, 4096, 8192], [256, 1024, 4096, 8192]),
     0: ([512, 2048, 8192], [512, 2048, 8192]),
@@ -104,12 +106,10 @@ def sweep(layouts, log, classes=(1, 0, 2)):
         for M in sizes_mn:
             for N in sizes_mn:
                 for K in sizes_k:
-                    # class 0: every pitch off by 4 elements (8-byte rows only);
-                    # class 2: only K (A's pitch as M x K), for A . B
-                    m, n, k = {1: (M, N, K), 0: (M + 4, N + 4, K + 4), 2: (M, N, K + 4)}[aligned]
+                    # class 2: every pitch off by 4 elements (8-byte rows);
+                    # class 0: every pitch odd (2-byte rows)
+                    m, n, k = {1: (M, N, K), 2: (M + 4, N + 4, K + 4), 0: (M + 1, N + 1, K + 1)}[aligned]
                     for ta, tb in layouts:
-                        if aligned == 2 and (ta or tb):
-                            continue
                         a = torch.randn((k, m) if ta else (m, k), device="cuda").half()
                         b = (torch.randn((n, k) if tb else (k, n), device="cuda") / math.sqrt(k)).half()
                         c = torch.empty((m, n), device="cuda", dtype=torch.float16)
@@ -170,8 +170,9 @@ def sweep(layouts, log, classes=(1, 0, 2)):
 
 
 def narrow_configs(g):
-    """Names of the configurations whose loads stay narrower than 16 bytes on
-    16-byte-aligned operands (the fallbacks for misaligned pitches)."""
+    """Names of the configurations built for rows narrower than 16 bytes
+    (vec_a or vec_b below 8 on 16-byte-aligned operands: the fallbacks for
+    misaligned pitches)."""
     out = set()
     for c in range(g.num_configs()):
         try:
@@ -210,7 +211,7 @@ def write_table(rows, path, note, names, narrow=()):
         "// tiled_dense_gemm_fp16_amd/tune.py; do not edit by hand.",
         f"// {note}",
         "// fields: log2 M, log2 N, log2 K (of the swept shape), trans_a, trans_b,",
-        "// pitches aligned to 16 bytes (1), only B's (2: A's rows 4-byte aligned) or neither (0),",
+        "// rows of both operands 16-byte aligned (1), both at least 4-byte aligned (2), otherwise (0),",
         "// best configuration, K splits, its TFLOP/s, best configuration unsplit, its TFLOP/s",
     ]
     for r in rows:
@@ -230,7 +231,7 @@ def main() -> int:
     ap.add_argument("--layouts", default="nn,nt,tn,tt",
                     help="comma-separated layouts to sweep (n: as stored, t: given transposed)")
     ap.add_argument("--classes", default="1,0,2",
-                    help="alignment classes to sweep: 1 aligned, 0 every pitch off by 4, 2 only K off by 4 (NN)")
+                    help="alignment classes to sweep: 1 aligned, 2 every pitch off by 4, 0 every pitch odd")
     ap.add_argument("--out", default=OUT)
     ap.add_argument("--log", default=None, help="also write every measurement (JSON lines) here")
     ap.add_argument("--from-log", nargs="+", default=None, metavar="LOG",
