@@ -92,7 +92,8 @@ def test_ragged_shapes(shape, epilogue):
 # chunk at the end of a k-row (A given M x K, B given N x K) runs into the
 # next row's first elements, which the kernel zeroes in LDS; an mn-row's
 # chunk past M or N only reaches outputs that are never stored.
-U_NAMES = ("256x256x64_s2_direct_m16_u", "128x128x64_s4_direct_m16_u", "64x64x64_s4_direct_u")
+U_NAMES = ("256x256x64_s2_direct_m16_u", "256x128x64_s3_direct_m16_u", "128x128x64_s4_direct_m16_u",
+           "128x64x64_s4_direct_u", "64x64x64_s4_direct_u")
 # every pitch even; K % 8 in {2, 4, 6}; M and N pitches off 16-byte alignment in some
 U_SHAPES = [(300, 264, 130), (520, 392, 198), (258, 522, 66), (64, 64, 2), (510, 268, 4100), (130, 134, 132)]
 ALL_LAYOUTS = [(False, False), (False, True), (True, False), (True, True)]

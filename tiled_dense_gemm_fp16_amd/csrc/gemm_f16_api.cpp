@@ -25,8 +25,8 @@ const ConfigDesc kConfigs[kNumConfigs] = {
     {"128x128x32_s2_staged", 128, 128, 32, 2, 4, false, 1, 1, kAllLayouts, 2},
     {"64x64x64_s2_staged", 64, 64, 64, 2, 4, false, 1, 1, kAllLayouts, 5},
     {"256x256x64_s2_direct_w8n", 256, 256, 64, 2, 8, true, 8, 8, kAllLayouts, 1},
-    {"256x256x64_s2_staged_w8", 256, 256, 64, 2, 8, false, 4, 4, kAllLayouts, 1},
-    {"256x128x64_s2_staged", 256, 128, 64, 2, 4, false, 4, 4, kNN, 1},
+    {"256x128x64_s3_direct_m16_u", 256, 128, 64, 3, 4, true, 2, 2, kAllLayouts, 1},
+    {"128x64x64_s4_direct_u", 128, 64, 64, 4, 4, true, 2, 2, kAllLayouts, 1},
     {"256x256x64_s2_direct_m16", 256, 256, 64, 2, 4, true, 8, 8, kAllLayouts, 1},
     {"256x256x64_s2_direct_m16_u", 256, 256, 64, 2, 4, true, 2, 2, kAllLayouts, 1},
     {"256x256x32_s4_direct_m16", 256, 256, 32, 4, 4, true, 8, 8, kAllLayouts, 1},
@@ -120,9 +120,9 @@ double config_efficiency(int c)
     case 5: return 1.00;    // 256x256x64 direct, 8 waves
     case 0: return 0.94;    // 256x128x64 direct, 3 stages, 16x16x32 MFMAs
     case 1: return 0.90;    // 256x128x64 direct
-    case 6: return 0.85;    // 256x256x64 register-staged, 8 waves (vectors of 4 or 8)
+    case 6: return 0.92;    // 0 for rows only 4-byte aligned
     case 2: return 0.76;    // 128x128x64 direct
-    case 7: return 0.66;    // 256x128x64 register-staged (vectors of 4 or 8)
+    case 7: return 0.58;    // 14 for rows only 4-byte aligned
     case 3: return 0.46;    // 128x128x32 register-staged, any alignment
     case 4: return 0.25;    // 64x64x64 register-staged, any alignment
     default: return 0.0;

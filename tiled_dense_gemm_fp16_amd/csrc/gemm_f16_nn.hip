@@ -14,8 +14,8 @@ hipError_t launch_nn(int config, const KernelArgs &a, int va, int vb, int64_t gr
     case 3: return launch_staged<128, 128, 32, 2, 2, 2, AR, BR>(a, va, vb, grid, s);
     case 4: return launch_staged<64, 64, 64, 2, 2, 2, AR, BR>(a, va, vb, grid, s);
     case 5: return launch_one<256, 256, 64, 2, 4, 2, true, 8, 8, AR, BR, 2>(a, grid, s);
-    case 6: return launch_staged_wide<256, 256, 64, 2, 4, 2, AR, BR>(a, va, vb, grid, s);
-    case 7: return launch_staged_wide<256, 128, 64, 2, 2, 2, AR, BR>(a, va, vb, grid, s);
+    case 6: return launch_one<256, 128, 64, 2, 2, 3, true, 2, 2, AR, BR, 1, false, true>(a, grid, s);
+    case 7: return launch_one<128, 64, 64, 2, 2, 4, true, 2, 2, AR, BR, 1>(a, grid, s);
     case 8: return launch_one<256, 256, 64, 2, 2, 2, true, 8, 8, AR, BR, GEMM_F16_M16_SPREAD, false, true>(a, grid, s);
     case 9: return launch_one<256, 256, 64, 2, 2, 2, true, 2, 2, AR, BR, GEMM_F16_M16_SPREAD, false, true>(a, grid, s);
     case 10: return launch_one<256, 256, 32, 2, 2, 4, true, 8, 8, AR, BR, 1, false, true>(a, grid, s);

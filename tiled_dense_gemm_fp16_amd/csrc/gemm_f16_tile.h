@@ -829,14 +829,12 @@ gemm_f16_kernel(KernelArgs args)
                                       : T::TM + (SPARSE ? 4 : 2) * T::TN + (WIDE_META ? T::TM : 0);
     // The next step's fragment reads are requested during the current step's
     // MFMAs, at the rate set by the placement switches above.
-    // the 8-wave register-staged tile takes one read per MFMA (+2-3 % on the
-    // 3000x5000x4100 workload it serves; the 4-wave staged 128x128 tile lost 5 %)
     // (a small 16x16x32 wave tile has fewer MFMAs than reads per step: one
     // MFMA then carries as many reads as it takes)
     constexpr bool kM16Fits = kMfmaPerStep / GEMM_F16_M16_READ_EVERY * GEMM_F16_M16_READS_PER_MFMA >= kReadsPerStep;
     constexpr int kReadsPerMfma = M16 ? (kM16Fits ? GEMM_F16_M16_READS_PER_MFMA
                                                   : (kReadsPerStep + kMfmaPerStep - 1) / kMfmaPerStep)
-                                      : (!DIRECT && T::kWaves == 8) ? 1 : GEMM_F16_READS_PER_MFMA;
+                                      : GEMM_F16_READS_PER_MFMA;
     constexpr int kReadEvery = M16 ? (kM16Fits ? GEMM_F16_M16_READ_EVERY : 1) : GEMM_F16_READ_EVERY;
     static_assert(!M16 || kMfmaPerStep / kReadEvery * kReadsPerMfma >= kReadsPerStep, "every read has a slot");
     constexpr int kVmemEvery = M16 ? GEMM_F16_M16_VMEM_EVERY : GEMM_F16_VMEM_EVERY;
@@ -1584,18 +1582,6 @@ static hipError_t launch_staged(const KernelArgs &a, int va, int vb, int64_t gri
 #undef GEMM_F16_VB
 }
 
-// Wide register-staged tiles keep every vector width >= 4 (narrower vectors
-// would need more staging registers than a 256-wide tile leaves free).
-template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool AR, bool BR>
-static hipError_t launch_staged_wide(const KernelArgs &a, int va, int vb, int64_t grid, hipStream_t s)
-{
-    if (va == 8)
-        return vb == 8 ? launch_one<BM, BN, BK, WM, WN, STAGES, false, 8, 8, AR, BR>(a, grid, s)
-                       : launch_one<BM, BN, BK, WM, WN, STAGES, false, 8, 4, AR, BR>(a, grid, s);
-    return vb == 8 ? launch_one<BM, BN, BK, WM, WN, STAGES, false, 4, 8, AR, BR>(a, grid, s)
-                   : launch_one<BM, BN, BK, WM, WN, STAGES, false, 4, 4, AR, BR>(a, grid, s);
-}
-
 // Register-staged tiles for the transposed layouts: 16-byte vectors when the
 // pitch allows them, else single elements.
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool AR, bool BR>
@@ -1620,14 +1606,15 @@ hipError_t launch_transposed(int config, const KernelArgs &a, int va, int vb, in
     case 3: return launch_staged_8or1<128, 128, 32, 2, 2, 2, AR, BR>(a, va, vb, grid, s);
     case 4: return launch_staged_8or1<64, 64, 64, 2, 2, 2, AR, BR>(a, va, vb, grid, s);
     case 5: return launch_one<256, 256, 64, 2, 4, 2, true, 8, 8, AR, BR, 2>(a, grid, s);
-    case 6: return launch_staged_wide<256, 256, 64, 2, 4, 2, AR, BR>(a, va, vb, grid, s);
     case 8: return launch_one<256, 256, 64, 2, 2, 2, true, 8, 8, AR, BR, GEMM_F16_M16_SPREAD, false, true>(a, grid, s);
     case 10: return launch_one<256, 256, 32, 2, 2, 4, true, 8, 8, AR, BR, 1, false, true>(a, grid, s);
     case 11: return launch_persistent<8, AR, BR>(a, grid, s);
     case 12: return launch_one<64, 64, 64, 2, 2, 4, true, 8, 8, AR, BR, 1>(a, grid, s);
     case 13: return launch_one<128, 128, 64, 2, 2, 4, true, 8, 8, AR, BR, 1, false, true>(a, grid, s);
     case 14: return launch_one<128, 64, 64, 2, 2, 4, true, 8, 8, AR, BR, 1>(a, grid, s);
-    // rows only 4-byte aligned: 9 = 8, 15 = 13, 16 = 12
+    // rows only 4-byte aligned: 6 = 0, 7 = 14, 9 = 8, 15 = 13, 16 = 12
+    case 6: return launch_one<256, 128, 64, 2, 2, 3, true, 2, 2, AR, BR, 1, false, true>(a, grid, s);
+    case 7: return launch_one<128, 64, 64, 2, 2, 4, true, 2, 2, AR, BR, 1>(a, grid, s);
     case 9: return launch_one<256, 256, 64, 2, 2, 2, true, 2, 2, AR, BR, GEMM_F16_M16_SPREAD, false, true>(a, grid, s);
     case 15: return launch_one<128, 128, 64, 2, 2, 4, true, 2, 2, AR, BR, 1, false, true>(a, grid, s);
     case 16: return launch_one<64, 64, 64, 2, 2, 4, true, 2, 2, AR, BR, 1>(a, grid, s);

@@ -235,13 +235,21 @@ def main() -> int:
     ap.add_argument("--out", default=OUT)
     ap.add_argument("--log", default=None, help="also write every measurement (JSON lines) here")
     ap.add_argument("--from-log", nargs="+", default=None, metavar="LOG",
-                    help="write the table from earlier sweeps' logs instead of measuring")
+                    help="write the table from earlier sweeps' logs instead of measuring (a shape in a "
+                         "later log replaces its record in an earlier one)")
     args = ap.parse_args()
     import tiled_dense_gemm_fp16_amd as g
 
     names = [g.config_name(c) for c in range(g.num_configs())]
     if args.from_log:
-        rows = [json.loads(line) for path in args.from_log for line in open(path) if line.strip()]
+        # a shape measured again in a later log replaces the earlier record
+        latest = {}
+        for path in args.from_log:
+            for line in open(path):
+                if line.strip():
+                    r = json.loads(line)
+                    latest[(r["M"], r["N"], r["K"], r["trans_a"], r["trans_b"], r["aligned"])] = r
+        rows = list(latest.values())
         write_table(rows, args.out, f"combined from {len(args.from_log)} sweep log(s)", names, narrow_configs(g))
         print(f"wrote {args.out} ({len(rows)} shapes)", flush=True)
         return 0
