@@ -502,3 +502,27 @@ def test_persistent_loop_matches_one_tile_kernel():
         loop = g.gemm(ad, bd, config=c, splits=1)
         torch.cuda.synchronize()
         assert torch.equal(one, loop)
+
+
+def test_prepared_call_matches_gemm():
+    """prepare() checks and binds the tensors once; every call of the
+    returned function enqueues the same product as gemm() (bitwise: the
+    same plan and kernel), also when split or scaled or given transposed."""
+    M, N, K = 520, 392, 200
+    a, b = workloads.draw(M, N, K, "uniform", 77)
+    ad, bd = a.to(DEV), b.to(DEV)
+    bt = bd.t().contiguous()
+    cases = [(bd, {}), (bd, {"epilogue": "relu"}), (bd, {"alpha": 0.5}), (bd, {"splits": 2}),
+             (bd, {"config": configs_for(M, N, K)[0]}), (bt, {"trans_b": True})]
+    for b_arg, kw in cases:
+        print(f"[parity] prepared call {kw}", flush=True)
+        want = g.gemm(ad, b_arg, **kw)
+        out = torch.empty((M, N), dtype=torch.float16, device=DEV)
+        call = g.prepare(ad, b_arg, out=out, **kw)
+        for _ in range(3):
+            out.fill_(float("nan"))
+            assert call() is out
+            torch.cuda.synchronize()
+            assert torch.equal(out, want), kw
+    res = oracle.compare(u16(out), oracle.gemm(u16(a), u16(b)))
+    assert res["pass"], res

@@ -173,25 +173,9 @@ def _auto_split(M, N, K, a, b, out, config, trans_a, trans_b, splits):
     return hit
 
 
-def gemm(a, b, epilogue: str = "none", out=None, config: int = CONFIG_AUTO, stream=None,
-         trans_a: bool = False, trans_b: bool = False, splits: int | None = None, workspace=None,
-         alpha: float = 1.0):
-    """C = epi(alpha * (op(a) @ op(b))) for 2-D contiguous float16 GPU tensors.
-
-    a is M x K (or K x M with ``trans_a``), b is K x N (or N x K with
-    ``trans_b``).  Returns ``out`` (allocated as an M x N float16 tensor when
-    not given).  The kernels are enqueued on ``stream`` (default: torch's
-    current stream) and the call returns without synchronising.
-
-    ``splits``: None lets the planner split K when that pays for the shape
-    (gemm_f16_split with SPLITS_AUTO), 1 runs one kernel (gemm_f16 /
-    gemm_f16_ex / gemm_f16_trans), a larger count asks for that split.  A
-    split needs a workspace of fp32 partial sums: ``workspace`` (a contiguous
-    GPU tensor used as scratch) or, when it is None, one taken from torch's
-    caching allocator on ``stream`` for this call.  The C library itself
-    never allocates.  ``alpha`` (taken as an fp32 value) scales the result
-    before the epilogue (gemm_f16_scaled / gemm_f16_split_scaled).
-    """
+def _bind(a, b, epilogue, out, config, stream, trans_a, trans_b, splits, workspace, alpha):
+    """Check the arguments of gemm()/prepare() and choose the entry point:
+    (the C function, its arguments, out, the tensors the call uses)."""
     import torch
 
     if epilogue not in _EPILOGUES:
@@ -223,37 +207,91 @@ def gemm(a, b, epilogue: str = "none", out=None, config: int = CONFIG_AUTO, stre
     if stream is None:
         stream = torch.cuda.current_stream(a.device)
     request = SPLITS_AUTO if splits is None else int(splits)
-    with torch.cuda.device(a.device):
-        if workspace is None and request != 1 and M > 0 and N > 0:
-            n_split, ws_bytes = _auto_split(M, N, K, a, b, out, config, trans_a, trans_b, request)
-            if n_split > 1:
-                with torch.cuda.stream(stream):
-                    workspace = torch.empty(-(-ws_bytes // 4), dtype=torch.float32, device=a.device)
-            else:
-                request = 1
-        scaled = float(alpha) != 1.0
-        if workspace is None and request in (1, SPLITS_AUTO):
-            if scaled:
-                st = lib().gemm_f16_scaled(M, N, K, a.data_ptr() or None, int(trans_a), b.data_ptr() or None,
-                                           int(trans_b), out.data_ptr() or None, float(alpha), _EPILOGUES[epilogue],
-                                           config, stream.cuda_stream or None)
-            else:
-                st = gemm_f16_raw(M, N, K, a.data_ptr(), b.data_ptr(), out.data_ptr(), _EPILOGUES[epilogue],
-                                  stream.cuda_stream, config, trans_a, trans_b)
+    if workspace is None and request != 1 and M > 0 and N > 0:
+        n_split, ws_bytes = _auto_split(M, N, K, a, b, out, config, trans_a, trans_b, request)
+        if n_split > 1:
+            with torch.cuda.device(a.device), torch.cuda.stream(stream):
+                workspace = torch.empty(-(-ws_bytes // 4), dtype=torch.float32, device=a.device)
         else:
-            ws_ptr = workspace.data_ptr() if workspace is not None else None
-            ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-            args = (M, N, K, a.data_ptr() or None, int(trans_a), b.data_ptr() or None, int(trans_b),
-                    out.data_ptr() or None)
-            if scaled:
-                st = lib().gemm_f16_split_scaled(*args, float(alpha), _EPILOGUES[epilogue], config, request,
-                                                 ws_ptr or None, ws_bytes, stream.cuda_stream or None)
-            else:
-                st = lib().gemm_f16_split(*args, _EPILOGUES[epilogue], config, request, ws_ptr or None, ws_bytes,
-                                          stream.cuda_stream or None)
+            request = 1
+    S = stream.cuda_stream or None
+    A, B, C = a.data_ptr() or None, b.data_ptr() or None, out.data_ptr() or None
+    epi = _EPILOGUES[epilogue]
+    scaled = float(alpha) != 1.0
+    h = lib()
+    if workspace is None and request in (1, SPLITS_AUTO):
+        if scaled:
+            fn, args = h.gemm_f16_scaled, (M, N, K, A, int(trans_a), B, int(trans_b), C, float(alpha), epi, config, S)
+        elif trans_a or trans_b:
+            fn, args = h.gemm_f16_trans, (M, N, K, A, int(trans_a), B, int(trans_b), C, epi, config, S)
+        elif config == CONFIG_AUTO:
+            fn, args = h.gemm_f16, (M, N, K, A, B, C, epi, S)
+        else:
+            fn, args = h.gemm_f16_ex, (M, N, K, A, B, C, epi, config, S)
+    else:
+        ws_ptr = workspace.data_ptr() if workspace is not None else None
+        ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+        head = (M, N, K, A, int(trans_a), B, int(trans_b), C)
+        if scaled:
+            fn, args = h.gemm_f16_split_scaled, head + (float(alpha), epi, config, request, ws_ptr or None, ws_bytes, S)
+        else:
+            fn, args = h.gemm_f16_split, head + (epi, config, request, ws_ptr or None, ws_bytes, S)
+    return fn, args, out, (a, b, out, workspace, stream)
+
+
+def gemm(a, b, epilogue: str = "none", out=None, config: int = CONFIG_AUTO, stream=None,
+         trans_a: bool = False, trans_b: bool = False, splits: int | None = None, workspace=None,
+         alpha: float = 1.0):
+    """C = epi(alpha * (op(a) @ op(b))) for 2-D contiguous float16 GPU tensors.
+
+    a is M x K (or K x M with ``trans_a``), b is K x N (or N x K with
+    ``trans_b``).  Returns ``out`` (allocated as an M x N float16 tensor when
+    not given).  The kernels are enqueued on ``stream`` (default: torch's
+    current stream) and the call returns without synchronising.
+
+    ``splits``: None lets the planner split K when that pays for the shape
+    (gemm_f16_split with SPLITS_AUTO), 1 runs one kernel (gemm_f16 /
+    gemm_f16_ex / gemm_f16_trans), a larger count asks for that split.  A
+    split needs a workspace of fp32 partial sums: ``workspace`` (a contiguous
+    GPU tensor used as scratch) or, when it is None, one taken from torch's
+    caching allocator on ``stream`` for this call.  The C library itself
+    never allocates.  ``alpha`` (taken as an fp32 value) scales the result
+    before the epilogue (gemm_f16_scaled / gemm_f16_split_scaled).
+    """
+    import torch
+
+    fn, args, out, _ = _bind(a, b, epilogue, out, config, stream, trans_a, trans_b, splits, workspace, alpha)
+    with torch.cuda.device(a.device):
+        st = fn(*args)
     if st != SUCCESS:
         raise GemmError(st, "gemm_f16")
     return out
+
+
+def prepare(a, b, epilogue: str = "none", out=None, config: int = CONFIG_AUTO, stream=None,
+            trans_a: bool = False, trans_b: bool = False, splits: int | None = None, workspace=None,
+            alpha: float = 1.0):
+    """gemm() bound to fixed tensors, for loops that repeat one product on
+    the same buffers (serving, benchmarks).
+
+    Takes gemm()'s arguments, checks them and makes the split decision once
+    (a split's workspace is allocated here, once), and returns a function of
+    no arguments that enqueues the product on ``stream`` and returns
+    ``out``; the C library still validates and plans every call (from its
+    per-thread plan cache).  The bound tensors must stay in place: the
+    function keeps references to them, not copies.  Call it with the
+    tensors' device current."""
+    fn, args, out, keep = _bind(a, b, epilogue, out, config, stream, trans_a, trans_b, splits, workspace, alpha)
+
+    def call():
+        st = fn(*args)
+        if st != SUCCESS:
+            raise GemmError(st, "gemm_f16")
+        return out
+
+    call.out = out
+    call.bound = keep
+    return call
 
 
 # ---- 2:4 structured-sparse A (gemm_f16_sp*, see include/gemm_f16.h) --------

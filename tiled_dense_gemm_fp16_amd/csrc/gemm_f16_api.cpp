@@ -346,17 +346,11 @@ int choose_config(int64_t M, int64_t N, int64_t K, int va, int vb, int vc, bool 
     return best;
 }
 
-gemm_f16_status_t make_plan(int64_t M, int64_t N, int64_t K, const void *A, bool ta, const void *B, bool tb,
-                            const void *C, int config, int splits, gemm_f16_plan_t *plan)
+// The plan of a shape: the pointers matter only through the alignment of
+// the rows they start (va, vb: A's and B's rows; vc: C's stores).
+gemm_f16_status_t plan_for(int64_t M, int64_t N, int64_t K, bool ta, bool tb, int va, int vb, int vc, int config,
+                           int splits, gemm_f16_plan_t *plan)
 {
-    if (config != GEMM_F16_CONFIG_AUTO && (config < 0 || config >= kNumConfigs))
-        return GEMM_F16_ERROR_INVALID_VALUE;
-    if (splits < 0 || splits > GEMM_F16_MAX_SPLITS)
-        return GEMM_F16_ERROR_INVALID_VALUE;
-    // row pitches of the matrices as stored
-    const int64_t lda = ta ? M : K, ldb = tb ? K : N;
-    const int va = vec_width(A, lda), vb = vec_width(B, ldb);
-    const int vc = (N % 8 == 0 && (uintptr_t)C % 16 == 0) ? 8 : (N % 4 == 0 && (uintptr_t)C % 8 == 0) ? 4 : 1;
     int c = config;
     Split sp = {1, K};
     if (c == GEMM_F16_CONFIG_AUTO) {
@@ -396,6 +390,56 @@ gemm_f16_status_t make_plan(int64_t M, int64_t N, int64_t K, const void *A, bool
     if (plan->grid > 0x7fffffff)
         return GEMM_F16_ERROR_UNSUPPORTED_SIZE;
     return GEMM_F16_SUCCESS;
+}
+
+// Repeated calls of one shape skip the table search (a few microseconds of
+// host time per call): a small per-thread cache of plans, keyed by
+// everything plan_for reads.
+struct PlanKey {
+    int64_t M, N, K;
+    int ta, tb, va, vb, vc, config, splits;
+    bool operator==(const PlanKey &o) const
+    {
+        return M == o.M && N == o.N && K == o.K && ta == o.ta && tb == o.tb && va == o.va && vb == o.vb &&
+               vc == o.vc && config == o.config && splits == o.splits;
+    }
+};
+struct PlanSlot {
+    bool used;
+    PlanKey key;
+    gemm_f16_status_t status;
+    gemm_f16_plan_t plan;
+};
+constexpr int kPlanCacheSlots = 64;
+thread_local PlanSlot t_plans[kPlanCacheSlots];
+
+gemm_f16_status_t make_plan(int64_t M, int64_t N, int64_t K, const void *A, bool ta, const void *B, bool tb,
+                            const void *C, int config, int splits, gemm_f16_plan_t *plan)
+{
+    if (config != GEMM_F16_CONFIG_AUTO && (config < 0 || config >= kNumConfigs))
+        return GEMM_F16_ERROR_INVALID_VALUE;
+    if (splits < 0 || splits > GEMM_F16_MAX_SPLITS)
+        return GEMM_F16_ERROR_INVALID_VALUE;
+    // row pitches of the matrices as stored
+    const int64_t lda = ta ? M : K, ldb = tb ? K : N;
+    const int va = vec_width(A, lda), vb = vec_width(B, ldb);
+    const int vc = (N % 8 == 0 && (uintptr_t)C % 16 == 0) ? 8 : (N % 4 == 0 && (uintptr_t)C % 8 == 0) ? 4 : 1;
+    const PlanKey key = {M, N, K, (int)ta, (int)tb, va, vb, vc, config, splits};
+    uint64_t h = (uint64_t)M * 0x9E3779B97F4A7C15ull ^ (uint64_t)N * 0xC2B2AE3D27D4EB4Full ^
+                 (uint64_t)K * 0x165667B19E3779F9ull;
+    h ^= (uint64_t)(((ta * 2 + tb) * 16 + va) * 16 + vb) * 0x27D4EB2F165667C5ull;
+    h ^= (uint64_t)((vc * 64 + (config + 1)) * 64 + splits) * 0x94D049BB133111EBull;
+    PlanSlot &slot = t_plans[(h >> 32) % kPlanCacheSlots];
+    if (slot.used && slot.key == key) {
+        *plan = slot.plan;
+        return slot.status;
+    }
+    const gemm_f16_status_t st = plan_for(M, N, K, ta, tb, va, vb, vc, config, splits, plan);
+    slot.used = true;
+    slot.key = key;
+    slot.status = st;
+    slot.plan = *plan;
+    return st;
 }
 
 // Per-device check that the device is gfx950, done once per device.
