@@ -107,6 +107,19 @@ static int fails = 0;
 using gemm_f16_impl::kNumConfigs;
 using gemm_f16_impl::kNumSpConfigs;
 
+// Earlier planning calls and their results: replayed later, after other
+// shapes have gone through the planner's per-thread cache, they must give
+// the same status and the same plan.
+struct Planned {
+    int64_t M, N, K;
+    int ta, tb;
+    uintptr_t A, B, C;
+    int config, splits;
+    gemm_f16_status_t status;
+    gemm_f16_plan_t plan;
+};
+static Planned g_history[512];
+
 int main()
 {
     const int iterations = 200000;
@@ -132,6 +145,27 @@ int main()
             CHECK(plan.workspace_bytes == (plan.splits > 1 ? (int64_t)plan.splits * M * N * 4 : 0));
             CHECK(plan.k_split >= 0);
             CHECK(!(ta && M > GEMM_F16_MAX_M_TRANS_A));
+        }
+        // planning again (from the cache) gives the same answer, now and later
+        {
+            gemm_f16_plan_t again;
+            memset(&again, 0xCD, sizeof(again));
+            CHECK(gemm_f16_plan_split(M, N, K, (const void *)A, ta, (const void *)B, tb, (const void *)C, config,
+                                      splits, &again) == ps);
+            if (ps == GEMM_F16_SUCCESS)
+                CHECK(memcmp(&again, &plan, sizeof(plan)) == 0);
+            Planned &h = g_history[it % 512];
+            if (it >= 512 && next() % 4 == 0) {
+                gemm_f16_plan_t old;
+                memset(&old, 0xEF, sizeof(old));
+                const gemm_f16_status_t s_old = gemm_f16_plan_split(
+                    h.M, h.N, h.K, (const void *)h.A, h.ta, (const void *)h.B, h.tb, (const void *)h.C, h.config,
+                    h.splits, &old);
+                CHECK(s_old == h.status);
+                if (s_old == GEMM_F16_SUCCESS)
+                    CHECK(memcmp(&old, &h.plan, sizeof(old)) == 0);
+            }
+            h = Planned{M, N, K, ta, tb, A, B, C, config, splits, ps, plan};
         }
         // the workspace-free entry point: same validation, never a split
         const int before = g_launches, red_before = g_reductions;
