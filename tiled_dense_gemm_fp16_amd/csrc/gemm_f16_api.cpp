@@ -153,8 +153,6 @@ int kernel_vec(const ConfigDesc &d, int v, bool transposed, bool is_a)
 {
     if (d.direct)
         return is_a ? d.min_vec : d.min_vec_b;
-    if (d.min_vec >= 4)
-        return v >= 8 ? 8 : 4;              // wide register-staged tiles
     if (transposed)
         return v >= 8 ? 8 : 1;              // transposed layouts, narrow tiles: 16-byte vectors or elements
     return v;
