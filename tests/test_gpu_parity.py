@@ -123,6 +123,33 @@ def test_rows_4byte_aligned_direct_configs(ta, tb, shape):
             assert res["pass"], (ta, tb, shape, epi, g.config_name(c), res)
 
 
+@pytest.mark.parametrize("ta,tb", ALL_LAYOUTS)
+def test_rows_4byte_aligned_large_sampled(ta, tb):
+    """A large shape whose every row pitch is only 8-byte aligned (K % 8 = 4),
+    in each layout, through the automatic choice (a direct configuration for
+    4-byte rows): a seeded sample of rows and columns, with the tile edges,
+    against the oracle."""
+    M, N, K = 4100, 4108, 4100
+    a, b = workloads.draw(M, N, K, "normal", 4100 + 2 * ta + tb)
+    a_st = a.t().contiguous() if ta else a
+    b_st = b.t().contiguous() if tb else b
+    a_dev, b_dev = a_st.to(DEV), b_st.to(DEV)
+    p = g.plan(M, N, K, a_dev.data_ptr(), b_dev.data_ptr(), 1 << 20, trans_a=ta, trans_b=tb)
+    assert p["direct_lds"] == 1 and g.config_name(p["config"]).endswith("_u"), g.config_name(p["config"])
+    print(f"[parity] 4-byte rows, large, sampled, ta={ta} tb={tb} {g.config_name(p['config'])}", flush=True)
+    out = g.gemm(a_dev, b_dev, trans_a=ta, trans_b=tb)
+    torch.cuda.synchronize()
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(77 + 2 * ta + tb)
+    edges = [0, 1, 127, 128, 255, 256, 4095, 4096]
+    rows = sorted(set(torch.randperm(M, generator=gen)[:192].tolist() + edges + [M - 1]))
+    cols = sorted(set(torch.randperm(N, generator=gen)[:192].tolist() + edges + [N - 1]))
+    got = u16(out[torch.tensor(rows, device=DEV)][:, torch.tensor(cols, device=DEV)])
+    ref = oracle.gemm_sampled(u16(a), u16(b), rows, cols)
+    res = oracle.compare(got, ref)
+    assert res["pass"], (ta, tb, res)
+
+
 def compare_with_specials(got, ref):
     """NaN and infinity where the oracle has them (same sign); every finite
     reference element within the usual bound."""

@@ -225,6 +225,9 @@ def test_python_wrapper_argument_checks():
         g.gemm(a, a, epilogue="gelu")
     with pytest.raises(ValueError):
         g.gemm(a, a)                                           # CPU tensors
+    for kw in ({}, {"epilogue": "gelu"}, {"trans_b": True}):
+        with pytest.raises(ValueError):                        # prepare() checks the same, once
+            g.prepare(a, a, **kw)
     with pytest.raises(ValueError):
         g.gemm(a.float(), a)
 
