@@ -150,6 +150,25 @@ def test_rows_4byte_aligned_large_sampled(ta, tb):
     assert res["pass"], (ta, tb, res)
 
 
+@pytest.mark.parametrize("ta,tb", ALL_LAYOUTS)
+def test_rows_4byte_aligned_split_k(ta, tb):
+    """The configurations for 4-byte rows with K split three ways: only the
+    last split's range ends inside a chunk (K % 8 = 4)."""
+    M, N, K = 300, 268, 1348
+    a_st, b_st = stored(M, N, K, ta, tb, 31 + 2 * ta + tb)
+    a_dev, b_dev = a_st.to(DEV), b_st.to(DEV)
+    ref = oracle.gemm(u16(a_st), u16(b_st), trans_a=ta, trans_b=tb)
+    ws = torch.empty(3 * M * N, dtype=torch.float32, device=DEV)
+    for c in u_configs():
+        p = g.plan(M, N, K, a_dev.data_ptr(), b_dev.data_ptr(), 1 << 20, config=c, trans_a=ta, trans_b=tb, splits=3)
+        assert p["splits"] == 3, p
+        print(f"[parity] 4-byte rows, K split 3, ta={ta} tb={tb} {g.config_name(c)}", flush=True)
+        out = g.gemm(a_dev, b_dev, config=c, trans_a=ta, trans_b=tb, splits=3, workspace=ws)
+        torch.cuda.synchronize()
+        res = oracle.compare(u16(out), ref)
+        assert res["pass"], (ta, tb, g.config_name(c), res)
+
+
 def compare_with_specials(got, ref):
     """NaN and infinity where the oracle has them (same sign); every finite
     reference element within the usual bound."""
