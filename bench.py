@@ -224,6 +224,9 @@ def main() -> int:
     ap.add_argument("--sparse", action="store_true",
                     help="time the 2:4-sparse product instead: A pruned to 2:4 and compressed once "
                          "on the GPU before timing")
+    ap.add_argument("--layout", default="nn", choices=["nn", "nt", "tn", "tt"],
+                    help="dense only: A and/or B given transposed (t: A stored K x M, B stored N x K), "
+                         "the same product C = A . B")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the MFMA-only ceiling probe")
@@ -253,13 +256,17 @@ def main() -> int:
         __graft_entry__.build()
 
     w = workloads.WORKLOADS[args.workload]
-    workload_name = w.name + ("_sparse_2of4" if args.sparse else "")
+    if args.sparse and args.layout != "nn":
+        print("--layout applies to the dense product only", file=sys.stderr)
+        return 2
+    ta, tb = args.layout[0] == "t", args.layout[1] == "t"
+    workload_name = w.name + ("" if args.layout == "nn" else "_" + args.layout) + ("_sparse_2of4" if args.sparse else "")
     if args.traffic_from:
         if args.sparse:
             p = g.plan_sp(w.M, w.N, w.K, 1 << 20, 1 << 20, 1 << 20, 1 << 20, config=args.config)
             name = g.sp_config_name(p["config"])
         else:
-            p = g.plan(w.M, w.N, w.K, 1 << 20, 1 << 20, 1 << 20, config=args.config)
+            p = g.plan(w.M, w.N, w.K, 1 << 20, 1 << 20, 1 << 20, config=args.config, trans_a=ta, trans_b=tb)
             name = g.config_name(p["config"])
         return traffic_from(args.traffic_from, workload_name, name)
     dev = torch.device("cuda:0")
@@ -279,10 +286,15 @@ def main() -> int:
         def call():
             g.gemm_sp(vals, meta, bd, epilogue=epi, out=cd, config=args.config, stream=stream)
     else:
-        plan = g.plan(w.M, w.N, w.K, ad.data_ptr(), bd.data_ptr(), cd.data_ptr(), config=args.config)
+        if ta:
+            ad = ad.t().contiguous()
+        if tb:
+            bd = bd.t().contiguous()
+        plan = g.plan(w.M, w.N, w.K, ad.data_ptr(), bd.data_ptr(), cd.data_ptr(), config=args.config,
+                      trans_a=ta, trans_b=tb)
         # the arguments are checked once; each call enters the C library
         # (which validates, plans and launches) with the bound tensors
-        call = g.prepare(ad, bd, epilogue=epi, out=cd, config=args.config, stream=stream)
+        call = g.prepare(ad, bd, epilogue=epi, out=cd, config=args.config, stream=stream, trans_a=ta, trans_b=tb)
 
     for _ in range(args.warmup):
         call()
@@ -345,7 +357,7 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic",
-        "config": {"workload": workload_name, "M": w.M, "N": w.N, "K": w.K,
+        "config": {"workload": workload_name, "M": w.M, "N": w.N, "K": w.K, "layout": args.layout,
                    "epilogue": epi, "inputs": f"{w.dist} seed {w.seed}" + (", A pruned to 2:4" if args.sparse else ""),
                    "sha256_A": workloads.sha256(a), "sha256_B": workloads.sha256(b),
                    "kernel": config_name},
