@@ -133,3 +133,30 @@ def test_random_sparse_cases(block):
         assert res["pass"], (label, res)
         host = u16(cbuf)
         assert np.all(host[:off] == sentinel) and np.all(host[off + M * N:] == sentinel), label
+
+
+def test_random_large_cases_sampled():
+    """Seeded random large shapes (257 to 5000 in each dimension), each
+    layout and alignment, the automatic choice (which for such grids picks
+    the 256-wide tiles and their tile remap over many rounds): a seeded
+    sample of rows and columns, with the first and last, against the oracle."""
+    rng = np.random.default_rng(4242)
+    for case in range(16):
+        M, N, K = (int(x) for x in rng.integers(257, 5001, size=3))
+        if case % 2 == 0:
+            M, N, K = ((x // 8) * 8 for x in (M, N, K))
+        ta, tb = bool(rng.integers(2)), bool(rng.integers(2))
+        seed = int(rng.integers(1 << 30))
+        a, b = workloads.draw(M, N, K, "normal", seed)
+        ad = (a.t().contiguous() if ta else a).to(DEV)
+        bd = (b.t().contiguous() if tb else b).to(DEV)
+        p = g.plan(M, N, K, ad.data_ptr(), bd.data_ptr(), 1 << 20, trans_a=ta, trans_b=tb)
+        label = f"large case {case}: {M}x{N}x{K} ta={ta} tb={tb} seed={seed} config={g.config_name(p['config'])}"
+        print(label, flush=True)
+        out = g.gemm(ad, bd, trans_a=ta, trans_b=tb, splits=1)
+        torch.cuda.synchronize()
+        rows = sorted(set(rng.choice(M, size=48, replace=False).tolist() + [0, M - 1]))
+        cols = sorted(set(rng.choice(N, size=48, replace=False).tolist() + [0, N - 1]))
+        got = u16(out[torch.tensor(rows, device=DEV)][:, torch.tensor(cols, device=DEV)])
+        res = oracle.compare(got, oracle.gemm_sampled(u16(a), u16(b), rows, cols))
+        assert res["pass"], (label, res)
