@@ -36,6 +36,7 @@ const ConfigDesc kConfigs[kNumConfigs] = {
     {"128x64x64_s4_direct", 128, 64, 64, 4, 4, true, 8, 8, kAllLayouts, 1},
     {"128x128x64_s4_direct_m16_u", 128, 128, 64, 4, 4, true, 2, 2, kAllLayouts, 1},
     {"64x64x64_s4_direct_u", 64, 64, 64, 4, 4, true, 2, 2, kAllLayouts, 2},
+    {"128x128x64_s2_staged", 128, 128, 64, 2, 4, false, 1, 1, kAllLayouts, 1},
 };
 
 // Sparse configurations (2:4 A): fields as above; every one takes A as
@@ -124,6 +125,7 @@ double config_efficiency(int c)
     case 2: return 0.76;    // 128x128x64 direct
     case 7: return 0.58;    // 14 for rows only 4-byte aligned
     case 3: return 0.46;    // 128x128x32 register-staged, any alignment
+    case 17: return 0.50;   // 128x128x64 register-staged, any alignment (twice the k step of 3)
     case 4: return 0.25;    // 64x64x64 register-staged, any alignment
     default: return 0.0;
     }

@@ -42,7 +42,7 @@ struct ConfigDesc {
     bool persistent;      // one resident workgroup per CU loops over the tiles
 };
 
-constexpr int kNumConfigs = 17;
+constexpr int kNumConfigs = 18;
 extern const ConfigDesc kConfigs[kNumConfigs];
 
 // Launch configuration `config` with `grid` workgroups on `s`.

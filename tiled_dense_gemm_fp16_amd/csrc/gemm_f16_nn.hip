@@ -25,6 +25,7 @@ hipError_t launch_nn(int config, const KernelArgs &a, int va, int vb, int64_t gr
     case 14: return launch_one<128, 64, 64, 2, 2, 4, true, 8, 8, AR, BR, 1>(a, grid, s);
     case 15: return launch_one<128, 128, 64, 2, 2, 4, true, 2, 2, AR, BR, 1, false, true>(a, grid, s);
     case 16: return launch_one<64, 64, 64, 2, 2, 4, true, 2, 2, AR, BR, 1>(a, grid, s);
+    case 17: return launch_staged<128, 128, 64, 2, 2, 2, AR, BR>(a, va, vb, grid, s);
     default: return hipErrorInvalidValue;
     }
 }

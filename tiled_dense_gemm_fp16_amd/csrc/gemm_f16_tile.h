@@ -1605,6 +1605,7 @@ hipError_t launch_transposed(int config, const KernelArgs &a, int va, int vb, in
     case 2: return launch_one<128, 128, 64, 2, 2, 3, true, 8, 8, AR, BR, 4>(a, grid, s);
     case 3: return launch_staged_8or1<128, 128, 32, 2, 2, 2, AR, BR>(a, va, vb, grid, s);
     case 4: return launch_staged_8or1<64, 64, 64, 2, 2, 2, AR, BR>(a, va, vb, grid, s);
+    case 17: return launch_staged_8or1<128, 128, 64, 2, 2, 2, AR, BR>(a, va, vb, grid, s);
     case 5: return launch_one<256, 256, 64, 2, 4, 2, true, 8, 8, AR, BR, 2>(a, grid, s);
     case 8: return launch_one<256, 256, 64, 2, 2, 2, true, 8, 8, AR, BR, GEMM_F16_M16_SPREAD, false, true>(a, grid, s);
     case 10: return launch_one<256, 256, 32, 2, 2, 4, true, 8, 8, AR, BR, 1, false, true>(a, grid, s);
