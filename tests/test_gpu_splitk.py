@@ -230,6 +230,41 @@ def test_split_in_a_captured_graph():
     del graph
 
 
+def test_prepared_calls_in_a_captured_graph():
+    """prepare() takes a split's workspace when it binds the call, so a graph
+    of prepared calls records kernels only; every replay (with eager work and
+    synchronisations between) matches the eager results."""
+    split_case = Case(96, 96, 30000, seed=17)
+    plain_case = Case(520, 392, 200, tb=True, seed=18)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    out1 = torch.empty((96, 96), dtype=torch.float16, device=DEV)
+    out2 = torch.empty((520, 392), dtype=torch.float16, device=DEV)
+    with torch.cuda.stream(side):
+        p1 = g.prepare(split_case.ad, split_case.bd, out=out1, splits=3, epilogue="relu")
+        p2 = g.prepare(plain_case.ad, plain_case.bd, out=out2, trans_b=True, alpha=0.5)
+        p1()
+        p2()
+    side.synchronize()
+    e1, e2 = u16(out1), u16(out2)
+    assert oracle.compare(e1, split_case.ref("relu"))["pass"]
+    assert oracle.compare(e2, oracle.gemm(u16(plain_case.a), u16(plain_case.b), trans_b=True, scale=0.5))["pass"]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        p1()
+        p2()
+    for _ in range(3):
+        out1.fill_(7.0)
+        out2.fill_(7.0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(u16(out1), e1) and np.array_equal(u16(out2), e2)
+        g.gemm(split_case.ad, split_case.bd, splits=2)     # eager split work between the replays
+        torch.cuda.synchronize()
+    del graph
+
+
 def test_split_scaled():
     """The scale of the scaled entry points on the split path: the reduction
     multiplies the sum of the partials by alpha before the ReLU."""
